@@ -1,0 +1,325 @@
+"""Python binding of libmla, the MI355X (gfx950) MLA library.
+
+Argument marshalling only: torch tensors are checked against the dims (shape,
+dtype, device, contiguity) so that no kernel is launched on mismatched
+buffers, and are handed to the C ABI in include/mla.h as raw device pointers
+on the current torch stream. Every step of the computation runs in the HIP
+kernels of libmla.so; there is no fallback. If the library is not built the
+first call raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import dataclasses
+import math
+import os
+from typing import Optional
+
+import torch
+
+__all__ = [
+    "Dims", "Cache", "QProj", "MLAError", "library", "library_path",
+    "mla_rope_latent_project", "mla_decode", "mla_prefill",
+    "mla_project_workspace_size", "mla_decode_workspace_size", "mla_prefill_workspace_size",
+    "mla_status_string", "mla_decode_path", "mla_prefill_path", "mla_version",
+]
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(_PKG, "libmla.so")
+
+MLA_F32, MLA_BF16 = 0, 1
+_TORCH_DTYPE = {MLA_F32: torch.float32, MLA_BF16: torch.bfloat16}
+
+
+class MLAError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        super().__init__(f"{where}: status {status} ({mla_status_string(status)})")
+        self.status = status
+
+
+# ------------------------------------------------------------- C structs ---
+class _Dims(ctypes.Structure):
+    _fields_ = [("n_heads", ctypes.c_int32), ("d_c", ctypes.c_int32), ("d_rope", ctypes.c_int32),
+                ("d_nope", ctypes.c_int32), ("d_v", ctypes.c_int32), ("softmax_scale", ctypes.c_float),
+                ("rope_base", ctypes.c_float), ("dtype", ctypes.c_int32)]
+
+
+class _Cache(ctypes.Structure):
+    _fields_ = [("rows", ctypes.c_void_p), ("num_blocks", ctypes.c_int32), ("block_size", ctypes.c_int32),
+                ("block_table", ctypes.c_void_p), ("max_blocks_per_seq", ctypes.c_int32),
+                ("context_lens", ctypes.c_void_p), ("max_context", ctypes.c_int32)]
+
+
+class _QProj(ctypes.Structure):
+    _fields_ = [("d_q", ctypes.c_int32), ("w_dq", ctypes.c_void_p), ("w_uq", ctypes.c_void_p),
+                ("w_qr", ctypes.c_void_p), ("q_nope", ctypes.c_void_p), ("q_pe", ctypes.c_void_p)]
+
+
+_lib = None
+
+
+def library_path() -> str:
+    return _LIB_PATH
+
+
+def library():
+    """The loaded libmla.so (ctypes), loading it on first use."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB_PATH):
+            raise RuntimeError(f"{_LIB_PATH} is missing: build it with `python -m mla_latent_kv_09_amd.build`")
+        lib = ctypes.CDLL(_LIB_PATH)
+        vp, i32, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_size_t
+        pd, pc, pq = ctypes.POINTER(_Dims), ctypes.POINTER(_Cache), ctypes.POINTER(_QProj)
+        lib.mla_rope_latent_project.argtypes = [pd, i32, i32, vp, vp, vp, vp, vp, pc, pq, vp, sz, vp]
+        lib.mla_decode.argtypes = [pd, i32, vp, vp, vp, vp, pc, vp, vp, sz, vp]
+        lib.mla_prefill.argtypes = [pd, i32, i32, vp, vp, vp, vp, pc, vp, vp, sz, vp]
+        lib.mla_project_workspace_size.argtypes = [pd, i32, i32, ctypes.POINTER(sz)]
+        lib.mla_decode_workspace_size.argtypes = [pd, i32, i32, ctypes.POINTER(sz)]
+        lib.mla_prefill_workspace_size.argtypes = [pd, i32, i32, i32, ctypes.POINTER(sz)]
+        lib.mla_status_string.argtypes = [ctypes.c_int]
+        lib.mla_status_string.restype = ctypes.c_char_p
+        lib.mla_decode_path.argtypes = [pd, i32, i32]
+        lib.mla_prefill_path.argtypes = [pd, i32, i32]
+        for f in ("mla_rope_latent_project", "mla_decode", "mla_prefill", "mla_project_workspace_size",
+                  "mla_decode_workspace_size", "mla_prefill_workspace_size"):
+            getattr(lib, f).restype = ctypes.c_int
+        for f in ("mla_decode_path", "mla_prefill_path", "mla_version"):
+            getattr(lib, f).restype = ctypes.c_int32
+        _lib = lib
+    return _lib
+
+
+# ------------------------------------------------------------ Python side ---
+@dataclasses.dataclass(frozen=True)
+class Dims:
+    n_heads: int
+    d_c: int
+    d_rope: int
+    d_nope: int
+    d_v: int
+    dtype: str = "bf16"            # "bf16" or "f32"
+    softmax_scale: float = 0.0     # <= 0: 1/sqrt(d_nope + d_rope)
+    rope_base: float = 10000.0
+
+    @classmethod
+    def of(cls, d) -> "Dims":
+        if isinstance(d, cls):
+            return d
+        if isinstance(d, _Dims):
+            return cls(d.n_heads, d.d_c, d.d_rope, d.d_nope, d.d_v,
+                       {MLA_F32: "f32", MLA_BF16: "bf16"}.get(d.dtype, d.dtype), d.softmax_scale, d.rope_base)
+        return cls(d.n_heads, d.d_c, d.d_rope, d.d_nope, d.d_v, getattr(d, "dtype", "bf16"),
+                   getattr(d, "softmax_scale", 0.0), getattr(d, "rope_base", 10000.0))
+
+    @property
+    def code(self) -> int:
+        return {"f32": MLA_F32, "bf16": MLA_BF16}.get(self.dtype, self.dtype)
+
+    @property
+    def torch_dtype(self):
+        return _TORCH_DTYPE[self.code]
+
+    @property
+    def row(self) -> int:
+        return self.d_c + self.d_rope
+
+    def c(self) -> _Dims:
+        return _Dims(self.n_heads, self.d_c, self.d_rope, self.d_nope, self.d_v, self.softmax_scale,
+                     self.rope_base, self.code)
+
+
+@dataclasses.dataclass
+class Cache:
+    """Latent cache on the device.
+
+    rows: [num_blocks, block_size, d_c + d_rope] with a block table [batch,
+    max_blocks] (int32), or [batch, max_context, d_c + d_rope] with none.
+    context_lens: int32 [batch]. max_context: host-side bound of context_lens.
+    """
+    rows: torch.Tensor
+    context_lens: torch.Tensor
+    max_context: int
+    block_table: Optional[torch.Tensor] = None
+
+    @property
+    def batch(self) -> int:
+        return self.context_lens.shape[0]
+
+    def c(self) -> _Cache:
+        if self.block_table is None:
+            return _Cache(self.rows.data_ptr(), 0, 0, None, 0, self.context_lens.data_ptr(), int(self.max_context))
+        return _Cache(self.rows.data_ptr(), self.rows.shape[0], self.rows.shape[1], self.block_table.data_ptr(),
+                      self.block_table.shape[1], self.context_lens.data_ptr(), int(self.max_context))
+
+
+@dataclasses.dataclass
+class QProj:
+    """Optional query path of mla_rope_latent_project (outputs q_nope, q_pe)."""
+    w_dq: torch.Tensor      # [d_q, d_model]
+    w_uq: torch.Tensor      # [H*d_nope, d_q]
+    w_qr: torch.Tensor      # [H*d_rope, d_q]
+    q_nope: torch.Tensor    # out [n_tokens, H, d_nope]
+    q_pe: torch.Tensor      # out [n_tokens, H, d_rope]
+
+    @property
+    def d_q(self) -> int:
+        return self.w_dq.shape[0]
+
+
+def _need(t: torch.Tensor, name: str, shape, dtype):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be on the GPU")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} has dtype {t.dtype}, expected {dtype}")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def _check_cache(cache: Cache, d: Dims, batch: int):
+    _need(cache.context_lens, "context_lens", (batch,), torch.int32)
+    if cache.block_table is None:
+        _need(cache.rows, "cache rows", (batch, cache.max_context, d.row), d.torch_dtype)
+    else:
+        r = cache.rows
+        if r.dim() != 3:
+            raise ValueError("paged cache rows must be [num_blocks, block_size, row]")
+        _need(r, "cache rows", (r.shape[0], r.shape[1], d.row), d.torch_dtype)
+        _need(cache.block_table, "block_table", (batch, cache.block_table.shape[1]), torch.int32)
+
+
+def _stream(stream) -> int:
+    s = torch.cuda.current_stream() if stream is None else stream
+    return int(s.cuda_stream) if hasattr(s, "cuda_stream") else int(s)
+
+
+def _workspace(nbytes: int, device, workspace):
+    if nbytes == 0:
+        return None, 0
+    if workspace is None:
+        workspace = torch.empty(nbytes, dtype=torch.uint8, device=device)
+    if workspace.numel() * workspace.element_size() < nbytes:
+        raise ValueError(f"workspace has {workspace.numel() * workspace.element_size()} bytes, needs {nbytes}")
+    return workspace, workspace.numel() * workspace.element_size()
+
+
+def _ok(status: int, where: str):
+    if status != 0:
+        raise MLAError(status, where)
+
+
+def mla_status_string(status: int) -> str:
+    return library().mla_status_string(int(status)).decode()
+
+
+def mla_version() -> int:
+    return library().mla_version()
+
+
+def mla_project_workspace_size(dims, n_tokens: int, d_q: int = 0) -> int:
+    n = ctypes.c_size_t(0)
+    _ok(library().mla_project_workspace_size(ctypes.byref(Dims.of(dims).c()), n_tokens, d_q, ctypes.byref(n)),
+        "mla_project_workspace_size")
+    return n.value
+
+
+def mla_decode_workspace_size(dims, batch: int, max_context: int) -> int:
+    n = ctypes.c_size_t(0)
+    _ok(library().mla_decode_workspace_size(ctypes.byref(Dims.of(dims).c()), batch, max_context, ctypes.byref(n)),
+        "mla_decode_workspace_size")
+    return n.value
+
+
+def mla_prefill_workspace_size(dims, batch: int, seq_len: int, max_context: int) -> int:
+    n = ctypes.c_size_t(0)
+    _ok(library().mla_prefill_workspace_size(ctypes.byref(Dims.of(dims).c()), batch, seq_len, max_context,
+                                             ctypes.byref(n)), "mla_prefill_workspace_size")
+    return n.value
+
+
+def mla_decode_path(dims, block_size: int = 64, paged: bool = True) -> int:
+    return library().mla_decode_path(ctypes.byref(Dims.of(dims).c()), block_size, int(paged))
+
+
+def mla_prefill_path(dims, block_size: int = 64, paged: bool = True) -> int:
+    return library().mla_prefill_path(ctypes.byref(Dims.of(dims).c()), block_size, int(paged))
+
+
+def mla_rope_latent_project(dims, h, w_dkv, w_kr, positions, slots, cache: Cache, qproj: Optional[QProj] = None,
+                            workspace=None, stream=None):
+    """Write [c_KV || RoPE(k)] of each token of h into its cache slot (see include/mla.h)."""
+    d = Dims.of(dims)
+    T, d_model = h.shape
+    dt = d.torch_dtype
+    _need(h, "h", (T, d_model), dt)
+    _need(w_dkv, "w_dkv", (d.d_c, d_model), dt)
+    _need(w_kr, "w_kr", (d.d_rope, d_model), dt)
+    _need(positions, "positions", (T,), torch.int32)
+    _need(slots, "slots", (T,), torch.int32)
+    rows = cache.rows
+    if rows.shape[-1] != d.row or rows.dtype != dt or not rows.is_contiguous():
+        raise ValueError("cache rows do not match dims")
+    qp = None
+    d_q = 0
+    if qproj is not None:
+        d_q = qproj.d_q
+        _need(qproj.w_dq, "w_dq", (d_q, d_model), dt)
+        _need(qproj.w_uq, "w_uq", (d.n_heads * d.d_nope, d_q), dt)
+        _need(qproj.w_qr, "w_qr", (d.n_heads * d.d_rope, d_q), dt)
+        _need(qproj.q_nope, "q_nope", (T, d.n_heads, d.d_nope), dt)
+        _need(qproj.q_pe, "q_pe", (T, d.n_heads, d.d_rope), dt)
+        qp = _QProj(d_q, qproj.w_dq.data_ptr(), qproj.w_uq.data_ptr(), qproj.w_qr.data_ptr(),
+                    qproj.q_nope.data_ptr(), qproj.q_pe.data_ptr())
+    ws, nbytes = _workspace(mla_project_workspace_size(d, T, d_q), h.device, workspace)
+    cc = cache.c()
+    _ok(library().mla_rope_latent_project(ctypes.byref(d.c()), T, d_model, h.data_ptr(), w_dkv.data_ptr(),
+                                          w_kr.data_ptr(), positions.data_ptr(), slots.data_ptr(), ctypes.byref(cc),
+                                          ctypes.byref(qp) if qp is not None else None,
+                                          ws.data_ptr() if ws is not None else None, nbytes, _stream(stream)),
+        "mla_rope_latent_project")
+
+
+def mla_decode(dims, q_nope, q_pe, w_uk, w_uv, cache: Cache, out=None, workspace=None, stream=None):
+    """One query per sequence over its whole cached context; returns out [B, H, d_v]."""
+    d = Dims.of(dims)
+    B = q_nope.shape[0]
+    dt = d.torch_dtype
+    _need(q_nope, "q_nope", (B, d.n_heads, d.d_nope), dt)
+    _need(q_pe, "q_pe", (B, d.n_heads, d.d_rope), dt)
+    _need(w_uk, "w_uk", (d.n_heads * d.d_nope, d.d_c), dt)
+    _need(w_uv, "w_uv", (d.n_heads * d.d_v, d.d_c), dt)
+    _check_cache(cache, d, B)
+    if out is None:
+        out = torch.empty((B, d.n_heads, d.d_v), dtype=dt, device=q_nope.device)
+    _need(out, "out", (B, d.n_heads, d.d_v), dt)
+    ws, nbytes = _workspace(mla_decode_workspace_size(d, B, cache.max_context), q_nope.device, workspace)
+    cc = cache.c()
+    _ok(library().mla_decode(ctypes.byref(d.c()), B, q_nope.data_ptr(), q_pe.data_ptr(), w_uk.data_ptr(),
+                             w_uv.data_ptr(), ctypes.byref(cc), out.data_ptr(),
+                             ws.data_ptr() if ws is not None else None, nbytes, _stream(stream)), "mla_decode")
+    return out
+
+
+def mla_prefill(dims, q_nope, q_pe, w_uk, w_uv, cache: Cache, out=None, workspace=None, stream=None):
+    """Causal attention of the last S tokens of each sequence; returns out [B, S, H, d_v]."""
+    d = Dims.of(dims)
+    B, S = q_nope.shape[:2]
+    dt = d.torch_dtype
+    _need(q_nope, "q_nope", (B, S, d.n_heads, d.d_nope), dt)
+    _need(q_pe, "q_pe", (B, S, d.n_heads, d.d_rope), dt)
+    _need(w_uk, "w_uk", (d.n_heads * d.d_nope, d.d_c), dt)
+    _need(w_uv, "w_uv", (d.n_heads * d.d_v, d.d_c), dt)
+    _check_cache(cache, d, B)
+    if out is None:
+        out = torch.empty((B, S, d.n_heads, d.d_v), dtype=dt, device=q_nope.device)
+    _need(out, "out", (B, S, d.n_heads, d.d_v), dt)
+    ws, nbytes = _workspace(mla_prefill_workspace_size(d, B, S, cache.max_context), q_nope.device, workspace)
+    cc = cache.c()
+    _ok(library().mla_prefill(ctypes.byref(d.c()), B, S, q_nope.data_ptr(), q_pe.data_ptr(), w_uk.data_ptr(),
+                              w_uv.data_ptr(), ctypes.byref(cc), out.data_ptr(),
+                              ws.data_ptr() if ws is not None else None, nbytes, _stream(stream)), "mla_prefill")
+    return out

@@ -275,3 +275,19 @@ WORKLOADS = {
     4: "bf16 ragged decode: B=32 H=128 L~U[1024,32768], shuffled 64-token pages",
     5: "bf16 causal prefill: B=4 S=4096 d_model=7168 d_q=1536 H=128, projections + attention",
 }
+
+
+# ----------------------------------------------------------- device copies --
+def to_torch(a: np.ndarray, device="cuda"):
+    """Device tensor of a generated array: uint16 bf16 bits -> torch.bfloat16,
+    float32 -> torch.float32, int32 stays int32. Bits are copied unchanged."""
+    import torch
+    if a.dtype == np.uint16:
+        return torch.from_numpy(a.view(np.int16).copy()).view(torch.bfloat16).to(device)
+    return torch.from_numpy(np.ascontiguousarray(a)).to(device)
+
+
+def from_torch(t) -> np.ndarray:
+    """Host float64 copy of a device tensor (bf16 widened exactly)."""
+    import torch
+    return t.detach().to("cpu", torch.float64).numpy()

@@ -1,0 +1,52 @@
+"""Shared helpers of the GPU tests: device copies of generated cases, calls
+through the binding, and the acceptance bars."""
+import numpy as np
+import torch
+
+import mla_latent_kv_09_amd as mla
+from synth import from_torch, to_torch
+
+
+def device_cache(cache, device="cuda"):
+    rows = to_torch(cache.pool, device)
+    lens = to_torch(cache.context_lens.astype(np.int32), device)
+    table = None if cache.block_table is None else to_torch(cache.block_table.astype(np.int32), device)
+    return mla.Cache(rows, lens, int(cache.context_lens.max()), table)
+
+
+def run_decode(case, device="cuda", workspace=None):
+    c = device_cache(case.cache, device)
+    out = mla.mla_decode(case.dims, to_torch(case.q_nope, device), to_torch(case.q_pe, device),
+                         to_torch(case.w_uk, device), to_torch(case.w_uv, device), c, workspace=workspace)
+    torch.cuda.synchronize()
+    return from_torch(out)
+
+
+def bar(dtype):
+    """(max-abs, normwise-relative, max-abs relative to max|ref|) bars."""
+    if dtype == "f32":
+        return 1e-4, 1e-4, 1e-4
+    return 2e-2, 1e-2, 5e-2
+
+
+def assert_parity(got, ref, dtype, what=""):
+    got = np.asarray(got, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    assert got.shape == ref.shape, (what, got.shape, ref.shape)
+    assert np.all(np.isfinite(got)), f"{what}: non-finite output"
+    d = np.abs(got - ref)
+    max_abs, rel_bar, peak_bar = bar(dtype)
+    rel = np.linalg.norm(got - ref) / max(np.linalg.norm(ref), 1e-30)
+    msg = f"{what}: max|d|={d.max():.3e} rel={rel:.3e} max|ref|={np.abs(ref).max():.3e}"
+    assert d.max() <= max_abs, msg
+    assert rel <= rel_bar, msg
+    assert d.max() <= peak_bar * np.abs(ref).max(), msg
+    return d.max(), rel
+
+
+def fails_bar(got, ref, dtype):
+    try:
+        assert_parity(got, ref, dtype)
+    except AssertionError:
+        return True
+    return False

@@ -1,0 +1,201 @@
+"""Parity of the HIP library with the CPU oracle, through the C ABI.
+
+Inputs are the seeded synthetic workloads; the oracle computes the plain
+definition (explicit K/V up-projection, two-pass softmax) in float64. Bars:
+fp32 max|d| <= 1e-4; bf16 max|d| <= 2e-2 plus normwise relative error <= 1e-2
+and max|d| <= 5% of max|ref|.
+"""
+import numpy as np
+import pytest
+import torch
+
+import mla_latent_kv_09_amd as mla
+import oracle
+from synth import Dims, from_torch, make_decode_case, make_project_case, to_torch, workload
+
+from gpu_helpers import assert_parity, device_cache, fails_bar, run_decode
+
+pytestmark = pytest.mark.gpu
+
+V3 = dict(d_c=512, d_rope=64, d_nope=128, d_v=128)
+
+
+def oracle_decode(case, rows=None):
+    c = case.cache
+    return oracle.decode(case.dims, case.q_nope, case.q_pe, case.w_uk, case.w_uv, c.pool, c.block_table,
+                         c.context_lens, batch_rows=rows)
+
+
+def _log(msg):
+    print(msg, flush=True)
+
+
+# ------------------------------------------------------------ tiny fp32 ----
+
+def test_workload1_tiny_fp32_project_then_decode():
+    _log("workload 1: tiny fp32 projection + decode")
+    case = workload(1)
+    d = case.dims
+    rows = torch.zeros((1, 64, d.row), dtype=torch.float32, device="cuda")
+    lens = torch.tensor([64], dtype=torch.int32, device="cuda")
+    cache = mla.Cache(rows, lens, 64, None)
+    mla.mla_rope_latent_project(d, to_torch(case.h), to_torch(case.w_dkv), to_torch(case.w_kr),
+                                to_torch(case.positions), to_torch(case.slots), cache)
+    out = mla.mla_decode(d, to_torch(case.q_nope), to_torch(case.q_pe), to_torch(case.w_uk),
+                         to_torch(case.w_uv), cache)
+    torch.cuda.synchronize()
+    ref_rows = oracle.latent_rows(case.h, case.w_dkv, case.w_kr, case.positions, store="f32")
+    assert np.abs(from_torch(rows)[0] - ref_rows).max() <= 1e-5
+    ref = oracle.decode(d, case.q_nope, case.q_pe, case.w_uk, case.w_uv, ref_rows[None], None,
+                        np.array([64], dtype=np.int32))
+    assert_parity(from_torch(out), ref, "f32", "workload 1")
+
+
+# --------------------------------------------------------- bf16 decode -----
+
+SMALL = [
+    ("H16 ragged tails", 16, [1, 63, 64, 65, 700], True),
+    ("H128 ragged tails", 128, [1, 129, 1000], True),
+    ("H128 identity pages", 128, [64, 2047], False),
+    ("H32 long", 32, [5000, 3], True),
+]
+
+
+@pytest.mark.parametrize("name,H,lens,shuffle", SMALL, ids=[s[0] for s in SMALL])
+def test_decode_small_bf16(name, H, lens, shuffle):
+    _log(f"decode {name}")
+    case = make_decode_case(100 + H, len(lens), Dims(H, **V3), lens, shuffle=shuffle)
+    assert_parity(run_decode(case), oracle_decode(case), "bf16", name)
+
+
+def test_decode_tiny_dims_bf16_and_f32():
+    for dt in ("bf16", "f32"):
+        for H, dc, dr, dn, dv, lens in ((3, 8, 2, 5, 7, [1, 9]), (5, 40, 16, 24, 8, [130, 64, 65])):
+            _log(f"decode tiny dims {dt} H={H} dc={dc}")
+            case = make_decode_case(7, len(lens), Dims(H, dc, dr, dn, dv, dtype=dt), lens, shuffle=True,
+                                    w_std=0.5)
+            assert_parity(run_decode(case), oracle_decode(case), dt, f"tiny {dt}")
+
+
+def test_decode_contiguous_layout_bf16():
+    _log("decode contiguous layout")
+    case = make_decode_case(8, 3, Dims(16, **V3), [100, 1, 77], paged=False)
+    assert_parity(run_decode(case), oracle_decode(case), "bf16", "contiguous")
+
+
+def test_decode_negative_controls_fail_the_bar():
+    """Mistakes planted in the oracle (on the CPU) must fail the bar against
+    the GPU output, which proves the bar can fail."""
+    _log("negative controls")
+    lens = [300, 129]
+    case = make_decode_case(9, 2, Dims(16, **V3), lens, shuffle=True)
+    got = run_decode(case)
+    ref = oracle_decode(case)
+    assert_parity(got, ref, "bf16", "control")
+    c = case.cache
+    # k_pe dropped
+    pool = c.pool.copy()
+    pool[..., 512:] = 0
+    bad = oracle.decode(case.dims, case.q_nope, case.q_pe, case.w_uk, case.w_uv, pool, c.block_table,
+                        c.context_lens)
+    assert fails_bar(got, bad, "bf16")
+    # last page skipped
+    short = (c.context_lens - (c.context_lens - 1) % 64 - 1).astype(np.int32)
+    short = np.maximum(short, 1)
+    bad = oracle.decode(case.dims, case.q_nope, case.q_pe, case.w_uk, case.w_uv, c.pool, c.block_table, short)
+    assert fails_bar(got, bad, "bf16")
+    # block table ignored (identity placement)
+    ident = np.zeros_like(c.block_table)
+    g = 0
+    for b, L in enumerate(c.context_lens):
+        n = (int(L) + 63) // 64
+        ident[b, :n] = np.arange(g, g + n)
+        g += n
+    bad = oracle.decode(case.dims, case.q_nope, case.q_pe, case.w_uk, case.w_uv, c.pool, ident, c.context_lens)
+    assert fails_bar(got, bad, "bf16")
+    # query rotated at L instead of L-1: shift q_pe by one more position
+    qpe = oracle.rope(oracle.widen(case.q_pe), 1)
+    bad = oracle.decode(case.dims, case.q_nope, qpe, case.w_uk, case.w_uv, c.pool, c.block_table, c.context_lens)
+    assert fails_bar(got, bad, "bf16")
+    # W_UV of the wrong head
+    wuv = np.roll(case.w_uv, 128, axis=0)
+    bad = oracle.decode(case.dims, case.q_nope, case.q_pe, case.w_uk, wuv, c.pool, c.block_table, c.context_lens)
+    assert fails_bar(got, bad, "bf16")
+
+
+def test_decode_is_deterministic():
+    _log("determinism")
+    case = make_decode_case(10, 4, Dims(128, **V3), [3000, 64, 1, 4097], shuffle=True)
+    a = run_decode(case)
+    b = run_decode(case)
+    assert np.array_equal(a, b)
+
+
+# ------------------------------------------------------- projection --------
+
+def test_project_with_query_path_then_prefill_small():
+    _log("projection + query path + prefill (small)")
+    dims = Dims(16, **V3)
+    case = make_project_case(11, batch=2, seq_len=100, d_model=256, dims=dims, d_q=96, shuffle=True)
+    T = case.n_tokens
+    nb = case.num_blocks
+    rows = torch.zeros((nb, 64, dims.row), dtype=torch.bfloat16, device="cuda")
+    lens = torch.full((2,), 100, dtype=torch.int32, device="cuda")
+    cache = mla.Cache(rows, lens, 100, to_torch(case.block_table))
+    qn = torch.empty((T, 16, 128), dtype=torch.bfloat16, device="cuda")
+    qp = torch.empty((T, 16, 64), dtype=torch.bfloat16, device="cuda")
+    qproj = mla.QProj(to_torch(case.w_dq), to_torch(case.w_uq), to_torch(case.w_qr), qn, qp)
+    mla.mla_rope_latent_project(dims, to_torch(case.h), to_torch(case.w_dkv), to_torch(case.w_kr),
+                                to_torch(case.positions), to_torch(case.slots), cache, qproj)
+    out = mla.mla_prefill(dims, qn.view(2, 100, 16, 128), qp.view(2, 100, 16, 64), to_torch(case.w_uk),
+                          to_torch(case.w_uv), cache)
+    torch.cuda.synchronize()
+    ref_rows = oracle.latent_rows(case.h, case.w_dkv, case.w_kr, case.positions)
+    got_rows = from_torch(rows)[case.slots // 64, case.slots % 64]
+    # rows are stored in bf16: allow one bf16 rounding step of the fp64 value
+    assert np.all(np.abs(got_rows - ref_rows) <= 2 ** -7 * np.abs(ref_rows) + 1e-3)
+    ref_qn, ref_qp = oracle.query_projection(case.h, case.w_dq, case.w_uq, case.w_qr, 16, 128, 64)
+    assert_parity(from_torch(qn), ref_qn, "bf16", "q_nope")
+    assert_parity(from_torch(qp), ref_qp, "bf16", "q_pe")
+    ref = oracle.prefill(dims, ref_qn.reshape(2, 100, 16, 128), ref_qp.reshape(2, 100, 16, 64), case.w_uk,
+                         case.w_uv, oracle.round_to(ref_rows, "bf16").reshape(2, 100, -1))
+    assert_parity(from_torch(out), ref, "bf16", "prefill")
+
+
+def test_chunked_prefill_over_a_cached_prefix():
+    """Queries that are the last S tokens of a longer context see the prefix."""
+    _log("chunked prefill")
+    dims = Dims(16, **V3)
+    L, S = 300, 70
+    case = make_decode_case(12, 2, dims, [L, L], shuffle=True)
+    rng = np.random.default_rng(3)
+    from synth import f32_to_bf16_bits
+    qn = f32_to_bf16_bits(rng.standard_normal((2, S, 16, 128)).astype(np.float32))
+    qp = f32_to_bf16_bits(rng.standard_normal((2, S, 16, 64)).astype(np.float32))
+    c = device_cache(case.cache)
+    out = mla.mla_prefill(dims, to_torch(qn), to_torch(qp), to_torch(case.w_uk), to_torch(case.w_uv), c)
+    torch.cuda.synchronize()
+    got = from_torch(out)
+    for s in (0, 1, 63, 64, 69):
+        lens = np.array([L - S + s + 1] * 2, dtype=np.int32)
+        ref = oracle.decode(dims, qn[:, s], qp[:, s], case.w_uk, case.w_uv, case.cache.pool,
+                            case.cache.block_table, lens)
+        assert_parity(got[:, s], ref, "bf16", f"chunked query {s}")
+
+
+# ------------------------------------------------- measured workloads ------
+
+def test_workload2_full():
+    _log("workload 2 (B=16 H=16 L=4096), all sequences")
+    case = workload(2)
+    assert_parity(run_decode(case), oracle_decode(case), "bf16", "workload 2")
+
+
+@pytest.mark.parametrize("k", [3, 4])
+def test_workload_3_4_full_size_sampled(k):
+    _log(f"workload {k}: full size on the GPU, oracle on sampled sequences")
+    case = workload(k)
+    got = run_decode(case)
+    lens = case.cache.context_lens
+    sample = sorted({0, int(np.argmax(lens)), int(np.argmin(lens)), case.batch - 1})
+    assert_parity(got[sample], oracle_decode(case, rows=sample), "bf16", f"workload {k}")
