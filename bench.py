@@ -1,0 +1,193 @@
+"""Benchmark of the MLA decode hot path on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload 3]
+
+One step is one mla_decode call (query absorption, split-context attention
+over the paged latent cache, log-sum-exp combine and per-head W_UV) for one
+new token of every sequence in the batch, on seeded synthetic inputs that are
+already resident in HBM. Prints one JSON line with the decode throughput,
+the roofline position of the dominant kernel (timed with HIP events recorded
+around each library launch during the timed region) and the CPU oracle timed
+on a bounded sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
+BF16_PEAK_TFLOPS = 2516.6      # MI355X dense bf16 MFMA, TFLOP/s
+CACHE_ROW_BYTES = 1152         # one cached token: (512 + 64) bf16
+
+WORKLOAD_NAMES = {
+    2: "mla_decode B=16 H=16 L=4096 d_c=512 d_rope=64 bf16, 64-token pages",
+    3: "mla_decode B=64 H=128 L=8192 d_c=512 d_rope=64 bf16, 64-token pages (DeepSeek-V3 shape)",
+    4: "mla_decode B=32 H=128 L~U[1024,32768] d_c=512 d_rope=64 bf16, shuffled 64-token pages",
+}
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", type=int, default=3, choices=sorted(WORKLOAD_NAMES))
+    ap.add_argument("--cpu-seconds", type=float, default=10.0, help="budget of the CPU oracle sample")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle leg")
+    return ap.parse_args()
+
+
+def profile_end(lib):
+    n_max, name_len = 16, 64
+    names = ctypes.create_string_buffer(n_max * name_len)
+    tot = (ctypes.c_double * n_max)()
+    cnt = (ctypes.c_int32 * n_max)()
+    n = ctypes.c_int32(0)
+    lib.mla_profile_end.argtypes = [ctypes.c_int32, ctypes.c_char_p, ctypes.c_int32,
+                                    ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_int32),
+                                    ctypes.POINTER(ctypes.c_int32)]
+    st = lib.mla_profile_end(n_max, names, name_len, tot, cnt, ctypes.byref(n))
+    if st != 0:
+        raise RuntimeError(f"mla_profile_end failed: {st}")
+    out = {}
+    for i in range(min(n.value, n_max)):
+        nm = names.raw[i * name_len:(i + 1) * name_len].split(b"\0", 1)[0].decode()
+        out[nm] = (tot[i], cnt[i])
+    return out
+
+
+def cpu_baseline(case, budget_s):
+    """The oracle as it stands, on whole sequences of the same workload, until
+    the time budget is spent (at least one sequence)."""
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        threads = len(os.sched_getaffinity(0))
+    c = case.cache
+    done, t0 = 0, time.perf_counter()
+    order = np.argsort(c.context_lens)[::-1] if case.batch > 1 else [0]
+    rows_done = []
+    for b in order[: case.batch]:
+        oracle.decode(case.dims, case.q_nope, case.q_pe, case.w_uk, case.w_uv, c.pool, c.block_table,
+                      c.context_lens, batch_rows=[int(b)])
+        done += 1
+        rows_done.append(int(b))
+        if time.perf_counter() - t0 >= budget_s:
+            break
+    dt = time.perf_counter() - t0
+    toks = int(sum(int(c.context_lens[b]) for b in rows_done))
+    return {"value": done / dt, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"{done} of {case.batch} sequences ({toks} cached tokens, all {case.dims.n_heads} heads), "
+                      f"float64 numpy, {dt:.1f} s"}
+
+
+def main():
+    args = parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}, WORLD_SIZE {world}); "
+              "this library has no multi-GPU path.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import mla_latent_kv_09_amd as mla
+    from synth import to_torch, workload
+
+    dev = "cuda:0"
+    t_gen = time.perf_counter()
+    case = workload(args.workload)
+    c = case.cache
+    cache = mla.Cache(to_torch(c.pool, dev), to_torch(c.context_lens, dev), int(c.context_lens.max()),
+                      to_torch(c.block_table, dev))
+    q_nope, q_pe = to_torch(case.q_nope, dev), to_torch(case.q_pe, dev)
+    w_uk, w_uv = to_torch(case.w_uk, dev), to_torch(case.w_uv, dev)
+    d = mla.Dims.of(case.dims)
+    B, H = case.batch, d.n_heads
+    ws_bytes = mla.mla_decode_workspace_size(d, B, cache.max_context)
+    ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
+    out = torch.empty((B, H, d.d_v), dtype=torch.bfloat16, device=dev)
+    torch.cuda.synchronize()
+    print(f"[bench] workload {args.workload}: inputs ready in {time.perf_counter() - t_gen:.1f} s; "
+          f"decode path {mla.mla_decode_path(d)}; workspace {ws_bytes / 1e6:.1f} MB", file=sys.stderr, flush=True)
+
+    def step():
+        mla.mla_decode(d, q_nope, q_pe, w_uk, w_uv, cache, out=out, workspace=ws)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    lib = mla.library()
+    stream = torch.cuda.current_stream()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    lib.mla_profile_begin()
+    torch.cuda.synchronize()
+    ev0.record(stream)
+    for _ in range(args.steps):
+        step()
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    kern = profile_end(lib)
+    ms = ev0.elapsed_time(ev1) / args.steps
+
+    sum_l = int(c.context_lens.astype(np.int64).sum())
+    cache_bytes = sum_l * CACHE_ROW_BYTES
+    weight_bytes = 2 * H * 128 * 512 * 2
+    io_bytes = B * H * (128 + 64 + 128) * 2 + B * 4
+    step_bytes = cache_bytes + weight_bytes + io_bytes
+    step_flop = 2.0 * H * sum_l * (576 + 512) + 2 * 2.0 * B * H * 128 * 512
+    split_name = "mla_decode_split"
+    if split_name not in kern:
+        raise RuntimeError(f"no timing for {split_name}: {kern}")
+    split_ms = kern[split_name][0] / kern[split_name][1]
+    achieved = cache_bytes / (split_ms * 1e-3) / 1e9
+    kernels_us = {k: round(v[0] / v[1] * 1e3, 2) for k, v in kern.items()}
+
+    tokens_per_s = B / (ms * 1e-3)
+    line = {
+        "metric": "MLA decode tokens/s + achieved HBM GB/s / MFMA % of peak, 1×MI355X",
+        "value": round(tokens_per_s, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded N(0,1) cache rows and queries, weights std 1/sqrt(512))",
+        "config": {"workload": WORKLOAD_NAMES[args.workload], "batch": B, "heads": H,
+                   "cached_tokens": sum_l, "max_context": int(cache.max_context), "page": 64,
+                   "parallelism": "none (1 GPU)"},
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                     "kernel": split_name, "kernel_us": round(split_ms * 1e3, 2),
+                     "algorithmic_bytes": cache_bytes,
+                     "bytes_rule": f"{CACHE_ROW_BYTES} B per cached token x {sum_l} tokens"},
+        "step": {"algorithmic_bytes": step_bytes, "algorithmic_flop": step_flop,
+                 "hbm_GB_per_s": round(step_bytes / (ms * 1e-3) / 1e9, 1),
+                 "hbm_frac": round(step_bytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                 "mfma_TFLOP_per_s": round(step_flop / (ms * 1e-3) / 1e12, 1),
+                 "mfma_frac": round(step_flop / (ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 4),
+                 "kernels_us": kernels_us},
+    }
+    if not args.no_cpu:
+        line["cpu_baseline"] = cpu_baseline(case, args.cpu_seconds)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -179,6 +179,18 @@ const char* mla_status_string(mla_status status);
 int32_t mla_decode_path(const mla_dims* dims, int32_t block_size, int32_t paged);
 int32_t mla_prefill_path(const mla_dims* dims, int32_t block_size, int32_t paged);
 
+/* Per-kernel timing for measurement tools. After mla_profile_begin, every
+ * kernel the library launches is bracketed by HIP events on its stream (this
+ * adds no synchronisation). mla_profile_end stops recording, waits for the
+ * recorded events, and reports, per kernel name, the summed duration in ms
+ * and the launch count: names is a caller buffer of max_kernels entries of
+ * name_len chars each; *n_kernels receives the number of distinct kernels
+ * (entries beyond max_kernels are dropped). Host-side state is shared by all
+ * threads of the process. */
+mla_status mla_profile_begin(void);
+mla_status mla_profile_end(int32_t max_kernels, char* names, int32_t name_len, double* total_ms,
+                           int32_t* launches, int32_t* n_kernels);
+
 /* Library version, major * 10000 + minor * 100 + patch. */
 int32_t mla_version(void);
 

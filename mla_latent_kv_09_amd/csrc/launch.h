@@ -7,6 +7,19 @@
 
 namespace mla {
 
+// Records HIP events around the launches in its scope when profiling is on
+// (mla_profile_begin); a no-op otherwise.
+class ProfScope {
+ public:
+  ProfScope(const char* name, hipStream_t s);
+  ~ProfScope();
+
+ private:
+  const char* name_;
+  hipStream_t s_;
+  void* start_;
+};
+
 // Where cache row (b, t) lives. Paged: rows + (table[b][t / bs] * bs + t % bs) * R.
 // Contiguous: rows + (b * seq_stride + t) * R.
 struct CacheView {

@@ -70,7 +70,7 @@ def test_decode_small_bf16(name, H, lens, shuffle):
 
 def test_decode_tiny_dims_bf16_and_f32():
     for dt in ("bf16", "f32"):
-        for H, dc, dr, dn, dv, lens in ((3, 8, 2, 5, 7, [1, 9]), (5, 40, 16, 24, 8, [130, 64, 65])):
+        for H, dc, dr, dn, dv, lens in ((3, 8, 8, 5, 7, [1, 9]), (5, 40, 16, 24, 8, [130, 64, 65])):
             _log(f"decode tiny dims {dt} H={H} dc={dc}")
             case = make_decode_case(7, len(lens), Dims(H, dc, dr, dn, dv, dtype=dt), lens, shuffle=True,
                                     w_std=0.5)
@@ -199,3 +199,36 @@ def test_workload_3_4_full_size_sampled(k):
     lens = case.cache.context_lens
     sample = sorted({0, int(np.argmax(lens)), int(np.argmin(lens)), case.batch - 1})
     assert_parity(got[sample], oracle_decode(case, rows=sample), "bf16", f"workload {k}")
+
+
+# ------------------------------------------------- MFMA path specifics -----
+
+def test_mfma_path_is_selected_for_the_v3_shape():
+    assert mla.mla_decode_path(Dims(128, **V3)) == 1
+    assert mla.mla_decode_path(Dims(16, **V3)) == 1
+    assert mla.mla_decode_path(Dims(16, **V3), paged=False) == 0
+    assert mla.mla_decode_path(Dims(4, 32, 8, 16, 16, dtype="f32")) == 0
+
+
+@pytest.mark.parametrize("H", [1, 48, 100])
+def test_decode_odd_head_counts(H):
+    _log(f"decode H={H}")
+    case = make_decode_case(200 + H, 3, Dims(H, **V3), [129, 1, 640], shuffle=True)
+    assert_parity(run_decode(case), oracle_decode(case), "bf16", f"H={H}")
+
+
+def test_decode_large_score_growth_takes_the_rescale_branch():
+    """The k_pe slice of later pages is scaled up (1x -> 6x along the context),
+    so the running max of the scores grows far beyond the lazy-rescale
+    threshold inside one page run, while the values (c_KV) keep their scale."""
+    _log("decode rescale branch")
+    from synth import bf16_bits_to_f32, f32_to_bf16_bits
+    case = make_decode_case(13, 2, Dims(128, **V3), [700, 1500], shuffle=True)
+    pool = bf16_bits_to_f32(case.cache.pool)
+    table = case.cache.block_table
+    for b, L in enumerate(case.cache.context_lens):
+        n = (int(L) + 63) // 64
+        for p in range(n):
+            pool[table[b, p], :, 512:] *= 1.0 + 5.0 * p / n
+    case.cache.pool = f32_to_bf16_bits(pool)
+    assert_parity(run_decode(case), oracle_decode(case), "bf16", "rescale")
