@@ -111,76 +111,134 @@ WsLayout ws_layout(int H, int batch, int splits) {
 }
 
 // ------------------------------------------------------------ k_absorb ----
-// grid (H, DC / 64); 4 waves. Block (h, c0): Qt[:, h, c0 .. c0+63] for every
-// sequence, as a [B x 128] x [128 x 64] MFMA product with W_UK,h staged in LDS
-// and read transposed; block (h, 0) also writes the rotated q_pe slice.
+// grid (H, DC / 64); 4 waves. Block (h, c0) forms Qt[:, h, c0 .. c0+63] for
+// every sequence as the transposed product Qt^T[c, b] = sum_j W_UK[h*128+j, c]
+// q_nope[b, h, j]: the 128 x 64 slice of W_UK,h is staged in LDS and read
+// transposed (as the A operand); each lane then holds 4 consecutive columns of
+// one sequence and stores them with one 8-byte write. Block (h, 0) also writes
+// the rotated, scaled q_pe slice.
 __global__ __launch_bounds__(256) void k_absorb(int B, int H, const bf16* __restrict__ q_nope,
                                                 const bf16* __restrict__ q_pe, const bf16* __restrict__ w_uk,
                                                 const int32_t* __restrict__ ctx_lens, float qscale, float base,
                                                 bf16* __restrict__ qt) {
   constexpr int LD = 72;  // padded row (144 B) keeps the transposed reads conflict-free
+  constexpr int BT_CHUNK = 4;  // sequence tiles whose query loads are in flight together
   __shared__ __attribute__((aligned(16))) bf16 wt[DN * LD];
   const int h = blockIdx.x, c0 = blockIdx.y * 64;
-  for (int i = threadIdx.x; i < DN * 8; i += 256) {
-    const int j = i >> 3, ch = i & 7;
-    *(u32x4*)&wt[j * LD + ch * 8] = *(const u32x4*)(w_uk + (size_t)(h * DN + j) * DC + c0 + ch * 8);
+  const int w = threadIdx.x >> 6, lane = threadIdx.x & 63, i16 = lane & 15, G = lane >> 4;
+  // every independent load first: the W_UK slice and the first chunk of queries
+  u32x4 wr[DN * 8 / 256];
+#pragma unroll
+  for (int u = 0; u < DN * 8 / 256; ++u) {
+    const int i = threadIdx.x + 256 * u, j = i >> 3, ch = i & 7;
+    wr[u] = *(const u32x4*)(w_uk + (size_t)(h * DN + j) * DC + c0 + ch * 8);
+  }
+  auto load_q = [&](int bt0, u32x4 (&qv)[BT_CHUNK][DN / 32]) {
+#pragma unroll
+    for (int t = 0; t < BT_CHUNK; ++t)
+#pragma unroll
+      for (int ks = 0; ks < DN / 32; ++ks) {
+        const int b = (bt0 + t) * 16 + i16;
+        qv[t][ks] = b < B ? *(const u32x4*)(q_nope + ((size_t)b * H + h) * DN + 32 * ks + 8 * G) : (u32x4){0, 0, 0, 0};
+      }
+  };
+  u32x4 qv[BT_CHUNK][DN / 32];
+  load_q(0, qv);
+#pragma unroll
+  for (int u = 0; u < DN * 8 / 256; ++u) {
+    const int i = threadIdx.x + 256 * u, j = i >> 3, ch = i & 7;
+    *(u32x4*)&wt[j * LD + ch * 8] = wr[u];
   }
   __syncthreads();
-  const int w = threadIdx.x >> 6, lane = threadIdx.x & 63, i16 = lane & 15, G = lane >> 4;
   const LDS_AS char* wbase = (const LDS_AS char*)wt;
-  for (int mt = w; mt * 16 < B; mt += 4) {
-    f32x4 acc[4] = {};
-    const int brow = mt * 16 + i16;
+  // A fragments of column tile w (columns c0 + 16w .. +15), all 4 K-steps
+  bf16x8_t af[DN / 32];
 #pragma unroll
-    for (int ks = 0; ks < DN / 32; ++ks) {
-      u32x4 av = {0, 0, 0, 0};
-      if (brow < B) av = *(const u32x4*)(q_nope + ((size_t)brow * H + h) * DN + 32 * ks + 8 * G);
-      const bf16x8_t a = as_bf16x8(av);
+  for (int ks = 0; ks < DN / 32; ++ks) {
+    const int k0 = 32 * ks + 8 * G, col = 16 * w + 4 * (i16 & 3);
+    af[ks] = cat_tr(tr_read(wbase + ((k0 + (i16 >> 2)) * LD + col) * 2),
+                    tr_read(wbase + ((k0 + 4 + (i16 >> 2)) * LD + col) * 2));
+  }
+  for (int bt0 = 0; bt0 * 16 < B; bt0 += BT_CHUNK) {
+    u32x4 cur[BT_CHUNK][DN / 32];
 #pragma unroll
-      for (int nt = 0; nt < 4; ++nt) {
-        const int k0 = 32 * ks + 8 * G, col = 16 * nt + 4 * (i16 & 3);
-        const short4_t r1 = tr_read(wbase + ((k0 + (i16 >> 2)) * LD + col) * 2);
-        const short4_t r2 = tr_read(wbase + ((k0 + 4 + (i16 >> 2)) * LD + col) * 2);
-        acc[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, cat_tr(r1, r2), acc[nt], 0, 0, 0);
+    for (int t = 0; t < BT_CHUNK; ++t)
+#pragma unroll
+      for (int ks = 0; ks < DN / 32; ++ks) cur[t][ks] = qv[t][ks];
+    if ((bt0 + BT_CHUNK) * 16 < B) load_q(bt0 + BT_CHUNK, qv);
+#pragma unroll
+    for (int t = 0; t < BT_CHUNK; ++t) {
+      const int b = (bt0 + t) * 16 + i16;
+      f32x4 acc = {};
+#pragma unroll
+      for (int ks = 0; ks < DN / 32; ++ks)
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[ks], as_bf16x8(cur[t][ks]), acc, 0, 0, 0);
+      if (b < B) {
+        typedef __attribute__((ext_vector_type(4))) __bf16 bf16x4_t;
+        const bf16x4_t v = {(__bf16)(acc[0] * qscale), (__bf16)(acc[1] * qscale), (__bf16)(acc[2] * qscale),
+                            (__bf16)(acc[3] * qscale)};
+        *(bf16x4_t*)(qt + ((size_t)b * H + h) * ROW + c0 + 16 * w + 4 * G) = v;
       }
     }
-#pragma unroll
-    for (int nt = 0; nt < 4; ++nt)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int b = mt * 16 + 4 * G + r;
-        if (b < B) qt[((size_t)b * H + h) * ROW + c0 + 16 * nt + i16] = f2bf(acc[nt][r] * qscale);
-      }
   }
   if (blockIdx.y == 0) {
-    for (int idx = threadIdx.x; idx < B * (DR / 2); idx += 256) {
-      const int b = idx / (DR / 2), i = idx % (DR / 2);
-      const int pos = ctx_lens[b] - 1;
-      double sn, cs;
-      sincos(rope_angle(pos, i, DR, base), &sn, &cs);
+    // thread -> pair i = tid % 32 (fixed), sequences tid / 32, +8, ...
+    const int i = threadIdx.x & (DR / 2 - 1);
+    const double theta = pow((double)base, -2.0 * (double)i / (double)DR);
+    for (int b = threadIdx.x / (DR / 2); b < B; b += 256 / (DR / 2)) {
+      const double ang = (double)(ctx_lens[b] - 1) * theta;
+      // reduce to [-pi, pi] in double, then single-precision sin/cos
+      const float r = (float)(ang - 6.283185307179586 * rint(ang * 0.15915494309189535));
+      float sn, cs;
+      sincosf(r, &sn, &cs);
       const bf16* src = q_pe + ((size_t)b * H + h) * DR + 2 * i;
       const float x0 = bf2f(src[0]), x1 = bf2f(src[1]);
-      bf16* dst = qt + ((size_t)b * H + h) * ROW + DC + 2 * i;
-      dst[0] = f2bf((x0 * (float)cs - x1 * (float)sn) * qscale);
-      dst[1] = f2bf((x0 * (float)sn + x1 * (float)cs) * qscale);
+      typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2_t;
+      const bf16x2_t v = {(__bf16)((x0 * cs - x1 * sn) * qscale), (__bf16)((x0 * sn + x1 * cs) * qscale)};
+      *(bf16x2_t*)(qt + ((size_t)b * H + h) * ROW + DC + 2 * i) = v;
     }
   }
 }
 
 // ------------------------------------------------------------- k_split ----
-// grid (splits, B); 256 threads. Wave w owns heads 32w .. 32w+31 (lanes of
-// heads >= H compute on a copy of head H-1 and store nothing); every wave
-// streams a quarter of each page. Partials per (head, sequence, split):
-// O (512 fp32, unnormalised, relative to max m) and (m, l), log2 domain.
+// grid (splits, B); 256 threads (4 waves); one block per (sequence, run of
+// pages). The run is walked in tiles of 32 cache rows (half a page, 36 KB).
 //
-// Registers per lane: the latent part of the query (32 steps x 4 = 128) and
-// the output accumulators (16 tiles x 16 = 256) stay resident; the query's
-// 64-wide RoPE slice lives in LDS (16 KB next to the two 72 KB page buffers)
-// and the softmax runs per 32-token half page, so scores and probabilities
-// take 16 + 8 registers.
-constexpr int QR_BYTES = MAX_HEADS * DR * 2;  // 16 KB
-constexpr int LAT_STEPS = DC / 16;            // 32 MFMA steps over the latent columns
-constexpr int ROPE_STEPS = DR / 16;           // 4 steps over the RoPE columns
+// Work split inside the block, per tile:
+//   scores    wave w owns heads 32w .. 32w+31: S^T[t, h] = row_t . Qt[h]
+//             (36 MFMA steps of K = 16 over the 576 columns), then the online
+//             softmax of those heads (running max m and sum l stay with the
+//             owner). The probabilities P (bf16) and each head's rescale
+//             factor go to LDS.
+//   values    wave w owns latent columns 128w .. 128w+127 of every head:
+//             O^T[c, h] += V^T[c, t] P[t, h] (4 column tiles x 4 head tiles x
+//             2 steps). Each value fragment, read once from LDS, feeds four
+//             MFMAs; so does each P fragment.
+// Rows stream HBM -> LDS with direct 16-byte loads into a ring of three tile
+// slots: while tile i is computed, tiles i+1 and i+2 are in flight.
+//
+// Partials per (head, sequence, split): O (512 fp32, unnormalised, relative to
+// the head's reference max m) and (m, l), both in the log2 domain.
+constexpr int TILE = 32;                                  // rows per tile
+constexpr int TILE_BYTES = TILE * ROW_BYTES;              // 36864
+constexpr int TILE_LOADS = TILE * ROW_CHUNKS / SPLIT_THREADS;  // 9 per lane
+constexpr int N_SLOTS = 3;
+constexpr int QR_BYTES = MAX_HEADS * DR * 2;              // 16 KB: RoPE slice of Qt
+constexpr int PB_BYTES = MAX_HEADS * TILE * 2;            // 8 KB: P of one tile
+constexpr int LAT_STEPS = DC / 16;                        // 32 score steps over c_KV
+constexpr int ROPE_STEPS = DR / 16;                       // 4 score steps over k_pe
+constexpr int SPLIT_LDS = N_SLOTS * TILE_BYTES + QR_BYTES + PB_BYTES + MAX_HEADS * 4;
+
+// s_waitcnt with only vmcnt constrained (gfx9 encoding: vmcnt in bits 3:0 and
+// 15:14, expcnt 6:4 and lgkmcnt 11:8 left at their maxima).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x0F70);
+}
+
+// Workgroup barrier for LDS traffic only. __syncthreads() also waits for all
+// outstanding global loads (vmcnt 0), which would drain the tile prefetch.
+__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
 
 __global__ __launch_bounds__(SPLIT_THREADS, 1) void k_split(int H, int B, int splits, int pps,
                                                             const bf16* __restrict__ qt,
@@ -188,69 +246,77 @@ __global__ __launch_bounds__(SPLIT_THREADS, 1) void k_split(int H, int B, int sp
                                                             const int32_t* __restrict__ block_table,
                                                             int max_blocks, const int32_t* __restrict__ ctx_lens,
                                                             float* __restrict__ part_o, float* __restrict__ part_ml) {
-  __shared__ __attribute__((aligned(1024))) char lds[2 * PAGE_BYTES + QR_BYTES];
+  __shared__ __attribute__((aligned(1024))) char lds[SPLIT_LDS];
+  char* const qr = lds + N_SLOTS * TILE_BYTES;
+  char* const pb = qr + QR_BYTES;
+  float* const ab = (float*)(pb + PB_BYTES);
   const int split = blockIdx.x, b = blockIdx.y;
   const int L = ctx_lens[b];
-  const int n_pages = (L + PAGE - 1) / PAGE;
-  const int p0 = split * pps;
-  const int p1 = min(p0 + pps, n_pages);
-  if (p0 >= n_pages) return;
-  const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int hl = lane & 31, g = lane >> 5;
-  const int h = w * 32 + hl;
+  const int t_begin = split * pps * PAGE;
+  const int t_end = min(t_begin + pps * PAGE, L);
+  if (t_begin >= t_end) return;
+  const int n_tiles = (t_end - t_begin + TILE - 1) / TILE;
+  // the wave index is uniform: keep it (and the LDS bases derived from it) in SGPRs
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
+  const int hl = lane & 31, g = lane >> 5, i16 = lane & 15, G = lane >> 4;
+  const int h_own = w * 32 + hl;  // head of this lane in the score phase
   const int32_t* table = block_table + (size_t)b * max_blocks;
-  char* const qr = lds + 2 * PAGE_BYTES;
 
-  // Streams page p into buffer buf: 18 direct-to-LDS 16-byte loads per lane.
-  // Instruction k of wave w fills LDS chunks [(w*18+k)*64, +64) in order; the
-  // lane picks the global chunk that belongs at its (swizzled) position.
-  auto load_page = [&](int p, int buf) {
-    const char* src = (const char*)(rows + (size_t)table[p] * PAGE * ROW);
+  // Streams tile i into ring slot i % 3: 9 direct-to-LDS 16-byte loads per
+  // lane. Instruction k of wave w fills slot chunks [(w*9+k)*64, +64) in
+  // order; each lane picks the global chunk that belongs at its (swizzled)
+  // position.
+  auto load_tile = [&](int i) {
+    const int t0 = t_begin + i * TILE;
+    const char* src = (const char*)(rows + ((size_t)table[t0 / PAGE] * PAGE + (t0 % PAGE)) * ROW);
+    char* dst = lds + (i % N_SLOTS) * TILE_BYTES;
+    int ln = lane;
+    asm volatile("" : "+v"(ln));  // recompute the offsets per tile instead of holding 9 registers
 #pragma unroll
-    for (int k = 0; k < LOADS_PER_THREAD; ++k) {
-      const int base = (w * LOADS_PER_THREAD + k) * 64;
-      const int pos = base + lane;
+    for (int k = 0; k < TILE_LOADS; ++k) {
+      const int base = (w * TILE_LOADS + k) * 64;
+      const int pos = base + ln;
       const int t = pos / ROW_CHUNKS, jp = pos - t * ROW_CHUNKS;
       const uint32_t off = (uint32_t)(t * ROW_BYTES + ((jp ^ swz(t)) << 4));
-      __builtin_amdgcn_global_load_lds((const void*)(src + off), (LDS_AS void*)(lds + buf * PAGE_BYTES + base * 16),
-                                       16, 0, 0);
+      __builtin_amdgcn_global_load_lds((const void*)(src + off), (LDS_AS void*)(dst + base * 16), 16, 0, 0);
     }
   };
 
-  load_page(p0, 0);
-
-  // RoPE slice of the query for every head of the block, in LDS: head h's
-  // 16-byte chunk c (of 8) at h*128 + ((c ^ ((h >> 1) & 7)) * 16).
+  // RoPE slice of the query of every head, in LDS: head h's 16-byte chunk c
+  // (of 8) at h*128 + ((c ^ ((h >> 1) & 7)) * 16).
   for (int i = threadIdx.x; i < MAX_HEADS * (DR / 8); i += SPLIT_THREADS) {
     const int hh = i >> 3, c = i & 7;
     u32x4 v = {0, 0, 0, 0};
     if (hh < H) v = *(const u32x4*)(qt + ((size_t)b * H + hh) * ROW + DC + 8 * c);
     *(u32x4*)(qr + hh * 128 + ((c ^ ((hh >> 1) & 7)) << 4)) = v;
   }
-  // latent part of this lane's query: Qt[b, h, 16s + 8g .. +7], s < 32
-  // (lanes of heads >= H read head H-1; their columns are never stored)
+  // latent part of this lane's query: Qt[b, h_own, 16s + 8g .. +7], s < 32
+  // (lanes of heads >= H read head H-1; nothing of theirs is stored)
   bf16x8_t qf[LAT_STEPS];
   {
-    const bf16* q = qt + ((size_t)b * H + min(h, H - 1)) * ROW + 8 * g;
+    const bf16* q = qt + ((size_t)b * H + min(h_own, H - 1)) * ROW + 8 * g;
 #pragma unroll
     for (int s = 0; s < LAT_STEPS; ++s) qf[s] = as_bf16x8(*(const u32x4*)(q + 16 * s));
   }
-  f32x16 o[DC / 32];
+  wait_vmcnt<0>();  // query loads done: from here on only tile loads use vmcnt
+  load_tile(0);
+  if (n_tiles > 1) load_tile(1);
+
+  f32x16 o[4][4];  // [column tile][head tile]
 #pragma unroll
-  for (int i = 0; i < DC / 32; ++i) o[i] = (f32x16){};
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) o[i][j] = (f32x16){};
   float m_run = -INFINITY, l_run = 0.f;
 
-  // LDS byte offsets of this lane's operand reads, split into a lane part
-  // (below) and a compile-time part, so each read is one ds_read with an
-  // immediate offset. The swizzle only permutes the low three chunk bits and
-  // depends on row bits 1..3, so it folds into the lane part.
-  //  score operand (step s, tile mt): row 32mt + hl, chunk (2s + g) ^ swz(hl)
-  //    = qk_off[s % 4] + 32*mt*ROW_BYTES + (s / 4) * 128
+  // LDS byte offsets of this lane's operand reads (lane part; the rest is a
+  // compile-time immediate):
+  //  score operand, step s: row hl, chunk (2s + g) ^ swz(hl)
+  //    = qk_off[s % 4] + (s / 4) * 128
+  //  RoPE query operand, step r: head h_own, chunk 2r + g
   //  value operand (column tile ct, step j, half a/b): rows 16j + 4g + i16/4
-  //    (+8 for b), columns 32ct + 16(G%2) + 4(i16%4) .. +3
+  //    (+8 for b), columns 128w + 32ct + 16(G%2) + 4(i16%4) .. +3
   //    = pv_off[ct % 2][a/b] + 16*j*ROW_BYTES + (ct / 2) * 128
-  //  RoPE query operand (step r): head h, chunk 2r + g
-  const int i16 = lane & 15, G = lane >> 4;
   int qk_off[4], pv_off[2][2], qr_off[ROPE_STEPS];
   {
     const int x = swz(hl);
@@ -260,120 +326,152 @@ __global__ __launch_bounds__(SPLIT_THREADS, 1) void k_split(int H, int B, int sp
     const int y0 = 2 * (G & 1) + ((i16 & 3) >> 1), sub = 8 * (i16 & 1);
 #pragma unroll
     for (int par = 0; par < 2; ++par) {
-      pv_off[par][0] = ra * ROW_BYTES + (((4 * par + y0) ^ swz(ra)) << 4) + sub;
-      pv_off[par][1] = rb * ROW_BYTES + (((4 * par + y0) ^ swz(rb)) << 4) + sub;
+      pv_off[par][0] = ra * ROW_BYTES + (((4 * par + y0) ^ swz(ra)) << 4) + sub + w * 256;
+      pv_off[par][1] = rb * ROW_BYTES + (((4 * par + y0) ^ swz(rb)) << 4) + sub + w * 256;
     }
-    const int hq = min(h, MAX_HEADS - 1);
 #pragma unroll
-    for (int r = 0; r < ROPE_STEPS; ++r) qr_off[r] = hq * 128 + (((2 * r + g) ^ ((hq >> 1) & 7)) << 4);
+    for (int r = 0; r < ROPE_STEPS; ++r) qr_off[r] = h_own * 128 + (((2 * r + g) ^ ((h_own >> 1) & 7)) << 4);
   }
+  const LDS_AS char* qrl = (const LDS_AS char*)qr;
+  const LDS_AS char* pbl = (const LDS_AS char*)pb;
 
-  for (int p = p0; p < p1; ++p) {
-    const int buf = (p - p0) & 1;
-    wait_vmem_all();
-    __syncthreads();
-    if (p + 1 < p1) load_page(p + 1, buf ^ 1);
-    const LDS_AS char* page = (const LDS_AS char*)(lds + buf * PAGE_BYTES);
-    const LDS_AS char* qrl = (const LDS_AS char*)qr;
-    const int valid = L - p * PAGE;
+  for (int i = 0; i < n_tiles; ++i) {
+    if (i + 1 < n_tiles) wait_vmcnt<TILE_LOADS>();  // tile i landed, tile i+1 may fly
+    else wait_vmcnt<0>();
+    lds_barrier();  // tile i visible to all; slot (i+2)%3 and P/alpha buffers free
+    if (i + 2 < n_tiles) load_tile(i + 2);
+    const LDS_AS char* tile = (const LDS_AS char*)(lds + (i % N_SLOTS) * TILE_BYTES);
 
+    // ---- scores of this wave's 32 heads over the tile's 32 rows ----
+    f32x16 sc = {};
+    {
+      u32x4 fa[2][4], fb[2][4];
+      auto qk_load = [&](int grp, int slot) {
 #pragma unroll
-    for (int mt = 0; mt < 2; ++mt) {
-      // scores S^T[t, h] of the 32 rows 32mt .. 32mt+31
-      f32x16 sc = {};
-#pragma unroll
-      for (int s = 0; s < ROW / 16; ++s) {
-        const u32x4 a =
-            *(const LDS_AS u32x4*)(page + qk_off[s & 3] + (32 * mt * ROW_BYTES + (s >> 2) * 128));
-        const bf16x8_t bq = s < LAT_STEPS ? qf[s < LAT_STEPS ? s : 0]
-                                          : as_bf16x8(*(const LDS_AS u32x4*)(qrl + qr_off[(s - LAT_STEPS) & 3]));
-        sc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a), bq, sc, 0, 0, 0);
-        if ((s & 3) == 3) __builtin_amdgcn_sched_barrier(0);
-      }
-      // mask rows past the context (last page only)
-      if (valid < PAGE) {
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int t = 32 * mt + 8 * (r >> 2) + 4 * g + (r & 3);
-          if (t >= valid) sc[r] = -INFINITY;
+        for (int u = 0; u < 4; ++u) {
+          fa[slot][u] = *(const LDS_AS u32x4*)(tile + qk_off[u] + grp * 128);
+          if (4 * grp + u >= LAT_STEPS) fb[slot][u] = *(const LDS_AS u32x4*)(qrl + qr_off[u]);
         }
-      }
-      float mx = -INFINITY;
+      };
+      qk_load(0, 0);
 #pragma unroll
-      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sc[r]);
-      mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-      // Lazy rescaling: the reference max only moves when the tile max exceeds
-      // it by more than 8 (so p <= 2^8), so most tiles skip the rescale. A
-      // fully masked tile has mx = -inf and never moves it.
-      // A lane's first tile only sets the reference (its O and l are still 0).
-      float alpha = 1.f;
-      if (mx > m_run + 8.f) {
-        if (m_run != -INFINITY) alpha = exp2f(m_run - mx);
-        m_run = mx;
-      }
-      if (__ballot(alpha != 1.f)) {
-        l_run *= alpha;
+      for (int grp = 0; grp < ROW / 64; ++grp) {
+        if (grp + 1 < ROW / 64) qk_load(grp + 1, (grp + 1) & 1);
+        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-        for (int i = 0; i < DC / 32; ++i)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            float x = o[i][r];
-            scale_acc(x, alpha);
-            o[i][r] = x;
-          }
+        for (int u = 0; u < 4; ++u) {
+          const int s = 4 * grp + u;
+          const bf16x8_t bq = s < LAT_STEPS ? qf[s < LAT_STEPS ? s : 0] : as_bf16x8(fb[grp & 1][u]);
+          sc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(fa[grp & 1][u]), bq, sc, 0, 0, 0);
+        }
+        __builtin_amdgcn_sched_barrier(0);
       }
-      // probabilities as the PV operand: step jj covers rows 32mt + 16jj .. +15
-      bf16x8_t pf[2];
+    }
+    // mask rows past the context (last tile only); lane rows: 8(r/4) + 4g + r%4
+    const int valid = t_end - (t_begin + i * TILE);
+    if (valid < TILE) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r)
+        if (8 * (r >> 2) + 4 * g + (r & 3) >= valid) sc[r] = -INFINITY;
+    }
+    // ---- online softmax of the owned heads ----
+    float mx = sc[0];
+#pragma unroll
+    for (int r = 1; r < 16; ++r) mx = fmaxf(mx, sc[r]);
+    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+    // Lazy rescaling: the reference max only moves when the tile max exceeds
+    // it by more than 8 (so p <= 2^8); a lane's first tile just sets it.
+    float alpha = 1.f;
+    if (mx > m_run + 8.f) {
+      if (m_run != -INFINITY) alpha = __builtin_amdgcn_exp2f(m_run - mx);
+      m_run = mx;
+    }
+    l_run *= alpha;
+    {
       float lsum = 0.f;
+      // P fragment (head tile w, step j, lane group g, head hl): the 8 rows
+      // 16j + 8(k/4) + 4g + k%4 = this lane's registers 8j .. 8j+7
 #pragma unroll
-      for (int jj = 0; jj < 2; ++jj) {
-        uint32_t pk[4];
+      for (int j = 0; j < 2; ++j) {
+        bf16x8_t pk;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const float x0 = exp2f(sc[8 * jj + 2 * e] - m_run);
-          const float x1 = exp2f(sc[8 * jj + 2 * e + 1] - m_run);
-          lsum += x0 + x1;
-          pk[e] = pack_bf16x2(x0, x1);
+        for (int k = 0; k < 8; ++k) {
+          const float e = __builtin_amdgcn_exp2f(sc[8 * j + k] - m_run);
+          lsum += e;
+          pk[k] = (__bf16)e;
         }
-        const u32x4 v = {pk[0], pk[1], pk[2], pk[3]};
-        pf[jj] = as_bf16x8(v);
+        *(LDS_AS bf16x8_t*)((LDS_AS char*)pb + (w * 2 + j) * 1024 + lane * 16) = pk;
       }
       l_run += lsum;
-      // O^T[c, h] += V^T[c, t] P[t, h]; V^T fragments by transposed LDS reads
-      // (lane i of a 16-lane group receives 4 consecutive rows of column n0 + i).
+    }
+    if (g == 0) ab[h_own] = alpha;
+    lds_barrier();  // P and alpha of all heads visible
+
+    // ---- rescale (rare), then O^T[c, h] += V^T[c, t] P[t, h] ----
+    float al[4];
 #pragma unroll
-      for (int ct = 0; ct < DC / 32; ++ct) {
+    for (int ht = 0; ht < 4; ++ht) al[ht] = ab[32 * ht + hl];
+    if (__ballot(al[0] != 1.f || al[1] != 1.f || al[2] != 1.f || al[3] != 1.f)) {
 #pragma unroll
-        for (int jj = 0; jj < 2; ++jj) {
-          const int k = 16 * (2 * mt + jj) * ROW_BYTES + (ct >> 1) * 128;
-          const short4_t r1 = tr_read(page + pv_off[ct & 1][0] + k);
-          const short4_t r2 = tr_read(page + pv_off[ct & 1][1] + k);
-          o[ct] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(cat_tr(r1, r2), pf[jj], o[ct], 0, 0, 0);
-        }
-        if (ct & 1) __builtin_amdgcn_sched_barrier(0);
+      for (int ct = 0; ct < 4; ++ct)
+#pragma unroll
+        for (int ht = 0; ht < 4; ++ht)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            float x = o[ct][ht][r];
+            scale_acc(x, al[ht]);
+            o[ct][ht][r] = x;
+          }
+    }
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      bf16x8_t va[4], pf[4];
+#pragma unroll
+      for (int ct = 0; ct < 4; ++ct) {
+        const int k = 16 * j * ROW_BYTES + (ct >> 1) * 128;
+        va[ct] = cat_tr(tr_read(tile + pv_off[ct & 1][0] + k), tr_read(tile + pv_off[ct & 1][1] + k));
       }
+#pragma unroll
+      for (int ht = 0; ht < 4; ++ht) pf[ht] = *(const LDS_AS bf16x8_t*)(pbl + (ht * 2 + j) * 1024 + lane * 16);
+#pragma unroll
+      for (int ct = 0; ct < 4; ++ct)
+#pragma unroll
+        for (int ht = 0; ht < 4; ++ht)
+          o[ct][ht] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[ct], pf[ht], o[ct][ht], 0, 0, 0);
     }
   }
-  if (h >= H) return;
+
+  // ---- partials: (m, l) by the head owner, O slices by the column owner ----
   l_run += __shfl_xor(l_run, 32, 64);
-  const size_t prow = ((size_t)h * B + b) * splits + split;
-  if (g == 0) {
+  if (g == 0 && h_own < H) {
+    const size_t prow = ((size_t)h_own * B + b) * splits + split;
     part_ml[prow * 2] = m_run;
     part_ml[prow * 2 + 1] = l_run;
   }
-  float* po = part_o + prow * DC;
 #pragma unroll
-  for (int ct = 0; ct < DC / 32; ++ct)
+  for (int ht = 0; ht < 4; ++ht) {
+    const int hh = 32 * ht + hl;
+    if (hh >= H) continue;
+    float* po = part_o + (((size_t)hh * B + b) * splits + split) * DC + 128 * w;
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const f32x4 v = {o[ct][4 * q], o[ct][4 * q + 1], o[ct][4 * q + 2], o[ct][4 * q + 3]};
-      *(f32x4*)(po + 32 * ct + 8 * q + 4 * g) = v;
-    }
+    for (int ct = 0; ct < 4; ++ct)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const f32x4 v = {o[ct][ht][4 * q], o[ct][ht][4 * q + 1], o[ct][ht][4 * q + 2], o[ct][ht][4 * q + 3]};
+        *(f32x4*)(po + 32 * ct + 8 * q + 4 * g) = v;
+      }
+  }
 }
 
 // -------------------------------------------------------- k_combine_uv ----
 // One block per (head, tile of 16 sequences). Blocks of the same head share
 // blockIdx % 8, i.e. the same XCD and L2, so W_UV,h is fetched from HBM once.
+//   1. per sequence: M = max_s m_s, weights e_s = 2^(m_s - M), 1 / sum_s e_s l_s
+//      (one wave per 4 sequences, lanes over splits)
+//   2. o_c = sum_s e_s O_s / sum_s e_s l_s, 16 threads per sequence, all the
+//      split loads of a thread issued together; bf16 into LDS
+//   3. out^T[v, b] = sum_c W_UV[h*128 + v, c] o_c[b, c] on MFMA; each lane ends
+//      with 4 consecutive outputs of one sequence (one 8-byte store)
 __global__ __launch_bounds__(256) void k_combine_uv(int H, int B, int splits, int pps,
                                                     const int32_t* __restrict__ ctx_lens,
                                                     const float* __restrict__ part_o,
@@ -388,70 +486,86 @@ __global__ __launch_bounds__(256) void k_combine_uv(int H, int B, int splits, in
   const int bt = k % nbt, h = (k / nbt) * 8 + xcd;
   if (h >= H) return;
   const int b0 = bt * 16;
-  const int tid = threadIdx.x;
-  if (tid < 16) {
-    const int b = b0 + tid;
-    if (b < B) {
-      const int n_pages = (ctx_lens[b] + PAGE - 1) / PAGE;
-      const int ns = (n_pages + pps - 1) / pps;
-      const float* ml = part_ml + ((size_t)h * B + b) * splits * 2;
-      float M = -INFINITY;
-      for (int s = 0; s < ns; ++s) M = fmaxf(M, ml[2 * s]);
-      float l = 0.f;
-      for (int s = 0; s < splits; ++s) {
-        const float e = s < ns ? exp2f(ml[2 * s] - M) : 0.f;
-        wgt[tid][s] = e;
-        if (s < ns) l += e * ml[2 * s + 1];
-      }
-      inv_l[tid] = 1.f / l;
-    } else {
-      for (int s = 0; s < splits; ++s) wgt[tid][s] = 0.f;
-      inv_l[tid] = 0.f;
+  const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
+  const int i16 = lane & 15, G = lane >> 4;
+  // W_UV,h fragments of this wave (rows 32w .. 32w+31, all 512 columns) are
+  // independent of everything else: request them first
+  const bf16* wv = w_uv + (size_t)h * DV * DC;
+  u32x4 wf[DC / 32][2];
+#pragma unroll
+  for (int ks = 0; ks < DC / 32; ++ks)
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt) wf[ks][mt] = *(const u32x4*)(wv + (size_t)(32 * w + 16 * mt + i16) * DC + 32 * ks + 8 * G);
+#pragma unroll
+  for (int rr = 0; rr < 4; ++rr) {
+    const int r = 4 * w + rr, b = b0 + r;
+    const int ns = b < B ? ((ctx_lens[b] + PAGE - 1) / PAGE + pps - 1) / pps : 0;
+    const float* ml = part_ml + ((size_t)h * B + (b < B ? b : 0)) * splits * 2;
+    float M = -INFINITY;
+    for (int s = lane; s < ns; s += 64) M = fmaxf(M, ml[2 * s]);
+    M = wave_max(M);
+    float l = 0.f;
+    for (int s = lane; s < splits; s += 64) {
+      const float e = s < ns ? __builtin_amdgcn_exp2f(ml[2 * s] - M) : 0.f;
+      wgt[r][s] = e;
+      if (s < ns) l += e * ml[2 * s + 1];
     }
+    l = wave_sum(l);
+    if (lane == 0) inv_l[r] = ns > 0 ? 1.f / l : 0.f;
   }
   __syncthreads();
-  // latent output o_c of the 16 sequences, normalised, as bf16 in LDS
-  for (int idx = tid; idx < 16 * (DC / 4); idx += 256) {
-    const int r = idx / (DC / 4), c4 = idx % (DC / 4);
-    const int b = b0 + r;
-    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  {
+    const int r = tid >> 4, q = tid & 15, b = b0 + r;  // 16 threads per sequence, 8 float4 each
+    f32x4 acc[8] = {};
     if (b < B) {
-      const float* po = part_o + ((size_t)h * B + b) * splits * DC + 4 * c4;
-      for (int s = 0; s < splits; ++s) {
-        const float e = wgt[r][s];
-        if (e != 0.f) {
-          const f32x4 v = *(const f32x4*)(po + (size_t)s * DC);
-          acc += e * v;
+      const float* po = part_o + ((size_t)h * B + b) * splits * DC + 4 * q;
+      // two splits' loads in flight per step; splits past the context were
+      // never written, so their (arbitrary) values are selected away, not scaled
+      for (int s = 0; s < splits; s += 2) {
+        f32x4 v[2][8];
+#pragma unroll
+        for (int d = 0; d < 2; ++d)
+#pragma unroll
+          for (int u = 0; u < 8; ++u)
+            v[d][u] = s + d < splits ? *(const f32x4*)(po + (size_t)(s + d) * DC + 64 * u) : (f32x4){0, 0, 0, 0};
+#pragma unroll
+        for (int d = 0; d < 2; ++d) {
+          const float e = s + d < splits ? wgt[r][s + d] : 0.f;
+#pragma unroll
+          for (int u = 0; u < 8; ++u)
+#pragma unroll
+            for (int x = 0; x < 4; ++x) acc[u][x] += e != 0.f ? e * v[d][u][x] : 0.f;
         }
       }
-      acc *= inv_l[r];
     }
-    uint32_t* d = (uint32_t*)&oc[r * LDO + 4 * c4];
-    d[0] = pack_bf16x2(acc[0], acc[1]);
-    d[1] = pack_bf16x2(acc[2], acc[3]);
+    const float il = inv_l[r];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      typedef __attribute__((ext_vector_type(4))) __bf16 bf16x4_t;
+      const bf16x4_t v = {(__bf16)(acc[u][0] * il), (__bf16)(acc[u][1] * il), (__bf16)(acc[u][2] * il),
+                          (__bf16)(acc[u][3] * il)};
+      *(bf16x4_t*)&oc[r * LDO + 4 * q + 64 * u] = v;
+    }
   }
   __syncthreads();
-  // out[b, h, v] = sum_c o_c[b, c] W_UV[h*128 + v, c]; wave w: v in 32w .. 32w+31
-  const int w = tid >> 6, lane = tid & 63, i16 = lane & 15, G = lane >> 4;
+  // wave w: outputs v = 32w .. 32w+31 (two 16-row tiles), all 16 sequences
   f32x4 acc[2] = {};
-  const bf16* wv = w_uv + (size_t)h * DV * DC;
-#pragma unroll 4
-  for (int ks = 0; ks < DC / 32; ++ks) {
-    const bf16x8_t a = as_bf16x8(*(const u32x4*)&oc[i16 * LDO + 32 * ks + 8 * G]);
 #pragma unroll
-    for (int nt = 0; nt < 2; ++nt) {
-      const int v = 32 * w + 16 * nt + i16;
-      const bf16x8_t bv = as_bf16x8(*(const u32x4*)(wv + (size_t)v * DC + 32 * ks + 8 * G));
-      acc[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, bv, acc[nt], 0, 0, 0);
+  for (int ks = 0; ks < DC / 32; ++ks) {
+    const bf16x8_t bo = as_bf16x8(*(const u32x4*)&oc[i16 * LDO + 32 * ks + 8 * G]);
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt)
+      acc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(wf[ks][mt]), bo, acc[mt], 0, 0, 0);
+  }
+  const int b = b0 + i16;
+  if (b < B) {
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt) {
+      typedef __attribute__((ext_vector_type(4))) __bf16 bf16x4_t;
+      const bf16x4_t v = {(__bf16)acc[mt][0], (__bf16)acc[mt][1], (__bf16)acc[mt][2], (__bf16)acc[mt][3]};
+      *(bf16x4_t*)(out + ((size_t)b * H + h) * DV + 32 * w + 16 * mt + 4 * G) = v;
     }
   }
-#pragma unroll
-  for (int nt = 0; nt < 2; ++nt)
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int b = b0 + 4 * G + r;
-      if (b < B) out[((size_t)b * H + h) * DV + 32 * w + 16 * nt + i16] = f2bf(acc[nt][r]);
-    }
 }
 
 }  // namespace
