@@ -19,7 +19,7 @@ FLAGS = [
     "-O3", "-std=c++17", "-fPIC", "-shared", f"--offload-arch={ARCH}",
     # compiler-generated packed fp32 math stays off on this target
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-    "-Wall", "-Wno-unused-function", "-Wno-unused-result",
+    "-Wall", "-Wno-unused-function", "-Wno-unused-result", "-Wno-inline-asm",
 ]
 
 

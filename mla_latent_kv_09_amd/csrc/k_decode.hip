@@ -236,6 +236,17 @@ __device__ __forceinline__ void wait_vmcnt() {
   __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x0F70);
 }
 
+// One 16-byte HBM -> LDS load per lane: lane l's bytes land at LDS byte address
+// lds_addr + 16 l (lds_addr is wave-uniform and goes through M0). Issued from
+// asm so that the compiler does not treat every later LDS read as a possible
+// alias of the copy and drain all loads first; the kernel orders these copies
+// with explicit vmcnt waits before the barrier that publishes a tile. Nothing
+// else in the kernel uses M0.
+__device__ __forceinline__ void dma16(const void* g, uint32_t lds_addr) {
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(g), "s"(lds_addr)
+               : "memory", "m0");
+}
+
 // Workgroup barrier for LDS traffic only. __syncthreads() also waits for all
 // outstanding global loads (vmcnt 0), which would drain the tile prefetch.
 __device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
@@ -266,20 +277,23 @@ __global__ __launch_bounds__(SPLIT_THREADS, 1) void k_split(int H, int B, int sp
   // lane. Instruction k of wave w fills slot chunks [(w*9+k)*64, +64) in
   // order; each lane picks the global chunk that belongs at its (swizzled)
   // position.
+  // The 9 loads of wave w cover exactly rows 8w .. 8w+7 of the tile, so the
+  // per-lane global offsets are the same for every tile: computed once here.
+  uint32_t ld_off[TILE_LOADS];
+#pragma unroll
+  for (int k = 0; k < TILE_LOADS; ++k) {
+    const int pos = (w * TILE_LOADS + k) * 64 + lane;
+    const int t = pos / ROW_CHUNKS, jp = pos - t * ROW_CHUNKS;
+    ld_off[k] = (uint32_t)(t * ROW_BYTES + ((jp ^ swz(t)) << 4));
+  }
+  const uint32_t lds_base = (uint32_t)(size_t)(LDS_AS char*)lds;
   auto load_tile = [&](int i) {
     const int t0 = t_begin + i * TILE;
     const char* src = (const char*)(rows + ((size_t)table[t0 / PAGE] * PAGE + (t0 % PAGE)) * ROW);
-    char* dst = lds + (i % N_SLOTS) * TILE_BYTES;
-    int ln = lane;
-    asm volatile("" : "+v"(ln));  // recompute the offsets per tile instead of holding 9 registers
+    const uint32_t dst = __builtin_amdgcn_readfirstlane(lds_base + (i % N_SLOTS) * TILE_BYTES +
+                                                        w * TILE_LOADS * 64 * 16);
 #pragma unroll
-    for (int k = 0; k < TILE_LOADS; ++k) {
-      const int base = (w * TILE_LOADS + k) * 64;
-      const int pos = base + ln;
-      const int t = pos / ROW_CHUNKS, jp = pos - t * ROW_CHUNKS;
-      const uint32_t off = (uint32_t)(t * ROW_BYTES + ((jp ^ swz(t)) << 4));
-      __builtin_amdgcn_global_load_lds((const void*)(src + off), (LDS_AS void*)(dst + base * 16), 16, 0, 0);
-    }
+    for (int k = 0; k < TILE_LOADS; ++k) dma16(src + ld_off[k], dst + k * 64 * 16);
   };
 
   // RoPE slice of the query of every head, in LDS: head h's 16-byte chunk c
@@ -343,27 +357,23 @@ __global__ __launch_bounds__(SPLIT_THREADS, 1) void k_split(int H, int B, int sp
     const LDS_AS char* tile = (const LDS_AS char*)(lds + (i % N_SLOTS) * TILE_BYTES);
 
     // ---- scores of this wave's 32 heads over the tile's 32 rows ----
+    // Issue order is pinned to "MFMA s, read s+QK_AHEAD" so the LDS reads run
+    // while the MFMAs execute (in-order issue would otherwise hold them back).
     f32x16 sc = {};
     {
-      u32x4 fa[2][4], fb[2][4];
-      auto qk_load = [&](int grp, int slot) {
-#pragma unroll
-        for (int u = 0; u < 4; ++u) {
-          fa[slot][u] = *(const LDS_AS u32x4*)(tile + qk_off[u] + grp * 128);
-          if (4 * grp + u >= LAT_STEPS) fb[slot][u] = *(const LDS_AS u32x4*)(qrl + qr_off[u]);
-        }
+      constexpr int QK_AHEAD = 4;
+      u32x4 fa[QK_AHEAD], fb[QK_AHEAD];
+      auto qk_read = [&](int s) {
+        fa[s % QK_AHEAD] = *(const LDS_AS u32x4*)(tile + qk_off[s & 3] + (s >> 2) * 128);
+        if (s >= LAT_STEPS) fb[s % QK_AHEAD] = *(const LDS_AS u32x4*)(qrl + qr_off[(s - LAT_STEPS) & 3]);
       };
-      qk_load(0, 0);
 #pragma unroll
-      for (int grp = 0; grp < ROW / 64; ++grp) {
-        if (grp + 1 < ROW / 64) qk_load(grp + 1, (grp + 1) & 1);
-        __builtin_amdgcn_sched_barrier(0);
+      for (int s = 0; s < QK_AHEAD; ++s) qk_read(s);
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
-          const int s = 4 * grp + u;
-          const bf16x8_t bq = s < LAT_STEPS ? qf[s < LAT_STEPS ? s : 0] : as_bf16x8(fb[grp & 1][u]);
-          sc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(fa[grp & 1][u]), bq, sc, 0, 0, 0);
-        }
+      for (int s = 0; s < ROW / 16; ++s) {
+        const bf16x8_t bq = s < LAT_STEPS ? qf[s < LAT_STEPS ? s : 0] : as_bf16x8(fb[s % QK_AHEAD]);
+        sc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(fa[s % QK_AHEAD]), bq, sc, 0, 0, 0);
+        if (s + QK_AHEAD < ROW / 16) qk_read(s + QK_AHEAD);
         __builtin_amdgcn_sched_barrier(0);
       }
     }
@@ -423,22 +433,27 @@ __global__ __launch_bounds__(SPLIT_THREADS, 1) void k_split(int H, int B, int sp
             o[ct][ht][r] = x;
           }
     }
+    // value fragments (4 column tiles) and P fragments (4 head tiles) of step
+    // j; step 1's reads are issued between step 0's MFMAs
+    bf16x8_t va[2][4], pf[2][4];
+    auto pv_read = [&](int j, int ct) {
+      const int k = 16 * j * ROW_BYTES + (ct >> 1) * 128;
+      va[j][ct] = cat_tr(tr_read(tile + pv_off[ct & 1][0] + k), tr_read(tile + pv_off[ct & 1][1] + k));
+      pf[j][ct] = *(const LDS_AS bf16x8_t*)(pbl + (ct * 2 + j) * 1024 + lane * 16);
+    };
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      bf16x8_t va[4], pf[4];
+    for (int q = 0; q < 4; ++q) pv_read(0, q);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
 #pragma unroll
       for (int ct = 0; ct < 4; ++ct) {
-        const int k = 16 * j * ROW_BYTES + (ct >> 1) * 128;
-        va[ct] = cat_tr(tr_read(tile + pv_off[ct & 1][0] + k), tr_read(tile + pv_off[ct & 1][1] + k));
-      }
-#pragma unroll
-      for (int ht = 0; ht < 4; ++ht) pf[ht] = *(const LDS_AS bf16x8_t*)(pbl + (ht * 2 + j) * 1024 + lane * 16);
-#pragma unroll
-      for (int ct = 0; ct < 4; ++ct)
 #pragma unroll
         for (int ht = 0; ht < 4; ++ht)
-          o[ct][ht] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[ct], pf[ht], o[ct][ht], 0, 0, 0);
-    }
+          o[ct][ht] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[j][ct], pf[j][ht], o[ct][ht], 0, 0, 0);
+        if (j == 0) pv_read(1, ct);
+        __builtin_amdgcn_sched_barrier(0);
+      }
   }
 
   // ---- partials: (m, l) by the head owner, O slices by the column owner ----
