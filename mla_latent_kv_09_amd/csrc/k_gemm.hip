@@ -1,0 +1,284 @@
+// bf16 MFMA GEMM for the projections of the prefill path (gfx950):
+//   C[m, n] = sum_k A[m, k] * B[n, k]       (fp32 accumulate)
+// Both operands are K-contiguous ([rows, K] row-major), the orientation of the
+// pages' [out, in] weights applied to [tokens, in] activations.
+//
+// Block tile: 256 rows of A x 128 rows of B, K in steps of 64 through a ring of
+// three LDS stages filled by direct 16-byte HBM -> LDS copies. Four waves, each
+// owning 128 A-rows x 64 B-rows as 4 x 2 tiles of 32 x 32. Each wave computes
+// the transposed tile C^T[n, m] (B rows as the MFMA M side), so a lane ends with
+// 4 consecutive output columns n of one row m: RoPE pairs (2i, 2i+1) sit in one
+// lane and stores are 8 bytes wide.
+//
+// Epilogues: plain store (optionally split into two outputs by column), and
+// the latent-cache epilogue of "DeepSeek-V2 paper digest" §2.1/§2.3: columns
+// >= d_c are rotated in pairs at the token's position, then the row
+// [c_KV || k_pe] is written to its cache slot.
+#include <math.h>
+
+#include "common.h"
+#include "launch.h"
+
+namespace mla {
+namespace {
+
+constexpr int BM = 256, BN = 128, BK = 64;
+constexpr int G_THREADS = 256;
+constexpr int A_STAGE = BM * BK * 2;  // 32 KB
+constexpr int B_STAGE = BN * BK * 2;  // 16 KB
+constexpr int STAGE = A_STAGE + B_STAGE;
+constexpr int N_STAGES = 3;
+constexpr int A_LOADS = BM * BK * 2 / 16 / G_THREADS;  // 8 per lane
+constexpr int B_LOADS = BN * BK * 2 / 16 / G_THREADS;  // 4 per lane
+
+template <int N>
+__device__ __forceinline__ void g_wait_vmcnt() {
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x0F70);
+}
+__device__ __forceinline__ void g_lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+__device__ __forceinline__ void g_dma16(const void* g, uint32_t lds_addr) {
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(g), "s"(lds_addr)
+               : "memory", "m0");
+}
+__device__ __forceinline__ bf16x8_t g_as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8_t, v); }
+
+// 16-byte chunk c (of 8) of tile row r sits at chunk c ^ ((r >> 1) & 7): 16
+// consecutive rows reading the same chunk hit 16 distinct bank groups.
+__device__ __forceinline__ int g_swz(int r) { return (r >> 1) & 7; }
+
+}  // namespace
+
+
+namespace {
+
+__device__ __forceinline__ const bf16* a_row_ptr(const GemmArgs& g, int m) {
+  m = min(m, g.M - 1);
+  if (!g.a_table) return g.a + (size_t)m * g.lda;
+  const int b = m / g.a_seq, t = m % g.a_seq;
+  const int tt = t < g.a_lens[b] ? t : 0;
+  const int slot = g.a_table[(size_t)b * g.a_max_blocks + tt / g.a_block] * g.a_block + tt % g.a_block;
+  return g.a + (size_t)slot * g.lda;
+}
+
+__device__ __forceinline__ const bf16* b_row_ptr(const GemmArgs& g, int n) {
+  n = min(n, g.N - 1);
+  return n < g.n_split ? g.b0 + (size_t)n * g.ldb : g.b1 + (size_t)(n - g.n_split) * g.ldb;
+}
+
+template <int EPI>
+__global__ __launch_bounds__(G_THREADS, 1) void k_gemm(GemmArgs g) {
+  __shared__ __attribute__((aligned(1024))) char lds[N_STAGES * STAGE];
+  const int n_tiles = (g.N + BN - 1) / BN;
+  const int bid = blockIdx.x;
+  const int mt = bid / n_tiles, nt = bid % n_tiles;
+  const int m0 = mt * BM, n0 = nt * BN;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
+  const int wm = w & 1, wn = w >> 1;  // wave covers A rows m0 + 128wm .., B rows n0 + 64wn ..
+  const int k_steps = g.K / BK;
+
+  // per-lane source rows and LDS positions of the copies (fixed over K)
+  // instruction k of wave w fills tile chunks [(w*L + k)*64, +64): 8 rows x 8 chunks
+  const bf16* a_src[A_LOADS];
+  const bf16* b_src[B_LOADS];
+#pragma unroll
+  for (int k = 0; k < A_LOADS; ++k) {
+    const int pos = (w * A_LOADS + k) * 64 + lane, r = pos >> 3, cp = pos & 7;
+    a_src[k] = a_row_ptr(g, m0 + r) + 8 * (cp ^ g_swz(r));
+  }
+#pragma unroll
+  for (int k = 0; k < B_LOADS; ++k) {
+    const int pos = (w * B_LOADS + k) * 64 + lane, r = pos >> 3, cp = pos & 7;
+    b_src[k] = b_row_ptr(g, n0 + r) + 8 * (cp ^ g_swz(r));
+  }
+  const uint32_t lds_base = (uint32_t)(size_t)(LDS_AS char*)lds;
+  auto load_stage = [&](int ks) {
+    const uint32_t st = lds_base + (ks % N_STAGES) * STAGE;
+    const int kofs = ks * BK;
+#pragma unroll
+    for (int k = 0; k < A_LOADS; ++k)
+      g_dma16(a_src[k] + kofs, __builtin_amdgcn_readfirstlane(st + (w * A_LOADS + k) * 1024));
+#pragma unroll
+    for (int k = 0; k < B_LOADS; ++k)
+      g_dma16(b_src[k] + kofs, __builtin_amdgcn_readfirstlane(st + A_STAGE + (w * B_LOADS + k) * 1024));
+  };
+  constexpr int LOADS = A_LOADS + B_LOADS;
+
+  load_stage(0);
+  if (k_steps > 1) load_stage(1);
+
+  // operand read offsets inside a stage: MFMA A side = B rows (n), B side = A rows (m)
+  //   step s (16 of K) reads chunk 2s + g of its row
+  const int hl = lane & 31, gq = lane >> 5;
+  int an_off[2][4], bm_off[4][4];  // [tile][k-step within BK]
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int r = 64 * wn + 32 * i + hl;
+#pragma unroll
+    for (int s = 0; s < 4; ++s) an_off[i][s] = A_STAGE + r * 128 + (((2 * s + gq) ^ g_swz(r)) << 4);
+  }
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int r = 128 * wm + 32 * j + hl;
+#pragma unroll
+    for (int s = 0; s < 4; ++s) bm_off[j][s] = r * 128 + (((2 * s + gq) ^ g_swz(r)) << 4);
+  }
+
+  f32x16 acc[2][4];  // [n tile][m tile]
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[i][j] = (f32x16){};
+
+  for (int ks = 0; ks < k_steps; ++ks) {
+    if (ks + 1 < k_steps) g_wait_vmcnt<LOADS>();
+    else g_wait_vmcnt<0>();
+    g_lds_barrier();
+    if (ks + 2 < k_steps) load_stage(ks + 2);
+    const LDS_AS char* st = (const LDS_AS char*)(lds + (ks % N_STAGES) * STAGE);
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      bf16x8_t fa[2], fb[4];
+#pragma unroll
+      for (int i = 0; i < 2; ++i) fa[i] = g_as_bf16x8(*(const LDS_AS u32x4*)(st + an_off[i][s]));
+#pragma unroll
+      for (int j = 0; j < 4; ++j) fb[j] = g_as_bf16x8(*(const LDS_AS u32x4*)(st + bm_off[j][s]));
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[i], fb[j], acc[i][j], 0, 0, 0);
+    }
+  }
+
+  // epilogue: lane holds C[m][n .. n+3] for m = m0 + 128wm + 32j + hl,
+  // n = n0 + 64wn + 32i + 8q + 4gq (q = r / 4)
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int m = m0 + 128 * wm + 32 * j + hl;
+    if (m >= g.M) continue;
+    bf16* crow;
+    int pos = 0;
+    if (EPI == 1) {
+      crow = g.c0 + (size_t)g.slots[m] * g.ldc0;
+      pos = g.positions[m];
+    }
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int n = n0 + 64 * wn + 32 * i + 8 * q + 4 * gq;
+        if (n >= g.N) continue;
+        float v[4] = {acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]};
+        typedef __attribute__((ext_vector_type(4))) __bf16 bf16x4_t;
+        if (EPI == 1) {
+          if (n >= g.d_c) {  // d_c is a multiple of 8: all four columns are RoPE columns
+#pragma unroll
+            for (int e = 0; e < 4; e += 2) {
+              const int pr = (n + e - g.d_c) >> 1;
+              const double ang = (double)pos * pow((double)g.rope_base, -2.0 * pr / (double)g.d_rope);
+              const float r = (float)(ang - 6.283185307179586 * rint(ang * 0.15915494309189535));
+              float sn, cs;
+              sincosf(r, &sn, &cs);
+              const float x0 = v[e], x1 = v[e + 1];
+              v[e] = x0 * cs - x1 * sn;
+              v[e + 1] = x0 * sn + x1 * cs;
+            }
+          }
+          const bf16x4_t o = {(__bf16)v[0], (__bf16)v[1], (__bf16)v[2], (__bf16)v[3]};
+          *(bf16x4_t*)(crow + n) = o;
+        } else {
+          const bf16x4_t o = {(__bf16)v[0], (__bf16)v[1], (__bf16)v[2], (__bf16)v[3]};
+          if (n < g.c_split) *(bf16x4_t*)(g.c0 + (size_t)m * g.ldc0 + n) = o;
+          else *(bf16x4_t*)(g.c1 + (size_t)m * g.ldc1 + (n - g.c_split)) = o;
+        }
+      }
+  }
+}
+
+}  // namespace
+
+bool gemm_fast_supported(int M, int N, int K) { return M > 0 && N > 0 && N % 4 == 0 && K > 0 && K % BK == 0; }
+
+hipError_t gemm_fast(const GemmArgs& g, int epi, hipStream_t s) {
+  const int grid = ((g.M + BM - 1) / BM) * ((g.N + BN - 1) / BN);
+  if (epi == 1)
+    hipLaunchKernelGGL(k_gemm<1>, dim3(grid), dim3(G_THREADS), 0, s, g);
+  else
+    hipLaunchKernelGGL(k_gemm<0>, dim3(grid), dim3(G_THREADS), 0, s, g);
+  return hipGetLastError();
+}
+
+bool project_fast_supported(const mla_dims& d, int d_model, int d_q) {
+  return d.dtype == MLA_BF16 && d_model % BK == 0 && d.d_rope % 4 == 0 && (d_q == 0 || d_q % BK == 0);
+}
+
+// Latent rows (RoPE + scatter epilogue), then the optional query path: c_Q in
+// bf16 in the workspace, then [q_nope | q_pe] = c_Q [W_UQ; W_QR]^T split by column.
+hipError_t project_fast(const mla_dims& d, int n_tokens, int d_model, const void* h, const void* w_dkv,
+                        const void* w_kr, const int32_t* positions, const int32_t* slots, void* rows,
+                        const mla_qproj* qp, void* ws, hipStream_t s) {
+  GemmArgs g{};
+  g.M = n_tokens;
+  g.N = d.d_c + d.d_rope;
+  g.K = d_model;
+  g.a = (const bf16*)h;
+  g.lda = d_model;
+  g.b0 = (const bf16*)w_dkv;
+  g.b1 = (const bf16*)w_kr;
+  g.n_split = d.d_c;
+  g.ldb = d_model;
+  g.c0 = g.c1 = (bf16*)rows;
+  g.ldc0 = g.ldc1 = d.d_c + d.d_rope;
+  g.c_split = g.N;
+  g.slots = slots;
+  g.positions = positions;
+  g.d_c = d.d_c;
+  g.d_rope = d.d_rope;
+  g.rope_base = d.rope_base;
+  hipError_t e;
+  {
+    ProfScope ps("mla_project_latent", s);
+    e = gemm_fast(g, 1, s);
+  }
+  if (e != hipSuccess || !qp) return e;
+  bf16* cq = (bf16*)ws;
+  GemmArgs q{};
+  q.M = n_tokens;
+  q.N = qp->d_q;
+  q.K = d_model;
+  q.a = (const bf16*)h;
+  q.lda = d_model;
+  q.b0 = q.b1 = (const bf16*)qp->w_dq;
+  q.n_split = q.N;
+  q.ldb = d_model;
+  q.c0 = q.c1 = cq;
+  q.ldc0 = q.ldc1 = qp->d_q;
+  q.c_split = q.N;
+  {
+    ProfScope ps("mla_project_q_down", s);
+    e = gemm_fast(q, 0, s);
+  }
+  if (e != hipSuccess) return e;
+  const int hn = d.n_heads * d.d_nope, hr = d.n_heads * d.d_rope;
+  GemmArgs u{};
+  u.M = n_tokens;
+  u.N = hn + hr;
+  u.K = qp->d_q;
+  u.a = cq;
+  u.lda = qp->d_q;
+  u.b0 = (const bf16*)qp->w_uq;
+  u.b1 = (const bf16*)qp->w_qr;
+  u.n_split = hn;
+  u.ldb = qp->d_q;
+  u.c0 = (bf16*)qp->q_nope;
+  u.c1 = (bf16*)qp->q_pe;
+  u.ldc0 = hn;
+  u.ldc1 = hr;
+  u.c_split = hn;
+  {
+    ProfScope ps("mla_project_q_up", s);
+    e = gemm_fast(u, 0, s);
+  }
+  return e;
+}
+
+}  // namespace mla

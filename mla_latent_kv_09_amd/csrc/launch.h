@@ -55,4 +55,47 @@ hipError_t decode_fast(const mla_dims& d, float scale, int batch, int max_contex
                        const void* q_nope, const void* q_pe, const void* w_uk, const void* w_uv,
                        const CacheView& c, void* out, void* ws, size_t ws_bytes, hipStream_t s);
 
+// ---- MFMA GEMM (bf16, K multiple of 64, N multiple of 4) -----------------
+// C[m, n] = sum_k A[m, k] B[n, k]; A and B rows are K-contiguous.
+struct GemmArgs {
+  int M, N, K;
+  // A operand rows: plain (a + m * lda) or gathered from a paged latent cache
+  // (row m = (b, t) with b = m / a_seq, t = m % a_seq; rows t >= context are
+  // read from row 0 of the sequence and never used).
+  const uint16_t* a;
+  int lda;
+  const int32_t* a_table;
+  const int32_t* a_lens;
+  int a_seq, a_max_blocks, a_block;
+  // B operand rows n < n_split from b0, the rest from b1 (row n - n_split)
+  const uint16_t* b0;
+  const uint16_t* b1;
+  int n_split, ldb;
+  // plain epilogue: columns n < c_split to c0[m, n], the rest to c1[m, n - c_split]
+  uint16_t* c0;
+  uint16_t* c1;
+  int ldc0, ldc1, c_split;
+  // latent epilogue
+  const int32_t* slots;
+  const int32_t* positions;
+  int d_c, d_rope;
+  float rope_base;
+};
+
+bool gemm_fast_supported(int M, int N, int K);
+hipError_t gemm_fast(const GemmArgs& g, int epi, hipStream_t s);  // epi 0 store, 1 latent rows
+
+// ---- MFMA prefill attention (bf16, DeepSeek-V3 latent shape) --------------
+bool prefill_fast_supported(const mla_dims& d, const CacheView& c);
+size_t prefill_fast_workspace(const mla_dims& d, int batch, int max_context);
+hipError_t prefill_fast(const mla_dims& d, float scale, int batch, int seq_len, int max_context,
+                        const void* q_nope, const void* q_pe, const void* w_uk, const void* w_uv,
+                        const CacheView& c, void* out, void* ws, size_t ws_bytes, hipStream_t s);
+
+// ---- projection with the MFMA GEMM ----------------------------------------
+bool project_fast_supported(const mla_dims& d, int d_model, int d_q);
+hipError_t project_fast(const mla_dims& d, int n_tokens, int d_model, const void* h, const void* w_dkv,
+                        const void* w_kr, const int32_t* positions, const int32_t* slots, void* rows,
+                        const mla_qproj* qp, void* ws, hipStream_t s);
+
 }  // namespace mla

@@ -74,6 +74,13 @@ bool fast_dims(const mla_dims* d) {
   return mla::decode_fast_supported(*d, v);
 }
 
+bool prefill_fast_dims(const mla_dims* d) {
+  mla::CacheView v{};
+  v.paged = 1;
+  v.block_size = 64;
+  return mla::prefill_fast_supported(*d, v);
+}
+
 }  // namespace
 
 extern "C" {
@@ -118,7 +125,9 @@ mla_status mla_prefill_workspace_size(const mla_dims* d, int32_t batch, int32_t 
   if (st != MLA_OK) return st;
   if (!bytes) return MLA_ERR_NULL_ARG;
   if (batch < 0 || seq_len < 0 || max_context < 0) return MLA_ERR_BAD_SHAPE;
-  *bytes = 0;
+  *bytes = (prefill_fast_dims(d) && batch > 0 && seq_len > 0)
+               ? mla::prefill_fast_workspace(*d, batch, max_context > seq_len ? max_context : seq_len)
+               : 0;
   return MLA_OK;
 }
 
@@ -132,9 +141,10 @@ int32_t mla_decode_path(const mla_dims* d, int32_t block_size, int32_t paged) {
 
 int32_t mla_prefill_path(const mla_dims* d, int32_t block_size, int32_t paged) {
   if (check_dims(d) != MLA_OK) return -1;
-  (void)block_size;
-  (void)paged;
-  return 0;
+  mla::CacheView v{};
+  v.paged = paged;
+  v.block_size = block_size;
+  return mla::prefill_fast_supported(*d, v) ? 1 : 0;
 }
 
 mla_status mla_rope_latent_project(const mla_dims* d, int32_t n_tokens, int32_t d_model, const void* h,
@@ -160,9 +170,12 @@ mla_status mla_rope_latent_project(const mla_dims* d, int32_t n_tokens, int32_t 
   }
   if ((st = check_ws(ws, ws_bytes, need)) != MLA_OK) return st;
   hipStream_t s = (hipStream_t)stream;
+  const bool fast = mla::project_fast_supported(*d, d_model, qp ? qp->d_q : 0);
   if (trace_on())
-    fprintf(stderr, "[mla] project n_tokens=%d d_model=%d d_q=%d path=generic\n", n_tokens, d_model,
-            qp ? qp->d_q : 0);
+    fprintf(stderr, "[mla] project n_tokens=%d d_model=%d d_q=%d path=%s\n", n_tokens, d_model, qp ? qp->d_q : 0,
+            fast ? "mfma" : "generic");
+  if (fast)
+    return hip_status(mla::project_fast(*d, n_tokens, d_model, h, w_dkv, w_kr, positions, slots, cache->rows, qp, ws, s));
   hipError_t e = mla::project_latent_generic(*d, n_tokens, d_model, h, w_dkv, w_kr, positions, slots,
                                              cache->rows, s);
   if (e != hipSuccess || !qp) return hip_status(e);
@@ -219,10 +232,16 @@ mla_status mla_prefill(const mla_dims* d, int32_t batch, int32_t seq_len, const 
   CacheView v{};
   if ((st = check_cache(cache, &v)) != MLA_OK) return st;
   if (seq_len > cache->max_context) return MLA_ERR_BAD_SHAPE;
-  if ((st = check_ws(ws, ws_bytes, 0)) != MLA_OK) return st;
+  const bool fast = mla::prefill_fast_supported(*d, v);
+  const size_t need = fast ? mla::prefill_fast_workspace(*d, batch, cache->max_context) : 0;
+  if ((st = check_ws(ws, ws_bytes, need)) != MLA_OK) return st;
   hipStream_t s = (hipStream_t)stream;
   if (trace_on())
-    fprintf(stderr, "[mla] prefill batch=%d seq_len=%d heads=%d path=generic\n", batch, seq_len, d->n_heads);
+    fprintf(stderr, "[mla] prefill batch=%d seq_len=%d heads=%d path=%s ws=%zu\n", batch, seq_len, d->n_heads,
+            fast ? "mfma" : "generic", need);
+  if (fast)
+    return hip_status(mla::prefill_fast(*d, scale_of(d), batch, seq_len, cache->max_context, q_nope, q_pe, w_uk,
+                                        w_uv, v, out, ws, ws_bytes, s));
   return hip_status(mla::attn_generic(*d, scale_of(d), batch, seq_len, q_nope, q_pe, w_uk, w_uv, v, out, s));
 }
 

@@ -232,3 +232,75 @@ def test_decode_large_score_growth_takes_the_rescale_branch():
             pool[table[b, p], :, 512:] *= 1.0 + 5.0 * p / n
     case.cache.pool = f32_to_bf16_bits(pool)
     assert_parity(run_decode(case), oracle_decode(case), "bf16", "rescale")
+
+
+# ------------------------------------------------ MFMA projection/prefill --
+
+def _project_and_prefill(case, dims, d_q):
+    """Runs the latent + query projection and causal prefill on the GPU;
+    returns (rows gathered in token order, q_nope, q_pe, out) as float64."""
+    B, S, T = case.batch, case.seq_len, case.n_tokens
+    H = dims.n_heads
+    rows = torch.zeros((case.num_blocks, 64, dims.row), dtype=torch.bfloat16, device="cuda")
+    lens = torch.full((B,), S, dtype=torch.int32, device="cuda")
+    cache = mla.Cache(rows, lens, S, to_torch(case.block_table))
+    qn = torch.empty((T, H, dims.d_nope), dtype=torch.bfloat16, device="cuda")
+    qp = torch.empty((T, H, dims.d_rope), dtype=torch.bfloat16, device="cuda")
+    qproj = mla.QProj(to_torch(case.w_dq), to_torch(case.w_uq), to_torch(case.w_qr), qn, qp)
+    mla.mla_rope_latent_project(dims, to_torch(case.h), to_torch(case.w_dkv), to_torch(case.w_kr),
+                                to_torch(case.positions), to_torch(case.slots), cache, qproj)
+    out = mla.mla_prefill(dims, qn.view(B, S, H, dims.d_nope), qp.view(B, S, H, dims.d_rope),
+                          to_torch(case.w_uk), to_torch(case.w_uv), cache)
+    torch.cuda.synchronize()
+    got_rows = from_torch(rows)[case.slots // 64, case.slots % 64]
+    return got_rows, from_torch(qn), from_torch(qp), from_torch(out)
+
+
+def _check_rows(got_rows, ref_rows):
+    # one bf16 rounding of the fp64 value, plus accumulation-order slack
+    assert np.all(np.abs(got_rows - ref_rows) <= 2 ** -7 * np.abs(ref_rows) + 2e-3), \
+        float(np.abs(got_rows - ref_rows).max())
+
+
+def test_mfma_projection_and_prefill_ragged():
+    _log("MFMA projection + prefill, B=2 S=300 H=128")
+    dims = Dims(128, **V3)
+    assert mla.mla_prefill_path(dims) == 1
+    case = make_project_case(31, batch=2, seq_len=300, d_model=512, dims=dims, d_q=256, shuffle=True)
+    got_rows, qn, qp, out = _project_and_prefill(case, dims, 256)
+    ref_rows = oracle.latent_rows(case.h, case.w_dkv, case.w_kr, case.positions)
+    _check_rows(got_rows, ref_rows)
+    ref_qn, ref_qp = oracle.query_projection(case.h, case.w_dq, case.w_uq, case.w_qr, 128, 128, 64)
+    assert_parity(qn, ref_qn, "bf16", "q_nope")
+    assert_parity(qp, ref_qp, "bf16", "q_pe")
+    queries = [(0, 0), (0, 1), (0, 63), (0, 64), (0, 127), (0, 128), (1, 200), (1, 255), (1, 256), (1, 299)]
+    ref = oracle.prefill(dims, oracle.round_to(ref_qn, "bf16").reshape(2, 300, 128, 128),
+                         oracle.round_to(ref_qp, "bf16").reshape(2, 300, 128, 64), case.w_uk, case.w_uv,
+                         oracle.round_to(ref_rows, "bf16").reshape(2, 300, -1), queries=queries)
+    got = out.reshape(2, 300, 128, 128)[[b for b, _ in queries], [s for _, s in queries]]
+    assert_parity(got, ref, "bf16", "prefill")
+
+
+def test_workload5_full_size_sampled():
+    _log("workload 5: B=4 S=4096 d_model=7168 projection + prefill, oracle on sampled queries")
+    case = workload(5)
+    dims = case.dims
+    got_rows, qn, qp, out = _project_and_prefill(case, dims, 1536)
+    S = case.seq_len
+    sample_b = 2
+    tok = slice(sample_b * S, (sample_b + 1) * S)
+    ref_rows = oracle.latent_rows(case.h[tok], case.w_dkv, case.w_kr, case.positions[tok])
+    _check_rows(got_rows[tok], ref_rows)
+    picks = [0, 1, 777, 2048, S - 1]
+    ids = [sample_b * S + s for s in picks]
+    ref_qn, ref_qp = oracle.query_projection(case.h[ids], case.w_dq, case.w_uq, case.w_qr, 128, 128, 64)
+    assert_parity(qn[ids], ref_qn, "bf16", "q_nope")
+    assert_parity(qp[ids], ref_qp, "bf16", "q_pe")
+    qn_full = np.zeros((1, S, 128, 128))
+    qp_full = np.zeros((1, S, 128, 64))
+    qn_full[0, picks] = oracle.round_to(ref_qn, "bf16")
+    qp_full[0, picks] = oracle.round_to(ref_qp, "bf16")
+    ref = oracle.prefill(dims, qn_full, qp_full, case.w_uk, case.w_uv, oracle.round_to(ref_rows, "bf16")[None],
+                         queries=[(0, s) for s in picks])
+    got = out.reshape(4, S, 128, 128)[sample_b, picks]
+    assert_parity(got, ref, "bf16", "workload 5 prefill")
