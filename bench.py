@@ -33,6 +33,8 @@ WORKLOAD_NAMES = {
     2: "mla_decode B=16 H=16 L=4096 d_c=512 d_rope=64 bf16, 64-token pages",
     3: "mla_decode B=64 H=128 L=8192 d_c=512 d_rope=64 bf16, 64-token pages (DeepSeek-V3 shape)",
     4: "mla_decode B=32 H=128 L~U[1024,32768] d_c=512 d_rope=64 bf16, shuffled 64-token pages",
+    5: "mla_rope_latent_project (latent + query projections) + causal mla_prefill, B=4 S=4096 d_model=7168 "
+       "d_q=1536 H=128 bf16",
 }
 
 
@@ -93,6 +95,76 @@ def cpu_baseline(case, budget_s):
                       f"float64 numpy, {dt:.1f} s"}
 
 
+def prefill_bench(args):
+    """Workload 5: one step = latent + query projection of B*S tokens (cache
+    write) followed by causal prefill attention over them."""
+    import torch
+    import mla_latent_kv_09_amd as mla
+    from synth import to_torch, workload
+
+    dev = "cuda:0"
+    case = workload(5)
+    d = mla.Dims.of(case.dims)
+    B, S, T, H = case.batch, case.seq_len, case.n_tokens, d.n_heads
+    rows = torch.zeros((case.num_blocks, 64, d.row), dtype=torch.bfloat16, device=dev)
+    cache = mla.Cache(rows, torch.full((B,), S, dtype=torch.int32, device=dev), S, to_torch(case.block_table, dev))
+    h, w_dkv, w_kr = to_torch(case.h, dev), to_torch(case.w_dkv, dev), to_torch(case.w_kr, dev)
+    pos, slots = to_torch(case.positions, dev), to_torch(case.slots, dev)
+    qn = torch.empty((T, H, d.d_nope), dtype=torch.bfloat16, device=dev)
+    qp = torch.empty((T, H, d.d_rope), dtype=torch.bfloat16, device=dev)
+    qproj = mla.QProj(to_torch(case.w_dq, dev), to_torch(case.w_uq, dev), to_torch(case.w_qr, dev), qn, qp)
+    w_uk, w_uv = to_torch(case.w_uk, dev), to_torch(case.w_uv, dev)
+    ws_p = torch.empty(mla.mla_project_workspace_size(d, T, case.w_dq.shape[0]), dtype=torch.uint8, device=dev)
+    ws_a = torch.empty(mla.mla_prefill_workspace_size(d, B, S, S), dtype=torch.uint8, device=dev)
+    out = torch.empty((B, S, H, d.d_v), dtype=torch.bfloat16, device=dev)
+
+    def step():
+        mla.mla_rope_latent_project(d, h, w_dkv, w_kr, pos, slots, cache, qproj, workspace=ws_p)
+        mla.mla_prefill(d, qn.view(B, S, H, d.d_nope), qp.view(B, S, H, d.d_rope), w_uk, w_uv, cache, out=out,
+                        workspace=ws_a)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    lib = mla.library()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    lib.mla_profile_begin()
+    ev0.record()
+    for _ in range(args.steps):
+        step()
+    ev1.record()
+    torch.cuda.synchronize()
+    kern = profile_end(lib)
+    ms = ev0.elapsed_time(ev1) / args.steps
+    d_model, d_q = case.d_model, case.w_dq.shape[0]
+    pairs = B * S * (S + 1) // 2
+    flop = {
+        "mla_project_latent": 2.0 * T * d_model * (d.d_c + d.d_rope),
+        "mla_project_q_down": 2.0 * T * d_model * d_q,
+        "mla_project_q_up": 2.0 * T * d_q * H * (d.d_nope + d.d_rope),
+        "mla_prefill_kv_up": 2.0 * T * d.d_c * H * (d.d_nope + d.d_v),
+        "mla_prefill_attn": 2.0 * pairs * H * (d.d_nope + d.d_rope + d.d_v),
+    }
+    total = sum(flop.values())
+    per = {k: (v[0] / v[1]) for k, v in kern.items()}
+    dom = max(per, key=per.get)
+    achieved = flop[dom] / (per[dom] * 1e-3) / 1e12
+    line = {
+        "metric": "MLA prefill tokens/s (projections + causal attention), 1xMI355X",
+        "value": round(T / (ms * 1e-3), 1), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms, 4), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16", "data": "synthetic (seeded h ~ N(0,1), weights std 1/sqrt(fan_in))",
+        "config": {"workload": WORKLOAD_NAMES[5], "batch": B, "seq_len": S, "parallelism": "none (1 GPU)"},
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 1), "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(achieved / BF16_PEAK_TFLOPS, 4), "traffic": None, "kernel": dom,
+                     "kernel_us": round(per[dom] * 1e3, 1), "algorithmic_flop": flop[dom]},
+        "step": {"algorithmic_flop": total, "mfma_TFLOP_per_s": round(total / (ms * 1e-3) / 1e12, 1),
+                 "mfma_frac": round(total / (ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 4),
+                 "kernels_us": {k: round(v * 1e3, 1) for k, v in per.items()}},
+    }
+    print(json.dumps(line), flush=True)
+
+
 def main():
     args = parse()
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -100,6 +172,10 @@ def main():
         print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}, WORLD_SIZE {world}); "
               "this library has no multi-GPU path.", file=sys.stderr)
         sys.exit(2)
+
+    if args.workload == 5:
+        prefill_bench(args)
+        return
 
     import torch
     import mla_latent_kv_09_amd as mla

@@ -58,12 +58,14 @@ __device__ __forceinline__ void p_scale_acc(float& x, float a) {
       : "+a"(x), "=&v"(t)
       : "v"(a));
 }
-// K tile: 24 chunks per row; chunk c of row t at c ^ ((t >> 1) & 7) (score
-// operand reads: 16 consecutive rows, one chunk). V tile: 16 chunks per row;
-// chunk c of row t at c ^ (((t & 3) << 1) | ((t >> 2) & 1)) (transposed reads:
-// 4 consecutive rows x 2 neighbouring chunks, with a 256-byte row stride).
+// K tile: 24 chunks per row; chunk c of row t sits at (c & ~7) | ((c & 7) ^
+// ((t >> 1) & 7)): the 16 consecutive rows of a score-operand read hit 16
+// distinct bank groups. V tile: 16 chunks per row (a 256-byte stride, so every
+// row starts on bank 0); chunk c of row t sits at c ^ (4 (t & 3)): the 4 rows x
+// 4 chunks that 32 lanes of a transposed read touch land on 16 distinct chunk
+// positions.
 __device__ __forceinline__ int k_swz(int t) { return (t >> 1) & 7; }
-__device__ __forceinline__ int v_swz(int t) { return ((t & 3) << 1) | ((t >> 2) & 1); }
+__device__ __forceinline__ int v_pos(int t, int c) { return c ^ (4 * (t & 3)); }
 
 __global__ __launch_bounds__(P_THREADS, 1) void k_prefill_attn(
     int H, int S, float qscale, float base, const bf16* __restrict__ q_nope, const bf16* __restrict__ q_pe,
@@ -117,26 +119,28 @@ __global__ __launch_bounds__(P_THREADS, 1) void k_prefill_attn(
 
   // ---- copies of key tile j: per lane 10 chunks (K_nope 4, k_pe 2, V 4) ----
   // LDS chunk position p of a stage: K rows (24 chunks each) then V rows (16).
+  // A 64-key tile lies in one cache page (block_size is a multiple of 64), so
+  // its page comes from one scalar load; no per-lane global load precedes the
+  // copies (those would make the compiler drain the copies in flight).
   const uint32_t lds_base = (uint32_t)(size_t)(LDS_AS char*)lds;
   auto load_tile = [&](int j) {
     const uint32_t st = lds_base + (j % P_STAGES) * P_STAGE;
+    const int page = tb[(j * KT) / block_size];
+    const size_t pslot = (size_t)page * block_size + (j * KT) % block_size;
 #pragma unroll
     for (int k = 0; k < P_LOADS; ++k) {
       const int p = (w * P_LOADS + k) * 64 + lane;  // chunk position within the stage
       const bf16* src;
       if (p < KT * 24) {
         const int t = p / 24, cp = p % 24, c = (cp & ~7) | ((cp & 7) ^ k_swz(t));
-        const int tok = min(j * KT + t, L - 1);
-        if (c < 16) {
-          src = kn + ((size_t)b * seq_stride + tok) * H * DN + h * DN + 8 * c;
-        } else {
-          const int slot = tb[tok / block_size] * block_size + tok % block_size;
-          src = rows + (size_t)slot * ROW + DC + 8 * (c - 16);
-        }
+        const int dt = min(j * KT + t, L - 1) - j * KT;  // clamp into the context
+        const bf16* ksrc = kn + ((size_t)b * seq_stride + j * KT + dt) * H * DN + h * DN + 8 * c;
+        const bf16* psrc = rows + (pslot + dt) * ROW + DC + 8 * (c - 16);
+        src = c < 16 ? ksrc : psrc;
       } else {
-        const int q = p - KT * 24, t = q >> 4, cp = q & 15, c = (cp & 8) | ((cp & 7) ^ v_swz(t));
-        const int tok = min(j * KT + t, L - 1);
-        src = vv + ((size_t)b * seq_stride + tok) * H * DV + h * DV + 8 * c;
+        const int q = p - KT * 24, t = q >> 4, c = v_pos(t, q & 15);
+        const int dt = min(j * KT + t, L - 1) - j * KT;
+        src = vv + ((size_t)b * seq_stride + j * KT + dt) * H * DV + h * DV + 8 * c;
       }
       p_dma16(src, __builtin_amdgcn_readfirstlane(st + (w * P_LOADS + k) * 1024));
     }
@@ -158,15 +162,15 @@ __global__ __launch_bounds__(P_THREADS, 1) void k_prefill_attn(
       k_off[kh][st] = t * K_ROW_BYTES + (((c & ~7) | ((c & 7) ^ k_swz(t))) << 4);
     }
   }
-  int v_off[4][2];  // [dt][a/b] for ks = 0; rows advance by 16 per ks (swizzle is periodic in 8)
+  int v_off[4][2];  // [dt][a/b] for ks = 0; rows advance by 16 per ks (the swizzle has period 4)
   {
     const int ra = 4 * g + (i16 >> 2), rb = ra + 8;
 #pragma unroll
     for (int dt = 0; dt < 4; ++dt) {
       const int col = 32 * dt + 16 * (G & 1) + 4 * (i16 & 3);
       const int c = col >> 3, sub = (col & 7) * 2;
-      v_off[dt][0] = K_TILE + ra * V_ROW_BYTES + (((c & 8) | ((c & 7) ^ v_swz(ra))) << 4) + sub;
-      v_off[dt][1] = K_TILE + rb * V_ROW_BYTES + (((c & 8) | ((c & 7) ^ v_swz(rb))) << 4) + sub;
+      v_off[dt][0] = K_TILE + ra * V_ROW_BYTES + (v_pos(ra, c) << 4) + sub;
+      v_off[dt][1] = K_TILE + rb * V_ROW_BYTES + (v_pos(rb, c) << 4) + sub;
     }
   }
 
@@ -270,7 +274,7 @@ __global__ __launch_bounds__(P_THREADS, 1) void k_prefill_attn(
 
 bool prefill_fast_supported(const mla_dims& d, const CacheView& c) {
   return d.dtype == MLA_BF16 && d.d_c == DC && d.d_rope == DR && d.d_nope == DN && d.d_v == DV && c.paged &&
-         c.block_size % 64 == 0 && d.n_heads <= 256;
+         c.block_size % KT == 0 && d.n_heads <= 256;
 }
 
 size_t prefill_fast_workspace(const mla_dims& d, int batch, int max_context) {
