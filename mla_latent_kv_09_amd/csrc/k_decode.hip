@@ -18,6 +18,8 @@
 //                  sequences so each head's W_UV is read once.
 #include <math.h>
 
+#include <type_traits>
+
 #include "common.h"
 #include "launch.h"
 
@@ -206,28 +208,39 @@ __global__ __launch_bounds__(256) void k_absorb(int B, int H, const bf16* __rest
 //
 // Work split inside the block, per tile:
 //   scores    wave w owns heads 32w .. 32w+31: S^T[t, h] = row_t . Qt[h]
-//             (36 MFMA steps of K = 16 over the 576 columns), then the online
-//             softmax of those heads (running max m and sum l stay with the
-//             owner). The probabilities P (bf16) and each head's rescale
-//             factor go to LDS.
+//             (36 MFMA steps of K = 16 over the 576 columns; the query of the
+//             lane's head stays in registers), then the online softmax of those
+//             heads (running max m and sum l stay with the owner). The
+//             probabilities P (bf16) go to LDS.
 //   values    wave w owns latent columns 128w .. 128w+127 of every head:
 //             O^T[c, h] += V^T[c, t] P[t, h] (4 column tiles x 4 head tiles x
 //             2 steps). Each value fragment, read once from LDS, feeds four
 //             MFMAs; so does each P fragment.
-// Rows stream HBM -> LDS with direct 16-byte loads into a ring of three tile
-// slots: while tile i is computed, tiles i+1 and i+2 are in flight.
+// Software pipeline, one barrier per tile: iteration i computes the scores of
+// tile i, then the value product of tile i - 1 with the softmax of tile i
+// spread between its MFMAs (they are independent), then publishes P of tile
+// i. P is double-buffered; tiles stream HBM -> LDS with direct 16-byte loads
+// into a ring of four slots (tile i - 1 in the value step, tile i in the score
+// step, tiles i + 1 and i + 2 in flight): 4 x 36 KB + 2 x 8 KB = 160 KB.
+//
+// The reference max is set by the first tile and then moves lazily (only when
+// a tile's max exceeds it by more than 8) and only by whole steps k, so the
+// rescale factor of the other waves' accumulators is an exact power of two
+// 2^-k. The owner sends k (8 bits) in
+// the sign bits of the head's first P fragment (P >= 0, so those bits are
+// otherwise clear); the readers test them, and in the rare case decode k,
+// clear the bits and rescale.
 //
 // Partials per (head, sequence, split): O (512 fp32, unnormalised, relative to
 // the head's reference max m) and (m, l), both in the log2 domain.
 constexpr int TILE = 32;                                  // rows per tile
 constexpr int TILE_BYTES = TILE * ROW_BYTES;              // 36864
 constexpr int TILE_LOADS = TILE * ROW_CHUNKS / SPLIT_THREADS;  // 9 per lane
-constexpr int N_SLOTS = 3;
-constexpr int QR_BYTES = MAX_HEADS * DR * 2;              // 16 KB: RoPE slice of Qt
+constexpr int N_SLOTS = 4;
 constexpr int PB_BYTES = MAX_HEADS * TILE * 2;            // 8 KB: P of one tile
-constexpr int LAT_STEPS = DC / 16;                        // 32 score steps over c_KV
-constexpr int ROPE_STEPS = DR / 16;                       // 4 score steps over k_pe
-constexpr int SPLIT_LDS = N_SLOTS * TILE_BYTES + QR_BYTES + PB_BYTES + MAX_HEADS * 4;
+constexpr int QK_STEPS = ROW / 16;                        // 36 score steps
+constexpr int SPLIT_LDS = N_SLOTS * TILE_BYTES + 2 * PB_BYTES;
+static_assert(SPLIT_LDS <= 160 * 1024, "LDS budget of one workgroup");
 
 // s_waitcnt with only vmcnt constrained (gfx9 encoding: vmcnt in bits 3:0 and
 // 15:14, expcnt 6:4 and lgkmcnt 11:8 left at their maxima).
@@ -247,6 +260,28 @@ __device__ __forceinline__ void dma16(const void* g, uint32_t lds_addr) {
                : "memory", "m0");
 }
 
+// Same copy with the address split into a uniform 64-bit base (SGPRs) and a
+// per-lane 32-bit byte offset, so no 64-bit per-lane pointer is kept live.
+__device__ __forceinline__ void dma16s(const void* base, uint32_t voff, uint32_t lds_addr) {
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(base), "s"(lds_addr)
+               : "memory", "m0");
+}
+
+// Score MFMA (32x32x16 bf16) with its accumulator in VGPRs, written out so the
+// compiler does not place it in AGPRs (all of which hold the value
+// accumulators) and shuttle registers around it. Chained MFMAs on the same
+// accumulator need no wait states; mfma_qk_done() pads the wait states a
+// vector instruction needs before it reads (or writes) the result.
+__device__ __forceinline__ void mfma_qk_first(f32x16& acc, bf16x8_t a, bf16x8_t b) {
+  asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=v"(acc) : "v"(a), "v"(b));
+}
+__device__ __forceinline__ void mfma_qk(f32x16& acc, bf16x8_t a, bf16x8_t b) {
+  asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(acc) : "v"(a), "v"(b));
+}
+__device__ __forceinline__ void mfma_qk_done(f32x16& acc) {
+  asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" : "+v"(acc));
+}
+
 // Workgroup barrier for LDS traffic only. __syncthreads() also waits for all
 // outstanding global loads (vmcnt 0), which would drain the tile prefetch.
 __device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
@@ -258,9 +293,6 @@ __global__ __launch_bounds__(SPLIT_THREADS, 1) void k_split(int H, int B, int sp
                                                             int max_blocks, const int32_t* __restrict__ ctx_lens,
                                                             float* __restrict__ part_o, float* __restrict__ part_ml) {
   __shared__ __attribute__((aligned(1024))) char lds[SPLIT_LDS];
-  char* const qr = lds + N_SLOTS * TILE_BYTES;
-  char* const pb = qr + QR_BYTES;
-  float* const ab = (float*)(pb + PB_BYTES);
   const int split = blockIdx.x, b = blockIdx.y;
   const int L = ctx_lens[b];
   const int t_begin = split * pps * PAGE;
@@ -273,46 +305,48 @@ __global__ __launch_bounds__(SPLIT_THREADS, 1) void k_split(int H, int B, int sp
   const int h_own = w * 32 + hl;  // head of this lane in the score phase
   const int32_t* table = block_table + (size_t)b * max_blocks;
 
-  // Streams tile i into ring slot i % 3: 9 direct-to-LDS 16-byte loads per
+  // Streams tile i into ring slot i % 4: 9 direct-to-LDS 16-byte loads per
   // lane. Instruction k of wave w fills slot chunks [(w*9+k)*64, +64) in
   // order; each lane picks the global chunk that belongs at its (swizzled)
-  // position.
-  // The 9 loads of wave w cover exactly rows 8w .. 8w+7 of the tile, so the
-  // per-lane global offsets are the same for every tile: computed once here.
-  uint32_t ld_off[TILE_LOADS];
+  // position. The 9 loads of wave w cover exactly rows 8w .. 8w+7 of the
+  // tile, so the per-lane global offsets are the same for every tile.
+  // (offsets < 36864: two per register, unpacked at each use)
+  uint32_t ld_off[(TILE_LOADS + 1) / 2];
 #pragma unroll
   for (int k = 0; k < TILE_LOADS; ++k) {
     const int pos = (w * TILE_LOADS + k) * 64 + lane;
     const int t = pos / ROW_CHUNKS, jp = pos - t * ROW_CHUNKS;
-    ld_off[k] = (uint32_t)(t * ROW_BYTES + ((jp ^ swz(t)) << 4));
+    const uint32_t off = (uint32_t)(t * ROW_BYTES + ((jp ^ swz(t)) << 4));
+    if (k & 1) ld_off[k / 2] |= off << 16;
+    else ld_off[k / 2] = off;
   }
+  // The run's page numbers (at most 32), one per lane, read once: each tile
+  // then takes its page from a register, so no scalar load (and its latency)
+  // sits in front of the copies.
+  const int run_pages = (t_end - t_begin + PAGE - 1) / PAGE;
+  const int page_of_lane = lane < run_pages ? table[t_begin / PAGE + lane] : 0;
   const uint32_t lds_base = (uint32_t)(size_t)(LDS_AS char*)lds;
   auto load_tile = [&](int i) {
-    const int t0 = t_begin + i * TILE;
-    const char* src = (const char*)(rows + ((size_t)table[t0 / PAGE] * PAGE + (t0 % PAGE)) * ROW);
+    const int page = __builtin_amdgcn_readlane(page_of_lane, i >> 1);  // TILE is half a page
+    const char* src = (const char*)(rows + ((size_t)page * PAGE + (i & 1) * TILE) * ROW);
     const uint32_t dst = __builtin_amdgcn_readfirstlane(lds_base + (i % N_SLOTS) * TILE_BYTES +
                                                         w * TILE_LOADS * 64 * 16);
 #pragma unroll
-    for (int k = 0; k < TILE_LOADS; ++k) dma16(src + ld_off[k], dst + k * 64 * 16);
+    for (int k = 0; k < TILE_LOADS; ++k) {
+      const uint32_t off = (k & 1) ? (ld_off[k / 2] >> 16) : (ld_off[k / 2] & 0xFFFFu);
+      dma16s(src, off, dst + k * 64 * 16);
+    }
   };
 
-  // RoPE slice of the query of every head, in LDS: head h's 16-byte chunk c
-  // (of 8) at h*128 + ((c ^ ((h >> 1) & 7)) * 16).
-  for (int i = threadIdx.x; i < MAX_HEADS * (DR / 8); i += SPLIT_THREADS) {
-    const int hh = i >> 3, c = i & 7;
-    u32x4 v = {0, 0, 0, 0};
-    if (hh < H) v = *(const u32x4*)(qt + ((size_t)b * H + hh) * ROW + DC + 8 * c);
-    *(u32x4*)(qr + hh * 128 + ((c ^ ((hh >> 1) & 7)) << 4)) = v;
-  }
-  // latent part of this lane's query: Qt[b, h_own, 16s + 8g .. +7], s < 32
-  // (lanes of heads >= H read head H-1; nothing of theirs is stored)
-  bf16x8_t qf[LAT_STEPS];
+  // query of this lane's head: Qt[b, h_own, 16s + 8g .. +7], s < 36 (lanes of
+  // heads >= H read head H-1; nothing of theirs is stored)
+  bf16x8_t qf[QK_STEPS];
   {
     const bf16* q = qt + ((size_t)b * H + min(h_own, H - 1)) * ROW + 8 * g;
 #pragma unroll
-    for (int s = 0; s < LAT_STEPS; ++s) qf[s] = as_bf16x8(*(const u32x4*)(q + 16 * s));
+    for (int s = 0; s < QK_STEPS; ++s) qf[s] = as_bf16x8(*(const u32x4*)(q + 16 * s));
   }
-  wait_vmcnt<0>();  // query loads done: from here on only tile loads use vmcnt
+  wait_vmcnt<0>();  // query and page loads done: from here on only tile loads use vmcnt
   load_tile(0);
   if (n_tiles > 1) load_tile(1);
 
@@ -327,11 +361,11 @@ __global__ __launch_bounds__(SPLIT_THREADS, 1) void k_split(int H, int B, int sp
   // compile-time immediate):
   //  score operand, step s: row hl, chunk (2s + g) ^ swz(hl)
   //    = qk_off[s % 4] + (s / 4) * 128
-  //  RoPE query operand, step r: head h_own, chunk 2r + g
   //  value operand (column tile ct, step j, half a/b): rows 16j + 4g + i16/4
   //    (+8 for b), columns 128w + 32ct + 16(G%2) + 4(i16%4) .. +3
   //    = pv_off[ct % 2][a/b] + 16*j*ROW_BYTES + (ct / 2) * 128
-  int qk_off[4], pv_off[2][2], qr_off[ROPE_STEPS];
+  //  P fragment (head tile ht, step j): buffer + (2ht + j) * 1024 + 16 lane
+  int qk_off[4], pv_off[2][2];
   {
     const int x = swz(hl);
 #pragma unroll
@@ -343,118 +377,198 @@ __global__ __launch_bounds__(SPLIT_THREADS, 1) void k_split(int H, int B, int sp
       pv_off[par][0] = ra * ROW_BYTES + (((4 * par + y0) ^ swz(ra)) << 4) + sub + w * 256;
       pv_off[par][1] = rb * ROW_BYTES + (((4 * par + y0) ^ swz(rb)) << 4) + sub + w * 256;
     }
-#pragma unroll
-    for (int r = 0; r < ROPE_STEPS; ++r) qr_off[r] = h_own * 128 + (((2 * r + g) ^ ((h_own >> 1) & 7)) << 4);
   }
-  const LDS_AS char* qrl = (const LDS_AS char*)qr;
-  const LDS_AS char* pbl = (const LDS_AS char*)pb;
+  auto slot = [&](int i) { return (const LDS_AS char*)(lds + ((i + N_SLOTS) % N_SLOTS) * TILE_BYTES); };
+  auto pbuf = [&](int i) { return (LDS_AS char*)(lds + N_SLOTS * TILE_BYTES + (i & 1) * PB_BYTES) + lane * 16; };
 
-  for (int i = 0; i < n_tiles; ++i) {
+  // ---- online softmax of the owned heads, in 8 slices (slice k of 8) ----
+  // slices 0-1: tile max, new reference and its shift k; slices
+  // 2-7: exponentials, row sum, bf16 P fragments
+  float sm_mx, sm_sub, sm_alpha, sm_lsum;
+  int sm_k;
+  bf16x8_t pk[2];
+  auto softmax_slice = [&](const f32x16& sc, int k) {
+    if (k == 0) {
+      sm_mx = sc[0];
+#pragma unroll
+      for (int r = 1; r < 8; ++r) sm_mx = fmaxf(sm_mx, sc[r]);
+    } else if (k == 1) {
+#pragma unroll
+      for (int r = 8; r < 16; ++r) sm_mx = fmaxf(sm_mx, sc[r]);
+      sm_mx = fmaxf(sm_mx, __shfl_xor(sm_mx, 32, 64));
+      // first tile: the reference is the exact max (its p is exactly 1);
+      // later moves are by whole steps k >= 9
+      const bool first = m_run == -INFINITY;
+      const bool up = !first && sm_mx > m_run + 8.f;
+      const float kf = up ? fminf(ceilf(sm_mx - m_run), 255.f) : 0.f;
+      sm_k = (int)kf;
+      sm_alpha = __builtin_amdgcn_ldexpf(1.f, -sm_k);
+      m_run = first ? sm_mx : m_run + kf;
+      sm_sub = m_run;
+      sm_lsum = 0.f;
+    } else {
+      // slices 2..7 take elements 0-2, 3-5, 6-8, 9-11, 12-14, 15
+      const int e0 = 3 * (k - 2), e1 = min(e0 + 3, 16);
+#pragma unroll
+      for (int e = e0; e < e1; ++e) {
+        const float pe = __builtin_amdgcn_exp2f(sc[e] - sm_sub);
+        sm_lsum += pe;
+        pk[e >> 3][e & 7] = (__bf16)pe;
+      }
+      if (k == 7) {
+        l_run = l_run * sm_alpha + sm_lsum;
+      }
+    }
+  };
+
+  // publish P of tile i (after its softmax); a moved reference travels in the
+  // sign bits of the first fragment, re-stored in that (rare) case. Storing
+  // first keeps the exponentials in the MFMA groups: nothing lets them sink
+  // past a branch to their store.
+  auto publish = [&](int i) {
+    LDS_AS char* pb = pbuf(i);
+    *(LDS_AS bf16x8_t*)(pb + (w * 2) * 1024) = pk[0];
+    *(LDS_AS bf16x8_t*)(pb + (w * 2 + 1) * 1024) = pk[1];
+    if (__ballot(sm_k != 0)) {
+      u32x4 v = __builtin_bit_cast(u32x4, pk[0]);
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+        v[q] |= (((uint32_t)sm_k >> (2 * q)) & 1u) << 15 | (((uint32_t)sm_k >> (2 * q + 1)) & 1u) << 31;
+      *(LDS_AS u32x4*)(pb + (w * 2) * 1024) = v;
+    }
+  };
+
+  // ---- one pipeline step -------------------------------------------------
+  // QK: scores of this wave's 32 heads over the 32 rows of tile i (36 MFMAs).
+  // PV: O^T[c, h] += V^T[c, t] P[t, h] for tile i - 1 (8 groups of 4 MFMAs,
+  // group k = step k / 4, column tile k % 4).
+  // The score MFMAs are interleaved with PV groups 0-3 (9 score steps per
+  // group), so the score operands' LDS reads are spread over 52 MFMAs; the
+  // softmax of tile i then runs between PV groups 4-7. Issue order is pinned
+  // with scheduling barriers, LDS reads a few MFMAs ahead of their use.
+  auto step = [&](auto do_qk, auto do_pv, int i) {
+    constexpr bool QK = decltype(do_qk)::value, PV = decltype(do_pv)::value;
+    const LDS_AS char* tq = slot(i);
+    const LDS_AS char* tv = slot(i - 1);
+    const LDS_AS char* pb = pbuf(i - 1);
+    bf16x8_t pf[4];  // P fragments of the current PV step j (j = 0 first)
+    bf16x8_t va[2];
+    auto va_read = [&](int k) {
+      const int j = k >> 2, ct = k & 3;
+      const int off = 16 * j * ROW_BYTES + (ct >> 1) * 128;
+      return cat_tr(tr_read(tv + pv_off[ct & 1][0] + off), tr_read(tv + pv_off[ct & 1][1] + off));
+    };
+    auto pv_group = [&](int k) {
+      const int ct = k & 3;
+      if (k + 1 < 8) va[(k + 1) & 1] = va_read(k + 1);
+#pragma unroll
+      for (int ht = 0; ht < 4; ++ht) {
+        o[ct][ht] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[k & 1], pf[ht], o[ct][ht], 0, 0, 0);
+        if (k == 3) pf[ht] = *(const LDS_AS bf16x8_t*)(pb + (2 * ht + 1) * 1024);
+      }
+    };
+    if constexpr (PV) {
+#pragma unroll
+      for (int ht = 0; ht < 4; ++ht) pf[ht] = *(const LDS_AS bf16x8_t*)(pb + (2 * ht) * 1024);
+      // sign bits set: the owner moved its reference; decode k from the raw
+      // fragment, then clear the bits (always: a branch that rewrites the
+      // fragments costs more registers than the 16 ANDs)
+      u32x4 raw[4];
+      uint32_t flag = 0;
+#pragma unroll
+      for (int ht = 0; ht < 4; ++ht) {
+        raw[ht] = __builtin_bit_cast(u32x4, pf[ht]);
+        flag |= (raw[ht][0] | raw[ht][1] | raw[ht][2] | raw[ht][3]) & 0x80008000u;
+        u32x4 v = raw[ht];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) v[q] &= 0x7FFF7FFFu;
+        pf[ht] = __builtin_bit_cast(bf16x8_t, v);
+      }
+      if (__ballot(flag != 0)) {
+#pragma unroll
+        for (int ht = 0; ht < 4; ++ht) {
+          int kk = 0;
+#pragma unroll
+          for (int q = 0; q < 4; ++q)
+            kk |= (int)((raw[ht][q] >> 15) & 1u) << (2 * q) | (int)((raw[ht][q] >> 31) & 1u) << (2 * q + 1);
+          const float al = __builtin_amdgcn_ldexpf(1.f, -kk);
+#pragma unroll
+          for (int ct = 0; ct < 4; ++ct)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+              float x = o[ct][ht][r];
+              scale_acc(x, al);
+              o[ct][ht][r] = x;
+            }
+        }
+      }
+      va[0] = va_read(0);
+    }
+    f32x16 sc;
+    if constexpr (QK) {
+      constexpr int QK_AHEAD = 4;
+      u32x4 fa[QK_AHEAD];
+#pragma unroll
+      for (int s = 0; s < QK_AHEAD; ++s) fa[s] = *(const LDS_AS u32x4*)(tq + qk_off[s & 3] + (s >> 2) * 128);
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int s = 0; s < QK_STEPS; ++s) {
+        if (s == 0) mfma_qk_first(sc, as_bf16x8(fa[0]), qf[0]);
+        else mfma_qk(sc, as_bf16x8(fa[s % QK_AHEAD]), qf[s]);
+        if (s == QK_STEPS - 1) mfma_qk_done(sc);
+        if (s + QK_AHEAD < QK_STEPS)
+          fa[s % QK_AHEAD] = *(const LDS_AS u32x4*)(tq + qk_off[(s + QK_AHEAD) & 3] + ((s + QK_AHEAD) >> 2) * 128);
+        __builtin_amdgcn_sched_barrier(0);
+        if constexpr (PV) {
+          if (s % 9 == 8) {
+            pv_group(s / 9);
+            __builtin_amdgcn_sched_barrier(0);
+          }
+        }
+      }
+      // mask rows past the context (last tile only); lane rows: 8(r/4) + 4g + r%4
+      const int valid = t_end - (t_begin + i * TILE);
+      if (valid < TILE) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          if (8 * (r >> 2) + 4 * g + (r & 3) >= valid) sc[r] = -INFINITY;
+      }
+    } else if constexpr (PV) {
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        pv_group(k);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+#pragma unroll
+    for (int k = 4; k < 8; ++k) {
+      if constexpr (PV) pv_group(k);
+      if constexpr (QK) {
+        softmax_slice(sc, 2 * (k - 4));
+        softmax_slice(sc, 2 * (k - 4) + 1);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    if constexpr (QK) publish(i);
+  };
+
+  using T = std::true_type;
+  using F = std::false_type;
+  // iteration 0: scores and softmax of tile 0
+  wait_vmcnt<TILE_LOADS>();
+  if (n_tiles == 1) wait_vmcnt<0>();
+  lds_barrier();
+  if (n_tiles > 2) load_tile(2);
+  step(T{}, F{}, 0);
+  for (int i = 1; i < n_tiles; ++i) {
     if (i + 1 < n_tiles) wait_vmcnt<TILE_LOADS>();  // tile i landed, tile i+1 may fly
     else wait_vmcnt<0>();
-    lds_barrier();  // tile i visible to all; slot (i+2)%3 and P/alpha buffers free
+    lds_barrier();  // tile i and P of tile i-1 visible; slot (i+2)%4 and P buffer i%2 free
     if (i + 2 < n_tiles) load_tile(i + 2);
-    const LDS_AS char* tile = (const LDS_AS char*)(lds + (i % N_SLOTS) * TILE_BYTES);
-
-    // ---- scores of this wave's 32 heads over the tile's 32 rows ----
-    // Issue order is pinned to "MFMA s, read s+QK_AHEAD" so the LDS reads run
-    // while the MFMAs execute (in-order issue would otherwise hold them back).
-    f32x16 sc = {};
-    {
-      constexpr int QK_AHEAD = 4;
-      u32x4 fa[QK_AHEAD], fb[QK_AHEAD];
-      auto qk_read = [&](int s) {
-        fa[s % QK_AHEAD] = *(const LDS_AS u32x4*)(tile + qk_off[s & 3] + (s >> 2) * 128);
-        if (s >= LAT_STEPS) fb[s % QK_AHEAD] = *(const LDS_AS u32x4*)(qrl + qr_off[(s - LAT_STEPS) & 3]);
-      };
-#pragma unroll
-      for (int s = 0; s < QK_AHEAD; ++s) qk_read(s);
-#pragma unroll
-      for (int s = 0; s < ROW / 16; ++s) {
-        const bf16x8_t bq = s < LAT_STEPS ? qf[s < LAT_STEPS ? s : 0] : as_bf16x8(fb[s % QK_AHEAD]);
-        sc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(fa[s % QK_AHEAD]), bq, sc, 0, 0, 0);
-        if (s + QK_AHEAD < ROW / 16) qk_read(s + QK_AHEAD);
-        __builtin_amdgcn_sched_barrier(0);
-      }
-    }
-    // mask rows past the context (last tile only); lane rows: 8(r/4) + 4g + r%4
-    const int valid = t_end - (t_begin + i * TILE);
-    if (valid < TILE) {
-#pragma unroll
-      for (int r = 0; r < 16; ++r)
-        if (8 * (r >> 2) + 4 * g + (r & 3) >= valid) sc[r] = -INFINITY;
-    }
-    // ---- online softmax of the owned heads ----
-    float mx = sc[0];
-#pragma unroll
-    for (int r = 1; r < 16; ++r) mx = fmaxf(mx, sc[r]);
-    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-    // Lazy rescaling: the reference max only moves when the tile max exceeds
-    // it by more than 8 (so p <= 2^8); a lane's first tile just sets it.
-    float alpha = 1.f;
-    if (mx > m_run + 8.f) {
-      if (m_run != -INFINITY) alpha = __builtin_amdgcn_exp2f(m_run - mx);
-      m_run = mx;
-    }
-    l_run *= alpha;
-    {
-      float lsum = 0.f;
-      // P fragment (head tile w, step j, lane group g, head hl): the 8 rows
-      // 16j + 8(k/4) + 4g + k%4 = this lane's registers 8j .. 8j+7
-#pragma unroll
-      for (int j = 0; j < 2; ++j) {
-        bf16x8_t pk;
-#pragma unroll
-        for (int k = 0; k < 8; ++k) {
-          const float e = __builtin_amdgcn_exp2f(sc[8 * j + k] - m_run);
-          lsum += e;
-          pk[k] = (__bf16)e;
-        }
-        *(LDS_AS bf16x8_t*)((LDS_AS char*)pb + (w * 2 + j) * 1024 + lane * 16) = pk;
-      }
-      l_run += lsum;
-    }
-    if (g == 0) ab[h_own] = alpha;
-    lds_barrier();  // P and alpha of all heads visible
-
-    // ---- rescale (rare), then O^T[c, h] += V^T[c, t] P[t, h] ----
-    float al[4];
-#pragma unroll
-    for (int ht = 0; ht < 4; ++ht) al[ht] = ab[32 * ht + hl];
-    if (__ballot(al[0] != 1.f || al[1] != 1.f || al[2] != 1.f || al[3] != 1.f)) {
-#pragma unroll
-      for (int ct = 0; ct < 4; ++ct)
-#pragma unroll
-        for (int ht = 0; ht < 4; ++ht)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            float x = o[ct][ht][r];
-            scale_acc(x, al[ht]);
-            o[ct][ht][r] = x;
-          }
-    }
-    // value fragments (4 column tiles) and P fragments (4 head tiles) of step
-    // j; step 1's reads are issued between step 0's MFMAs
-    bf16x8_t va[2][4], pf[2][4];
-    auto pv_read = [&](int j, int ct) {
-      const int k = 16 * j * ROW_BYTES + (ct >> 1) * 128;
-      va[j][ct] = cat_tr(tr_read(tile + pv_off[ct & 1][0] + k), tr_read(tile + pv_off[ct & 1][1] + k));
-      pf[j][ct] = *(const LDS_AS bf16x8_t*)(pbl + (ct * 2 + j) * 1024 + lane * 16);
-    };
-#pragma unroll
-    for (int q = 0; q < 4; ++q) pv_read(0, q);
-    __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-    for (int j = 0; j < 2; ++j)
-#pragma unroll
-      for (int ct = 0; ct < 4; ++ct) {
-#pragma unroll
-        for (int ht = 0; ht < 4; ++ht)
-          o[ct][ht] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[j][ct], pf[j][ht], o[ct][ht], 0, 0, 0);
-        if (j == 0) pv_read(1, ct);
-        __builtin_amdgcn_sched_barrier(0);
-      }
+    step(T{}, T{}, i);
   }
+  lds_barrier();
+  step(F{}, T{}, n_tiles);
 
   // ---- partials: (m, l) by the head owner, O slices by the column owner ----
   l_run += __shfl_xor(l_run, 32, 64);
@@ -589,6 +703,11 @@ bool decode_fast_supported(const mla_dims& d, const CacheView& c) {
   return d.dtype == MLA_BF16 && d.d_c == DC && d.d_rope == DR && d.d_nope == DN && d.d_v == DV &&
          d.n_heads <= MAX_HEADS && c.paged &&
          c.block_size == PAGE;
+}
+
+bool decode_fast_context_ok(int max_context) {
+  // a run's page numbers are held one per lane of a wave
+  return plan_splits(1, max_context).pages_per_split <= 64;
 }
 
 size_t decode_fast_workspace(const mla_dims& d, int batch, int max_context) {

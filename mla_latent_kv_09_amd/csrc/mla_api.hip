@@ -115,7 +115,9 @@ mla_status mla_decode_workspace_size(const mla_dims* d, int32_t batch, int32_t m
   if (st != MLA_OK) return st;
   if (!bytes) return MLA_ERR_NULL_ARG;
   if (batch < 0 || max_context < 0) return MLA_ERR_BAD_SHAPE;
-  *bytes = (fast_dims(d) && batch > 0 && max_context > 0) ? mla::decode_fast_workspace(*d, batch, max_context) : 0;
+  *bytes = (fast_dims(d) && batch > 0 && max_context > 0 && mla::decode_fast_context_ok(max_context))
+               ? mla::decode_fast_workspace(*d, batch, max_context)
+               : 0;
   return MLA_OK;
 }
 
@@ -205,7 +207,7 @@ mla_status mla_decode(const mla_dims* d, int32_t batch, const void* q_nope, cons
     return MLA_ERR_ALIGNMENT;
   CacheView v{};
   if ((st = check_cache(cache, &v)) != MLA_OK) return st;
-  const bool fast = mla::decode_fast_supported(*d, v);
+  const bool fast = mla::decode_fast_supported(*d, v) && mla::decode_fast_context_ok(cache->max_context);
   const size_t need = fast ? mla::decode_fast_workspace(*d, batch, cache->max_context) : 0;
   if ((st = check_ws(ws, ws_bytes, need)) != MLA_OK) return st;
   hipStream_t s = (hipStream_t)stream;
