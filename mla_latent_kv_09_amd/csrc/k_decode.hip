@@ -117,8 +117,8 @@ WsLayout ws_layout(int H, int batch, int splits) {
 // every sequence as the transposed product Qt^T[c, b] = sum_j W_UK[h*128+j, c]
 // q_nope[b, h, j]: the 128 x 64 slice of W_UK,h is staged in LDS and read
 // transposed (as the A operand); each lane then holds 4 consecutive columns of
-// one sequence and stores them with one 8-byte write. Block (h, 0) also writes
-// the rotated, scaled q_pe slice.
+// one sequence and stores them with one 8-byte write. The blocks of head h
+// also write its rotated, scaled q_pe slice, each for every 8th sequence.
 __global__ __launch_bounds__(256) void k_absorb(int B, int H, const bf16* __restrict__ q_nope,
                                                 const bf16* __restrict__ q_pe, const bf16* __restrict__ w_uk,
                                                 const int32_t* __restrict__ ctx_lens, float qscale, float base,
@@ -183,11 +183,13 @@ __global__ __launch_bounds__(256) void k_absorb(int B, int H, const bf16* __rest
       }
     }
   }
-  if (blockIdx.y == 0) {
-    // thread -> pair i = tid % 32 (fixed), sequences tid / 32, +8, ...
+  {
+    // the rotated, scaled q_pe slice, spread over the DC / 64 blocks of the
+    // head: thread -> pair i = tid % 32 (fixed); block y takes sequences
+    // 8k + y, thread group tid / 32 every 64th of those
     const int i = threadIdx.x & (DR / 2 - 1);
     const double theta = pow((double)base, -2.0 * (double)i / (double)DR);
-    for (int b = threadIdx.x / (DR / 2); b < B; b += 256 / (DR / 2)) {
+    for (int b = (threadIdx.x / (DR / 2)) * (DC / 64) + blockIdx.y; b < B; b += (256 / (DR / 2)) * (DC / 64)) {
       const double ang = (double)(ctx_lens[b] - 1) * theta;
       // reduce to [-pi, pi] in double, then single-precision sin/cos
       const float r = (float)(ang - 6.283185307179586 * rint(ang * 0.15915494309189535));
@@ -596,7 +598,7 @@ __global__ __launch_bounds__(SPLIT_THREADS, 1) void k_split(int H, int B, int sp
 // One block per (head, tile of 16 sequences). Blocks of the same head share
 // blockIdx % 8, i.e. the same XCD and L2, so W_UV,h is fetched from HBM once.
 //   1. per sequence: M = max_s m_s, weights e_s = 2^(m_s - M), 1 / sum_s e_s l_s
-//      (one wave per 4 sequences, lanes over splits)
+//      (16 lanes per sequence, each over every 16th split)
 //   2. o_c = sum_s e_s O_s / sum_s e_s l_s, 16 threads per sequence, all the
 //      split loads of a thread issued together; bf16 into LDS
 //   3. out^T[v, b] = sum_c W_UV[h*128 + v, c] o_c[b, c] on MFMA; each lane ends
@@ -625,22 +627,25 @@ __global__ __launch_bounds__(256) void k_combine_uv(int H, int B, int splits, in
   for (int ks = 0; ks < DC / 32; ++ks)
 #pragma unroll
     for (int mt = 0; mt < 2; ++mt) wf[ks][mt] = *(const u32x4*)(wv + (size_t)(32 * w + 16 * mt + i16) * DC + 32 * ks + 8 * G);
-#pragma unroll
-  for (int rr = 0; rr < 4; ++rr) {
-    const int r = 4 * w + rr, b = b0 + r;
+  // 1. lane group rr = lane / 16 of wave w owns sequence r = 4w + rr; lane q of
+  // the group takes splits q, q + 16, ...; 16-lane reductions
+  {
+    const int rr = lane >> 4, q = lane & 15, r = 4 * w + rr, b = b0 + r;
     const int ns = b < B ? ((ctx_lens[b] + PAGE - 1) / PAGE + pps - 1) / pps : 0;
     const float* ml = part_ml + ((size_t)h * B + (b < B ? b : 0)) * splits * 2;
     float M = -INFINITY;
-    for (int s = lane; s < ns; s += 64) M = fmaxf(M, ml[2 * s]);
-    M = wave_max(M);
+    for (int sp = q; sp < ns; sp += 16) M = fmaxf(M, ml[2 * sp]);
+#pragma unroll
+    for (int o = 8; o > 0; o >>= 1) M = fmaxf(M, __shfl_xor(M, o, 64));
     float l = 0.f;
-    for (int s = lane; s < splits; s += 64) {
-      const float e = s < ns ? __builtin_amdgcn_exp2f(ml[2 * s] - M) : 0.f;
-      wgt[r][s] = e;
-      if (s < ns) l += e * ml[2 * s + 1];
+    for (int sp = q; sp < splits; sp += 16) {
+      const float e = sp < ns ? __builtin_amdgcn_exp2f(ml[2 * sp] - M) : 0.f;
+      wgt[r][sp] = e;
+      if (sp < ns) l += e * ml[2 * sp + 1];
     }
-    l = wave_sum(l);
-    if (lane == 0) inv_l[r] = ns > 0 ? 1.f / l : 0.f;
+#pragma unroll
+    for (int o = 8; o > 0; o >>= 1) l += __shfl_xor(l, o, 64);
+    if (q == 0) inv_l[r] = ns > 0 ? 1.f / l : 0.f;
   }
   __syncthreads();
   {
