@@ -1,14 +1,21 @@
-"""Benchmark of the MLA decode hot path on one MI355X.
+"""Benchmark of the MLA hot path on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload 3]
+    python bench.py --workload 5          (prefill: projections + attention)
+    python bench.py --copy-bytes N        (known-size copy, for counter scaling)
 
-One step is one mla_decode call (query absorption, split-context attention
-over the paged latent cache, log-sum-exp combine and per-head W_UV) for one
-new token of every sequence in the batch, on seeded synthetic inputs that are
-already resident in HBM. Prints one JSON line with the decode throughput,
-the roofline position of the dominant kernel (timed with HIP events recorded
-around each library launch during the timed region) and the CPU oracle timed
-on a bounded sample of the same workload.
+Decode (workloads 2-4; 3 is the default): one step is one mla_decode call
+(query absorption, split-context attention over the paged latent cache,
+log-sum-exp combine and per-head W_UV) for one new token of every sequence in
+the batch, on seeded synthetic inputs that are already resident in HBM.
+Prefill (workload 5): one step is mla_rope_latent_project (latent rows into
+the cache, query path) followed by causal mla_prefill.
+
+Prints one JSON line with the throughput, the roofline position of the
+dominant kernel (timed with HIP events recorded around each library launch
+during the timed region; HBM traffic from the committed counter summary when
+it matches the kernel's source) and the CPU oracle timed on a bounded sample of
+the same workload.
 """
 from __future__ import annotations
 
@@ -46,6 +53,9 @@ def parse():
     ap.add_argument("--workload", type=int, default=3, choices=sorted(WORKLOAD_NAMES))
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="budget of the CPU oracle sample")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle leg")
+    ap.add_argument("--copy-bytes", type=int, default=0,
+                    help="instead of a workload, run 5 device-to-device copies of this many bytes "
+                         "(the known-size kernel that calibrates the HBM byte counters)")
     return ap.parse_args()
 
 
@@ -66,6 +76,56 @@ def profile_end(lib):
         nm = names.raw[i * name_len:(i + 1) * name_len].split(b"\0", 1)[0].decode()
         out[nm] = (tot[i], cnt[i])
     return out
+
+
+PROFILES = os.path.join(ROOT, "profiles")
+
+
+def source_digest(rel):
+    import hashlib
+    with open(os.path.join(ROOT, rel), "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()
+
+
+def measured_traffic(name, source):
+    """HBM bytes per launch of a kernel from its committed counter summary
+    (profiles/<name>_hbm_traffic.md): FETCH_SIZE and WRITE_SIZE (KiB per
+    dispatch), each scaled by what the same counter reads for a copy kernel of
+    known size. None when there is no summary or the kernel's source file has
+    changed since the counters were taken."""
+    path = os.path.join(PROFILES, f"{name}_hbm_traffic.md")
+    if not os.path.exists(path):
+        return None
+    vals = {}
+    with open(path) as f:
+        for line in f:
+            if ":" in line and line.strip().startswith("- `"):
+                k, v = line.strip()[3:].split("`", 1)
+                vals[k] = v.split(":", 1)[1].strip().strip("`")
+    try:
+        if vals["source_sha256"] != source_digest(source):
+            return None
+        return int(float(vals["fetch_kib"]) * 1024 * float(vals["fetch_scale"]) +
+                   float(vals["write_kib"]) * 1024 * float(vals["write_scale"]))
+    except (KeyError, ValueError):
+        return None
+
+
+def copy_calibration(nbytes):
+    """Five device-to-device copies of nbytes (reads nbytes, writes nbytes)."""
+    import torch
+    src = torch.empty(nbytes, dtype=torch.uint8, device="cuda:0").fill_(1)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ev0.record()
+    for _ in range(5):
+        dst.copy_(src)
+    ev1.record()
+    torch.cuda.synchronize()
+    ms = ev0.elapsed_time(ev1) / 5
+    print(json.dumps({"copy_bytes": nbytes, "ms_per_copy": round(ms, 4),
+                      "GB_per_s_read_plus_write": round(2 * nbytes / (ms * 1e-3) / 1e9, 1)}), flush=True)
 
 
 def cpu_baseline(case, budget_s):
@@ -93,6 +153,38 @@ def cpu_baseline(case, budget_s):
     return {"value": done / dt, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
             "sample": f"{done} of {case.batch} sequences ({toks} cached tokens, all {case.dims.n_heads} heads), "
                       f"float64 numpy, {dt:.1f} s"}
+
+
+def cpu_baseline_prefill(case, budget_s):
+    """The oracle as it stands on a prefix of sequence 0 of the prefill
+    workload: latent and query projection, then causal attention with the
+    explicit per-head keys and values, for the first n tokens, with n doubled
+    from 64 while the budget lasts."""
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        threads = len(os.sched_getaffinity(0))
+    dims = case.dims
+    n, best, t_all = 64, None, time.perf_counter()
+    while n <= case.seq_len:
+        t0 = time.perf_counter()
+        h = case.h[:n]
+        rows = oracle.latent_rows(h, case.w_dkv, case.w_kr, np.arange(n), dims.rope_base, store="bf16")
+        qn, qp = oracle.query_projection(h, case.w_dq, case.w_uq, case.w_qr, dims.n_heads, dims.d_nope,
+                                         dims.d_rope, store="bf16")
+        oracle.prefill(dims, qn[None], qp[None], case.w_uk, case.w_uv, rows[None])
+        dt = time.perf_counter() - t0
+        best = (n, dt)
+        if time.perf_counter() - t_all + 4.5 * dt > budget_s:
+            break
+        n *= 2
+    n, dt = best
+    return {"value": n / dt, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"first {n} of {case.seq_len} tokens of sequence 0 (all {dims.n_heads} heads; projections "
+                      f"+ causal attention with explicit K/V), float64 numpy, {dt:.1f} s; the attention cost per "
+                      f"token grows with position, so the full sequence runs slower per token"}
 
 
 def prefill_bench(args):
@@ -156,12 +248,16 @@ def prefill_bench(args):
         "vs_baseline": None, "dtype": "bf16", "data": "synthetic (seeded h ~ N(0,1), weights std 1/sqrt(fan_in))",
         "config": {"workload": WORKLOAD_NAMES[5], "batch": B, "seq_len": S, "parallelism": "none (1 GPU)"},
         "roofline": {"bound": "mfma", "achieved": round(achieved, 1), "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
-                     "frac": round(achieved / BF16_PEAK_TFLOPS, 4), "traffic": None, "kernel": dom,
+                     "frac": round(achieved / BF16_PEAK_TFLOPS, 4),
+                     "traffic": measured_traffic(f"{dom}_B{B}_S{S}_H{H}", "mla_latent_kv_09_amd/csrc/k_prefill.hip")
+                     if dom == "mla_prefill_attn" else None, "kernel": dom,
                      "kernel_us": round(per[dom] * 1e3, 1), "algorithmic_flop": flop[dom]},
         "step": {"algorithmic_flop": total, "mfma_TFLOP_per_s": round(total / (ms * 1e-3) / 1e12, 1),
                  "mfma_frac": round(total / (ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 4),
                  "kernels_us": {k: round(v * 1e3, 1) for k, v in per.items()}},
     }
+    if not args.no_cpu:
+        line["cpu_baseline"] = cpu_baseline_prefill(case, args.cpu_seconds)
     print(json.dumps(line), flush=True)
 
 
@@ -173,6 +269,9 @@ def main():
               "this library has no multi-GPU path.", file=sys.stderr)
         sys.exit(2)
 
+    if args.copy_bytes > 0:
+        copy_calibration(args.copy_bytes)
+        return
     if args.workload == 5:
         prefill_bench(args)
         return
@@ -249,7 +348,9 @@ def main():
                    "cached_tokens": sum_l, "max_context": int(cache.max_context), "page": 64,
                    "parallelism": "none (1 GPU)"},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                     "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": measured_traffic(f"{split_name}_B{B}_H{H}_L{int(cache.max_context)}",
+                                                 "mla_latent_kv_09_amd/csrc/k_decode.hip"),
                      "kernel": split_name, "kernel_us": round(split_ms * 1e3, 2),
                      "algorithmic_bytes": cache_bytes,
                      "bytes_rule": f"{CACHE_ROW_BYTES} B per cached token x {sum_l} tokens"},
