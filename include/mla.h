@@ -188,6 +188,10 @@ int32_t mla_prefill_path(const mla_dims* dims, int32_t block_size, int32_t paged
  * (entries beyond max_kernels are dropped). Host-side state is shared by all
  * threads of the process. */
 mla_status mla_profile_begin(void);
+/* Restricts the timing to launches named kernel_name (as reported by
+ * mla_profile_end), so a measured loop carries two events per step instead of
+ * two per kernel; NULL or "" times every launch again. */
+mla_status mla_profile_only(const char* kernel_name);
 mla_status mla_profile_end(int32_t max_kernels, char* names, int32_t name_len, double* total_ms,
                            int32_t* launches, int32_t* n_kernels);
 

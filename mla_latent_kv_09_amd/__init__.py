@@ -81,8 +81,11 @@ def library():
         lib.mla_status_string.restype = ctypes.c_char_p
         lib.mla_decode_path.argtypes = [pd, i32, i32]
         lib.mla_prefill_path.argtypes = [pd, i32, i32]
+        lib.mla_profile_begin.argtypes = []
+        lib.mla_profile_only.argtypes = [ctypes.c_char_p]
         for f in ("mla_rope_latent_project", "mla_decode", "mla_prefill", "mla_project_workspace_size",
-                  "mla_decode_workspace_size", "mla_prefill_workspace_size"):
+                  "mla_decode_workspace_size", "mla_prefill_workspace_size", "mla_profile_begin",
+                  "mla_profile_only"):
             getattr(lib, f).restype = ctypes.c_int
         for f in ("mla_decode_path", "mla_prefill_path", "mla_version"):
             getattr(lib, f).restype = ctypes.c_int32

@@ -62,21 +62,44 @@ __device__ __forceinline__ short4_t tr_read(const LDS_AS char* p) {
 
 __device__ __forceinline__ void wait_vmem_all() { __builtin_amdgcn_s_waitcnt(0); }
 
-// x *= a for an MFMA accumulator that lives in an AGPR. Written out so the
+// x[0..7] *= a for MFMA accumulators that live in AGPRs, written out so the
 // compiler keeps the 256 output accumulators in AGPRs across the page loop
-// (a plain multiply makes it shuttle them through VGPRs and spill). The
-// leading s_nops (21 wait states) cover an MFMA that may still be writing the
-// register, the trailing one a following MFMA that reads it as its C operand.
-__device__ __forceinline__ void scale_acc(float& x, float a) {
-  float t;
+// (a plain multiply makes it shuttle them through VGPRs and spill). Eight
+// reads, eight multiplies, eight writes: each VGPR is written two or more
+// instructions before it is read. The caller pads the wait states an
+// accumulator read needs after an MFMA wrote it (rescale_fence), once per
+// rescale rather than per register.
+__device__ __forceinline__ void scale_acc8(float& x0, float& x1, float& x2, float& x3, float& x4, float& x5,
+                                           float& x6, float& x7, float a) {
+  float t0, t1, t2, t3, t4, t5, t6, t7;
   asm volatile(
-      "s_nop 7\n\ts_nop 7\n\ts_nop 4\n\t"
-      "v_accvgpr_read_b32 %1, %0\n\t"
-      "v_mul_f32 %1, %1, %2\n\t"
-      "v_accvgpr_write_b32 %0, %1\n\t"
-      "s_nop 4"
-      : "+a"(x), "=&v"(t)
+      "v_accvgpr_read_b32 %8, %0\n\tv_accvgpr_read_b32 %9, %1\n\t"
+      "v_accvgpr_read_b32 %10, %2\n\tv_accvgpr_read_b32 %11, %3\n\t"
+      "v_accvgpr_read_b32 %12, %4\n\tv_accvgpr_read_b32 %13, %5\n\t"
+      "v_accvgpr_read_b32 %14, %6\n\tv_accvgpr_read_b32 %15, %7\n\t"
+      "v_mul_f32 %8, %8, %16\n\tv_mul_f32 %9, %9, %16\n\tv_mul_f32 %10, %10, %16\n\tv_mul_f32 %11, %11, %16\n\t"
+      "v_mul_f32 %12, %12, %16\n\tv_mul_f32 %13, %13, %16\n\tv_mul_f32 %14, %14, %16\n\tv_mul_f32 %15, %15, %16\n\t"
+      "v_accvgpr_write_b32 %0, %8\n\tv_accvgpr_write_b32 %1, %9\n\t"
+      "v_accvgpr_write_b32 %2, %10\n\tv_accvgpr_write_b32 %3, %11\n\t"
+      "v_accvgpr_write_b32 %4, %12\n\tv_accvgpr_write_b32 %5, %13\n\t"
+      "v_accvgpr_write_b32 %6, %14\n\tv_accvgpr_write_b32 %7, %15"
+      : "+a"(x0), "+a"(x1), "+a"(x2), "+a"(x3), "+a"(x4), "+a"(x5), "+a"(x6), "+a"(x7), "=&v"(t0), "=&v"(t1),
+        "=&v"(t2), "=&v"(t3), "=&v"(t4), "=&v"(t5), "=&v"(t6), "=&v"(t7)
       : "v"(a));
+}
+// 21 wait states: an MFMA that may still be writing an accumulator before it
+// is read, or an accumulator write before an MFMA reads it.
+__device__ __forceinline__ void rescale_fence() { asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 4" ::: "memory"); }
+
+// Scales the 16 accumulators of one MFMA tile.
+__device__ __forceinline__ void scale_tile(f32x16& v, float a) {
+  float x[16];
+#pragma unroll
+  for (int r = 0; r < 16; ++r) x[r] = v[r];
+  scale_acc8(x[0], x[1], x[2], x[3], x[4], x[5], x[6], x[7], a);
+  scale_acc8(x[8], x[9], x[10], x[11], x[12], x[13], x[14], x[15], a);
+#pragma unroll
+  for (int r = 0; r < 16; ++r) v[r] = x[r];
 }
 
 struct Plan {
@@ -469,9 +492,21 @@ __global__ __launch_bounds__(SPLIT_THREADS, 1) void k_split(int H, int B, int sp
         if (k == 3) pf[ht] = *(const LDS_AS bf16x8_t*)(pb + (2 * ht + 1) * 1024);
       }
     };
+    // every operand read that does not depend on the rescale test is issued
+    // before it, so its LDS latency overlaps the test's
+    constexpr int QK_AHEAD = 4;
+    u32x4 fa[QK_AHEAD];
     if constexpr (PV) {
 #pragma unroll
       for (int ht = 0; ht < 4; ++ht) pf[ht] = *(const LDS_AS bf16x8_t*)(pb + (2 * ht) * 1024);
+    }
+    if constexpr (QK) {
+#pragma unroll
+      for (int s = 0; s < QK_AHEAD; ++s) fa[s] = *(const LDS_AS u32x4*)(tq + qk_off[s & 3] + (s >> 2) * 128);
+    }
+    if constexpr (PV) va[0] = va_read(0);
+    __builtin_amdgcn_sched_barrier(0);
+    if constexpr (PV) {
       // sign bits set: the owner moved its reference; decode k from the raw
       // fragment, then clear the bits (always: a branch that rewrites the
       // fragments costs more registers than the 16 ANDs)
@@ -494,24 +529,15 @@ __global__ __launch_bounds__(SPLIT_THREADS, 1) void k_split(int H, int B, int sp
           for (int q = 0; q < 4; ++q)
             kk |= (int)((raw[ht][q] >> 15) & 1u) << (2 * q) | (int)((raw[ht][q] >> 31) & 1u) << (2 * q + 1);
           const float al = __builtin_amdgcn_ldexpf(1.f, -kk);
+          if (ht == 0) rescale_fence();
 #pragma unroll
-          for (int ct = 0; ct < 4; ++ct)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-              float x = o[ct][ht][r];
-              scale_acc(x, al);
-              o[ct][ht][r] = x;
-            }
+          for (int ct = 0; ct < 4; ++ct) scale_tile(o[ct][ht], al);
         }
+        rescale_fence();
       }
-      va[0] = va_read(0);
     }
     f32x16 sc;
     if constexpr (QK) {
-      constexpr int QK_AHEAD = 4;
-      u32x4 fa[QK_AHEAD];
-#pragma unroll
-      for (int s = 0; s < QK_AHEAD; ++s) fa[s] = *(const LDS_AS u32x4*)(tq + qk_off[s & 3] + (s >> 2) * 128);
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int s = 0; s < QK_STEPS; ++s) {

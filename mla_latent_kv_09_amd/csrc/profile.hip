@@ -20,6 +20,7 @@ struct Rec {
 
 std::mutex g_mu;
 bool g_on = false;
+std::string g_only;  // when set, only launches of this name are timed
 std::vector<Rec> g_recs;
 std::vector<hipEvent_t> g_pool;
 
@@ -38,9 +39,12 @@ hipEvent_t take_event() {
 
 ProfScope::ProfScope(const char* name, hipStream_t s) : name_(name), s_(s), start_(nullptr) {
   std::lock_guard<std::mutex> lk(g_mu);
-  if (!g_on) return;
+  if (!g_on || (!g_only.empty() && g_only != name_)) return;
   start_ = take_event();
-  if (start_) hipEventRecord((hipEvent_t)start_, s_);
+  if (start_ && hipEventRecord((hipEvent_t)start_, s_) != hipSuccess) {
+    g_pool.push_back((hipEvent_t)start_);
+    start_ = nullptr;
+  }
 }
 
 ProfScope::~ProfScope() {
@@ -51,7 +55,11 @@ ProfScope::~ProfScope() {
     g_pool.push_back((hipEvent_t)start_);
     return;
   }
-  hipEventRecord(stop, s_);
+  if (hipEventRecord(stop, s_) != hipSuccess) {
+    g_pool.push_back((hipEvent_t)start_);
+    g_pool.push_back(stop);
+    return;
+  }
   g_recs.push_back(Rec{name_, (hipEvent_t)start_, stop});
 }
 
@@ -59,10 +67,17 @@ ProfScope::~ProfScope() {
 
 using mla::g_mu;
 using mla::g_on;
+using mla::g_only;
 using mla::g_pool;
 using mla::g_recs;
 
 extern "C" {
+
+mla_status mla_profile_only(const char* kernel_name) {
+  std::lock_guard<std::mutex> lk(g_mu);
+  g_only = kernel_name ? kernel_name : "";
+  return MLA_OK;
+}
 
 mla_status mla_profile_begin(void) {
   std::lock_guard<std::mutex> lk(g_mu);
