@@ -10,10 +10,12 @@
 // 4 consecutive output columns n of one row m: RoPE pairs (2i, 2i+1) sit in one
 // lane and stores are 8 bytes wide.
 //
-// Epilogues: plain store (optionally split into two outputs by column), and
-// the latent-cache epilogue of "DeepSeek-V2 paper digest" §2.1/§2.3: columns
-// >= d_c are rotated in pairs at the token's position, then the row
-// [c_KV || k_pe] is written to its cache slot.
+// Epilogues: plain store (optionally split into two outputs by column), the
+// latent-cache epilogue of "DeepSeek-V2 paper digest" §2.1/§2.3 (columns >=
+// d_c are rotated in pairs at the token's position, then the row
+// [c_KV || k_pe] is written to its cache slot), and a transposed store for
+// the prefill values (the MFMA operands swap sides, so a lane holds 4
+// consecutive rows m of one column n and stores them as 8 bytes of C^T).
 #include <math.h>
 
 #include "common.h"
@@ -145,10 +147,34 @@ __global__ __launch_bounds__(G_THREADS, 1) void k_gemm(GemmArgs g) {
 #pragma unroll
       for (int i = 0; i < 2; ++i)
 #pragma unroll
-        for (int j = 0; j < 4; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[i], fb[j], acc[i][j], 0, 0, 0);
+        for (int j = 0; j < 4; ++j)
+          acc[i][j] = EPI == 2 ? __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[j], fa[i], acc[i][j], 0, 0, 0)
+                               : __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[i], fb[j], acc[i][j], 0, 0, 0);
     }
   }
 
+  if constexpr (EPI == 2) {
+    // lane holds C[m .. m+3][n] for n = n0 + 64wn + 32i + hl,
+    // m = m0 + 128wm + 32j + 8q + 4gq (q = r / 4)
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int n = n0 + 64 * wn + 32 * i + hl;
+      if (n >= g.N) continue;
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int m = m0 + 128 * wm + 32 * j + 8 * q + 4 * gq;
+          if (m >= g.M) continue;
+          const int b = m / g.a_seq, t = m - b * g.a_seq;
+          typedef __attribute__((ext_vector_type(4))) __bf16 bf16x4_t;
+          const bf16x4_t o = {(__bf16)acc[i][j][4 * q], (__bf16)acc[i][j][4 * q + 1], (__bf16)acc[i][j][4 * q + 2],
+                              (__bf16)acc[i][j][4 * q + 3]};
+          *(bf16x4_t*)(g.c0 + ((size_t)b * g.N + n) * g.ldc0 + t) = o;
+        }
+    }
+    return;
+  }
   // epilogue: lane holds C[m][n .. n+3] for m = m0 + 128wm + 32j + hl,
   // n = n0 + 64wn + 32i + 8q + 4gq (q = r / 4)
 #pragma unroll
@@ -202,6 +228,8 @@ hipError_t gemm_fast(const GemmArgs& g, int epi, hipStream_t s) {
   const int grid = ((g.M + BM - 1) / BM) * ((g.N + BN - 1) / BN);
   if (epi == 1)
     hipLaunchKernelGGL(k_gemm<1>, dim3(grid), dim3(G_THREADS), 0, s, g);
+  else if (epi == 2)
+    hipLaunchKernelGGL(k_gemm<2>, dim3(grid), dim3(G_THREADS), 0, s, g);
   else
     hipLaunchKernelGGL(k_gemm<0>, dim3(grid), dim3(G_THREADS), 0, s, g);
   return hipGetLastError();

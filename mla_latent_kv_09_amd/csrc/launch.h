@@ -85,7 +85,10 @@ struct GemmArgs {
 };
 
 bool gemm_fast_supported(int M, int N, int K);
-hipError_t gemm_fast(const GemmArgs& g, int epi, hipStream_t s);  // epi 0 store, 1 latent rows
+// epi 0: store C[m, n]; 1: latent rows (RoPE + slot scatter); 2: transposed
+// per-sequence store C^T: row b * N + n, column m - b * a_seq of c0 with row
+// length ldc0 (m = (b, t) as for the gathered A rows; a_seq % 4 == 0)
+hipError_t gemm_fast(const GemmArgs& g, int epi, hipStream_t s);
 
 // ---- MFMA prefill attention (bf16, DeepSeek-V3 latent shape) --------------
 bool prefill_fast_supported(const mla_dims& d, const CacheView& c);
