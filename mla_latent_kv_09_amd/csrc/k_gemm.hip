@@ -13,9 +13,12 @@
 // Epilogues: plain store (optionally split into two outputs by column), the
 // latent-cache epilogue of "DeepSeek-V2 paper digest" §2.1/§2.3 (columns >=
 // d_c are rotated in pairs at the token's position, then the row
-// [c_KV || k_pe] is written to its cache slot), and a transposed store for
-// the prefill values (the MFMA operands swap sides, so a lane holds 4
-// consecutive rows m of one column n and stores them as 8 bytes of C^T).
+// [c_KV || k_pe] is written to its cache slot), and two per-head stores for
+// the prefill keys and values: C[m, n] with m = (sequence b, token t) and n =
+// (head h, dim d) goes head-major to [b][h][t][d], or transposed in blocks of
+// 64 tokens to [b][h][t / 64][d][t % 64] (for the latter the MFMA operands
+// swap sides, so a lane holds 4 consecutive rows m of one column n and stores
+// them as 8 bytes).
 #include <math.h>
 
 #include "common.h"
@@ -30,6 +33,7 @@ constexpr int A_STAGE = BM * BK * 2;  // 32 KB
 constexpr int B_STAGE = BN * BK * 2;  // 16 KB
 constexpr int STAGE = A_STAGE + B_STAGE;
 constexpr int N_STAGES = 3;
+constexpr int HEAD_W = 128;  // head width of the per-head epilogues
 constexpr int A_LOADS = BM * BK * 2 / 16 / G_THREADS;  // 8 per lane
 constexpr int B_LOADS = BN * BK * 2 / 16 / G_THREADS;  // 4 per lane
 
@@ -153,6 +157,14 @@ __global__ __launch_bounds__(G_THREADS, 1) void k_gemm(GemmArgs g) {
     }
   }
 
+  // rows m = (sequence, token): a_seq is a multiple of 64 for the per-head
+  // epilogues, so each aligned group of 64 rows belongs to one sequence
+  int seq_of[2] = {0, 0};
+  if constexpr (EPI >= 2) {
+#pragma unroll
+    for (int u = 0; u < 2; ++u) seq_of[u] = (m0 + 128 * wm + 64 * u) / g.a_seq;
+  }
+  const int n_heads = g.N / HEAD_W;
   if constexpr (EPI == 2) {
     // lane holds C[m .. m+3][n] for n = n0 + 64wn + 32i + hl,
     // m = m0 + 128wm + 32j + 8q + 4gq (q = r / 4)
@@ -161,17 +173,21 @@ __global__ __launch_bounds__(G_THREADS, 1) void k_gemm(GemmArgs g) {
       const int n = n0 + 64 * wn + 32 * i + hl;
       if (n >= g.N) continue;
 #pragma unroll
-      for (int j = 0; j < 4; ++j)
+      for (int j = 0; j < 4; ++j) {
+        const int b = seq_of[j >> 1];
+        const int t_base = m0 + 128 * wm + 32 * j - b * g.a_seq;
+        bf16* dst = g.c0 + ((((size_t)b * n_heads + n / HEAD_W) * (g.a_seq / 64) + t_base / 64) * HEAD_W +
+                            n % HEAD_W) * 64 + t_base % 64;
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
           const int m = m0 + 128 * wm + 32 * j + 8 * q + 4 * gq;
           if (m >= g.M) continue;
-          const int b = m / g.a_seq, t = m - b * g.a_seq;
           typedef __attribute__((ext_vector_type(4))) __bf16 bf16x4_t;
           const bf16x4_t o = {(__bf16)acc[i][j][4 * q], (__bf16)acc[i][j][4 * q + 1], (__bf16)acc[i][j][4 * q + 2],
                               (__bf16)acc[i][j][4 * q + 3]};
-          *(bf16x4_t*)(g.c0 + ((size_t)b * g.N + n) * g.ldc0 + t) = o;
+          *(bf16x4_t*)(dst + 8 * q + 4 * gq) = o;
         }
+      }
     }
     return;
   }
@@ -187,6 +203,7 @@ __global__ __launch_bounds__(G_THREADS, 1) void k_gemm(GemmArgs g) {
       crow = g.c0 + (size_t)g.slots[m] * g.ldc0;
       pos = g.positions[m];
     }
+    const int seq_b = seq_of[j >> 1], seq_t = m - seq_b * g.a_seq;
 #pragma unroll
     for (int i = 0; i < 2; ++i)
 #pragma unroll
@@ -211,6 +228,9 @@ __global__ __launch_bounds__(G_THREADS, 1) void k_gemm(GemmArgs g) {
           }
           const bf16x4_t o = {(__bf16)v[0], (__bf16)v[1], (__bf16)v[2], (__bf16)v[3]};
           *(bf16x4_t*)(crow + n) = o;
+        } else if (EPI == 3) {
+          const bf16x4_t o = {(__bf16)v[0], (__bf16)v[1], (__bf16)v[2], (__bf16)v[3]};
+          *(bf16x4_t*)(g.c0 + (((size_t)seq_b * n_heads + n / HEAD_W) * g.a_seq + seq_t) * HEAD_W + n % HEAD_W) = o;
         } else {
           const bf16x4_t o = {(__bf16)v[0], (__bf16)v[1], (__bf16)v[2], (__bf16)v[3]};
           if (n < g.c_split) *(bf16x4_t*)(g.c0 + (size_t)m * g.ldc0 + n) = o;
@@ -225,11 +245,14 @@ __global__ __launch_bounds__(G_THREADS, 1) void k_gemm(GemmArgs g) {
 bool gemm_fast_supported(int M, int N, int K) { return M > 0 && N > 0 && N % 4 == 0 && K > 0 && K % BK == 0; }
 
 hipError_t gemm_fast(const GemmArgs& g, int epi, hipStream_t s) {
+  if (epi >= 2 && (g.N % HEAD_W != 0 || g.a_seq % 64 != 0 || g.a_seq < 64)) return hipErrorInvalidValue;
   const int grid = ((g.M + BM - 1) / BM) * ((g.N + BN - 1) / BN);
   if (epi == 1)
     hipLaunchKernelGGL(k_gemm<1>, dim3(grid), dim3(G_THREADS), 0, s, g);
   else if (epi == 2)
     hipLaunchKernelGGL(k_gemm<2>, dim3(grid), dim3(G_THREADS), 0, s, g);
+  else if (epi == 3)
+    hipLaunchKernelGGL(k_gemm<3>, dim3(grid), dim3(G_THREADS), 0, s, g);
   else
     hipLaunchKernelGGL(k_gemm<0>, dim3(grid), dim3(G_THREADS), 0, s, g);
   return hipGetLastError();

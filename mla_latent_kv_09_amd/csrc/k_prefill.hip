@@ -44,11 +44,11 @@ constexpr int P_AHEAD = P_STAGES - 1;            // sub-tiles in flight
 constexpr int P_LOADS = P_STAGE / 16 / P_THREADS;  // 5 copies per lane and sub-tile
 constexpr int WL_V = 2 * QK_STEPS;               // wave-copies 0..23 score blocks, 24..39 value blocks
 constexpr float LOG2E_P = 1.4426950408889634f;
-constexpr int MAX_PAIRS = 64;
+constexpr int PAIRS = DR / 2;
 
 // RoPE inverse frequencies base^(-2i/d_rope), formed on the host in double
 struct RopeTab {
-  double theta[MAX_PAIRS];
+  double theta[PAIRS];
 };
 
 template <int N>
@@ -106,21 +106,35 @@ __global__ __launch_bounds__(256) void k_gather_kpe(int B, int seq_stride, const
   *(u32x4*)(kpe + tok * DR + 8 * c) = v;
 }
 
+// cos and sin of the RoPE angle pos * theta_i for every position below
+// n_pos and pair i (DeepSeek-V2 paper digest, decoupled RoPE): entry
+// [pos][i] = (cos, sin) as fp32, the angle reduced to [-pi, pi] and both
+// evaluated in double. Every query of every head at that position reads it.
+__global__ __launch_bounds__(256) void k_rope_table(int n_pos, RopeTab rope, float2* __restrict__ cs) {
+  const int i = blockIdx.x * 256 + threadIdx.x;
+  if (i >= n_pos * PAIRS) return;
+  const double ang = (double)(i / PAIRS) * rope.theta[i % PAIRS];
+  const double r = ang - 6.283185307179586 * rint(ang * 0.15915494309189535);
+  double sn, cn;
+  sincos(r, &sn, &cn);
+  cs[i] = make_float2((float)cn, (float)sn);
+}
+
 // Byte offset of the 16-byte piece that lane `lane` of wave-copy wl brings in,
 // relative to the sub-tile's base of its source (K_nope, k_pe or V^T).
-__device__ __forceinline__ uint32_t piece_off(int wl, int lane, int H, int seq_stride) {
+__device__ __forceinline__ uint32_t piece_off(int wl, int lane) {
   if (wl < WL_V) {
     const int kh = wl / QK_STEPS, st = wl % QK_STEPS;
     const int t = 32 * kh + swap23(lane & 31), d = 8 * (lane >> 5);
-    if (st < DN / 16) return (uint32_t)t * H * DN * 2 + 2 * (16 * st + d);
+    if (st < DN / 16) return (uint32_t)t * DN * 2 + 2 * (16 * st + d);
     return (uint32_t)t * DR * 2 + 2 * (16 * (st - DN / 16) + d);
   }
   const int blk = wl - WL_V, dt = blk >> 2, ks = blk & 3;
-  return (uint32_t)(32 * dt + (lane & 31)) * seq_stride * 2 + 2 * (16 * ks + 8 * (lane >> 5));
+  return (uint32_t)(32 * dt + (lane & 31)) * KS * 2 + 2 * (16 * ks + 8 * (lane >> 5));
 }
 
 __global__ __launch_bounds__(P_THREADS, 1) void k_prefill_attn(
-    int H, int B, int S, int nq, float qscale, RopeTab rope, const bf16* __restrict__ q_nope,
+    int H, int B, int S, int nq, float qscale, const float2* __restrict__ rope_cs, const bf16* __restrict__ q_nope,
     const bf16* __restrict__ q_pe, const bf16* __restrict__ kn, const bf16* __restrict__ vt, int seq_stride,
     const bf16* __restrict__ kpe, const int32_t* __restrict__ ctx_lens, bf16* __restrict__ out) {
   __shared__ __attribute__((aligned(1024))) char lds[P_STAGES * P_STAGE];
@@ -140,7 +154,9 @@ __global__ __launch_bounds__(P_THREADS, 1) void k_prefill_attn(
     }
   }
   const int h = group % H, b = group / H;
-  const int L = ctx_lens[b];
+  // contexts are at most seq_stride (the workspace rows of a sequence); the
+  // clamp only keeps a bad length from reading past them
+  const int L = min(ctx_lens[b], seq_stride);
   const int s0 = qtile * QT;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
   const int hl = lane & 31, g = lane >> 5;
@@ -156,17 +172,17 @@ __global__ __launch_bounds__(P_THREADS, 1) void k_prefill_attn(
   // to a multiple of 64 tokens and hold finite values past the context.
   uint32_t soff[P_LOADS];
 #pragma unroll
-  for (int k = 0; k < P_LOADS; ++k) soff[k] = piece_off(w * P_LOADS + k, lane, H, seq_stride);
+  for (int k = 0; k < P_LOADS; ++k) soff[k] = piece_off(w * P_LOADS + k, lane);
   const uint32_t lds_base = (uint32_t)(size_t)(LDS_AS char*)lds;
-  const char* kn_b = (const char*)kn + ((size_t)b * seq_stride * H + h) * DN * 2;
+  const char* kn_b = (const char*)kn + ((size_t)b * H + h) * seq_stride * DN * 2;
   const char* kp_b = (const char*)kpe + (size_t)b * seq_stride * DR * 2;
   const char* vt_b = (const char*)vt + ((size_t)b * H + h) * DV * seq_stride * 2;
   auto load_sub = [&](int u) {
     const uint32_t st = lds_base + (u % P_STAGES) * P_STAGE;
     const int t0 = u * KS;
-    const char* bn = kn_b + (size_t)t0 * H * DN * 2;
+    const char* bn = kn_b + (size_t)t0 * DN * 2;
     const char* bp = kp_b + (size_t)t0 * DR * 2;
-    const char* bv = vt_b + (size_t)t0 * 2;
+    const char* bv = vt_b + (size_t)t0 * DV * 2;
 #pragma unroll
     for (int k = 0; k < P_LOADS; ++k) {
       const int wl = w * P_LOADS + k;
@@ -194,16 +210,17 @@ __global__ __launch_bounds__(P_THREADS, 1) void k_prefill_attn(
     for (int st = 0; st < DR / 16; ++st) {
       const bf16x8_t v = p_as_bf16x8(*(const u32x4*)(qp + 16 * st));
       bf16x8_t o;
+      // (cos, sin) of pairs 8st + 4g .. +3 at this lane's position
+      const float2* cs_p = rope_cs + (size_t)max(pos, 0) * PAIRS + 8 * st + 4 * g;
+      const float4 cs01 = *(const float4*)cs_p;
+      const float4 cs23 = *(const float4*)(cs_p + 2);
+      const float cs[8] = {cs01.x, cs01.y, cs01.z, cs01.w, cs23.x, cs23.y, cs23.z, cs23.w};
 #pragma unroll
       for (int e = 0; e < 8; e += 2) {
-        const int pr = 8 * st + 4 * g + e / 2;  // pair index in 0 .. 31
-        const double ang = (double)pos * rope.theta[pr];
-        const float r = (float)(ang - 6.283185307179586 * rint(ang * 0.15915494309189535));
-        float sn, cs;
-        sincosf(r, &sn, &cs);
+        const float c = cs[e], sn = cs[e + 1];
         const float x0 = (float)v[e], x1 = (float)v[e + 1];
-        o[e] = (__bf16)((x0 * cs - x1 * sn) * qscale);
-        o[e + 1] = (__bf16)((x0 * sn + x1 * cs) * qscale);
+        o[e] = (__bf16)((x0 * c - x1 * sn) * qscale);
+        o[e + 1] = (__bf16)((x0 * sn + x1 * c) * qscale);
       }
       qf[DN / 16 + st] = o;
     }
@@ -346,10 +363,11 @@ int ws_stride(int max_context) { return (max_context + KS - 1) / KS * KS; }
 }  // namespace
 
 size_t prefill_fast_workspace(const mla_dims& d, int batch, int max_context) {
-  // K_nope [batch * stride, H * 128], V^T [batch * H * 128, stride] and k_pe
-  // [batch * stride, 64] of every cached token
+  // K_nope [batch][H][stride][128], V^T [batch][H][stride / 64][128][64] and
+  // k_pe [batch * stride, 64] of every cached token, then the RoPE table
+  // [stride, 32] of (cos, sin)
   const size_t rows = (size_t)batch * ws_stride(max_context);
-  return 2 * rows * d.n_heads * DN * 2 + rows * DR * 2;
+  return 2 * rows * d.n_heads * DN * 2 + rows * DR * 2 + (size_t)ws_stride(max_context) * PAIRS * 8;
 }
 
 hipError_t prefill_fast(const mla_dims& d, float scale, int batch, int seq_len, int max_context,
@@ -362,9 +380,11 @@ hipError_t prefill_fast(const mla_dims& d, float scale, int batch, int seq_len, 
   bf16* kn = (bf16*)ws;
   bf16* vt = kn + rows * H * DN;
   bf16* kpe = vt + rows * H * DV;
+  float2* rope_cs = (float2*)(kpe + rows * DR);
   // K_nope = c W_UK^T and V = c W_UV^T for every cached token (rows gathered
   // through the block table; rows past a sequence's context repeat its row 0
-  // and are masked); V is stored transposed, per (sequence, head)
+  // and are masked), head-major so that a sub-tile of one head is contiguous;
+  // V is stored transposed in blocks of 64 tokens
   GemmArgs g{};
   g.M = (int)rows;
   g.K = DC;
@@ -385,11 +405,10 @@ hipError_t prefill_fast(const mla_dims& d, float scale, int batch, int seq_len, 
   hipError_t e;
   {
     ProfScope ps("mla_prefill_kv_up", s);
-    e = gemm_fast(g, 0, s);
+    e = gemm_fast(g, 3, s);
     if (e != hipSuccess) return e;
     g.b0 = g.b1 = (const bf16*)w_uv;
     g.c0 = g.c1 = vt;
-    g.ldc0 = g.ldc1 = stride;
     e = gemm_fast(g, 2, s);
   }
   if (e != hipSuccess) return e;
@@ -400,13 +419,19 @@ hipError_t prefill_fast(const mla_dims& d, float scale, int batch, int seq_len, 
                        (const bf16*)c.rows, c.block_table, c.max_blocks, c.block_size, c.context_lens, kpe);
   }
   if ((e = hipGetLastError()) != hipSuccess) return e;
-  RopeTab rope;
-  for (int i = 0; i < MAX_PAIRS; ++i) rope.theta[i] = pow((double)d.rope_base, -2.0 * i / (double)DR);
+  {
+    ProfScope ps("mla_prefill_rope", s);
+    RopeTab rope;
+    for (int i = 0; i < PAIRS; ++i) rope.theta[i] = pow((double)d.rope_base, -2.0 * i / (double)DR);
+    hipLaunchKernelGGL(k_rope_table, dim3((unsigned)((stride * PAIRS + 255) / 256)), dim3(256), 0, s, stride, rope,
+                       rope_cs);
+  }
+  if ((e = hipGetLastError()) != hipSuccess) return e;
   {
     ProfScope ps("mla_prefill_attn", s);
     const int nq = (seq_len + QT - 1) / QT;
     hipLaunchKernelGGL(k_prefill_attn, dim3(nq * H * batch), dim3(P_THREADS), 0, s, H, batch, seq_len, nq,
-                       scale * LOG2E_P, rope, (const bf16*)q_nope, (const bf16*)q_pe, kn, vt, stride, kpe,
+                       scale * LOG2E_P, rope_cs, (const bf16*)q_nope, (const bf16*)q_pe, kn, vt, stride, kpe,
                        c.context_lens, (bf16*)out);
   }
   return hipGetLastError();

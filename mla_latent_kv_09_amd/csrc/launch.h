@@ -85,9 +85,11 @@ struct GemmArgs {
 };
 
 bool gemm_fast_supported(int M, int N, int K);
-// epi 0: store C[m, n]; 1: latent rows (RoPE + slot scatter); 2: transposed
-// per-sequence store C^T: row b * N + n, column m - b * a_seq of c0 with row
-// length ldc0 (m = (b, t) as for the gathered A rows; a_seq % 4 == 0)
+// epi 0: store C[m, n]; 1: latent rows (RoPE + slot scatter). With m = (b, t)
+// as for the gathered A rows and n = (h, d), heads of 128 columns (N % 128 == 0,
+// a_seq a multiple of 64):
+// 2: c0[b][h][t / 64][d][t % 64] (values transposed in 64-token blocks);
+// 3: c0[b][h][t][d] (head-major)
 hipError_t gemm_fast(const GemmArgs& g, int epi, hipStream_t s);
 
 // ---- MFMA prefill attention (bf16, DeepSeek-V3 latent shape) --------------
