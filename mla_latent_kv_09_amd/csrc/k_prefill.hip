@@ -36,13 +36,12 @@ namespace {
 constexpr int DN = 128, DR = 64, DK = DN + DR, DV = 128, DC = 512, ROW = DC + DR;
 constexpr int P_THREADS = 512, QW = 32, QT = 8 * QW, KS = 64;
 constexpr int QK_STEPS = DK / 16;                // 12
-constexpr int K_BLOCK = 1024;
-constexpr int V_OFF = 2 * QK_STEPS * K_BLOCK;    // 24 KB of score blocks
-constexpr int P_STAGE = V_OFF + 16 * K_BLOCK;    // + 16 KB of value blocks
+constexpr int PE_OFF = KS * DN * 2;              // stage: K_nope rows (16 KB),
+constexpr int V_OFF = PE_OFF + KS * DR * 2;      // k_pe rows (8 KB),
+constexpr int P_STAGE = V_OFF + DV * KS * 2;     // V^T rows (16 KB)
 constexpr int P_STAGES = 4;                      // 160 KB of LDS
-constexpr int P_AHEAD = P_STAGES - 1;            // sub-tiles in flight
 constexpr int P_LOADS = P_STAGE / 16 / P_THREADS;  // 5 copies per lane and sub-tile
-constexpr int WL_V = 2 * QK_STEPS;               // wave-copies 0..23 score blocks, 24..39 value blocks
+constexpr int WL_PE = PE_OFF / 1024, WL_V = V_OFF / 1024;  // first wave-copy of k_pe and V^T
 constexpr float LOG2E_P = 1.4426950408889634f;
 constexpr int PAIRS = DR / 2;
 
@@ -120,17 +119,23 @@ __global__ __launch_bounds__(256) void k_rope_table(int n_pos, RopeTab rope, flo
   cs[i] = make_float2((float)cn, (float)sn);
 }
 
-// Byte offset of the 16-byte piece that lane `lane` of wave-copy wl brings in,
-// relative to the sub-tile's base of its source (K_nope, k_pe or V^T).
+// Stage layout: row t of K_nope (256 B), of k_pe (128 B) and row d of V^T
+// (128 B = 64 keys) as in the workspace, with the 16-byte chunks of each row
+// permuted: chunk c of K_nope row t sits at c ^ (t % 16), chunk c of a 128-byte
+// row r at c ^ ((r / 2) % 8). Sixteen lanes reading the same chunk of sixteen
+// consecutive rows (the operand reads) then hit sixteen distinct groups of
+// banks, while each 1 KB copy still reads 1 KB of consecutive workspace bytes.
+// Wave-copy wl fills stage bytes [1024 wl, +1024): K_nope for wl < 16, k_pe
+// for wl < 24, V^T after.
 __device__ __forceinline__ uint32_t piece_off(int wl, int lane) {
-  if (wl < WL_V) {
-    const int kh = wl / QK_STEPS, st = wl % QK_STEPS;
-    const int t = 32 * kh + swap23(lane & 31), d = 8 * (lane >> 5);
-    if (st < DN / 16) return (uint32_t)t * DN * 2 + 2 * (16 * st + d);
-    return (uint32_t)t * DR * 2 + 2 * (16 * (st - DN / 16) + d);
+  if (wl < WL_PE) {  // rows 4wl .. 4wl+3, lane -> row 4wl + lane / 16, position lane % 16
+    const int t = 4 * wl + (lane >> 4);
+    return (uint32_t)(t * 256 + (((lane & 15) ^ (t & 15)) << 4));
   }
-  const int blk = wl - WL_V, dt = blk >> 2, ks = blk & 3;
-  return (uint32_t)(32 * dt + (lane & 31)) * KS * 2 + 2 * (16 * ks + 8 * (lane >> 5));
+  // 128-byte rows 8j .. 8j+7, lane -> row 8j + lane / 8, position lane % 8
+  const int j = wl < WL_V ? wl - WL_PE : wl - WL_V;
+  const int r = 8 * j + (lane >> 3);
+  return (uint32_t)(r * 128 + (((lane & 7) ^ ((r >> 1) & 7)) << 4));
 }
 
 __global__ __launch_bounds__(P_THREADS, 1) void k_prefill_attn(
@@ -162,9 +167,12 @@ __global__ __launch_bounds__(P_THREADS, 1) void k_prefill_attn(
   const int hl = lane & 31, g = lane >> 5;
   const int last_key = min(L - S + min(s0 + QT, S) - 1, L - 1);  // of the whole block
   const int n_sub = last_key < 0 ? 0 : last_key / KS + 1;
-  const int pos = L - S + min(s0 + QW * w + hl, S - 1);  // this lane's query position
-  const int pos_lo = L - S + min(s0 + QW * w, S - 1);    // the wave's first query
-  const int pos_hi = L - S + min(s0 + QW * w + QW - 1, S - 1);
+  // query block of the wave: the two groups (waves 0-3, 4-7) take alternate
+  // blocks of 32, so their causal work is alike
+  const int qb = 2 * (w & 3) + (w >> 2);
+  const int pos = L - S + min(s0 + QW * qb + hl, S - 1);  // this lane's query position
+  const int pos_lo = L - S + min(s0 + QW * qb, S - 1);    // the wave's first query
+  const int pos_hi = L - S + min(s0 + QW * qb + QW - 1, S - 1);
 
   // ---- copies of sub-tile u into stage u % 4: wave-copy wl = 5w + k (1 KB
   // of the stage) is all K_nope, all k_pe or all V^T, so its source base is
@@ -177,25 +185,32 @@ __global__ __launch_bounds__(P_THREADS, 1) void k_prefill_attn(
   const char* kn_b = (const char*)kn + ((size_t)b * H + h) * seq_stride * DN * 2;
   const char* kp_b = (const char*)kpe + (size_t)b * seq_stride * DR * 2;
   const char* vt_b = (const char*)vt + ((size_t)b * H + h) * DV * seq_stride * 2;
-  auto load_sub = [&](int u) {
-    const uint32_t st = lds_base + (u % P_STAGES) * P_STAGE;
-    const int t0 = u * KS;
-    const char* bn = kn_b + (size_t)t0 * DN * 2;
-    const char* bp = kp_b + (size_t)t0 * DR * 2;
-    const char* bv = vt_b + (size_t)t0 * DV * 2;
+  // source of copy k of this wave (uniform): base and bytes per sub-tile
+  const char* src_base[P_LOADS];
+  uint32_t src_step[P_LOADS];
 #pragma unroll
-    for (int k = 0; k < P_LOADS; ++k) {
-      const int wl = w * P_LOADS + k;
-      const char* base = wl >= WL_V ? bv : ((wl % QK_STEPS) < DN / 16 ? bn : bp);
-      p_dma16s(base, soff[k], __builtin_amdgcn_readfirstlane(st + wl * 1024));
-    }
+  for (int k = 0; k < P_LOADS; ++k) {
+    const int wl = w * P_LOADS + k;
+    const bool is_v = wl >= WL_V, is_n = wl < WL_PE;
+    src_base[k] = is_v ? vt_b : (is_n ? kn_b : kp_b);
+    src_step[k] = is_v ? KS * DV * 2 : (is_n ? KS * DN * 2 : KS * DR * 2);
+  }
+  // copy k (of P_LOADS) of this wave for sub-tile u
+  auto load_piece = [&](int u, int k) __attribute__((always_inline)) {
+    const uint32_t st = lds_base + (u % P_STAGES) * P_STAGE;
+    p_dma16s(src_base[k] + (size_t)u * src_step[k], soff[k],
+             __builtin_amdgcn_readfirstlane(st + (w * P_LOADS + k) * 1024));
   };
-  for (int v = 0; v < min(P_AHEAD, n_sub); ++v) load_sub(v);
+  auto load_sub = [&](int u) __attribute__((always_inline)) {
+#pragma unroll
+    for (int k = 0; k < P_LOADS; ++k) load_piece(u, k);
+  };
+  for (int v = 0; v < min(2, n_sub); ++v) load_sub(v);
 
   // ---- query fragments (B operand): 12 steps of 16 over [q_nope || RoPE(q_pe)]
   bf16x8_t qf[QK_STEPS];
   {
-    const int s_lane = min(s0 + QW * w + hl, S - 1);
+    const int s_lane = min(s0 + QW * qb + hl, S - 1);
     const bf16* qn = q_nope + (((size_t)b * S + s_lane) * H + h) * DN + 8 * g;
 #pragma unroll
     for (int st = 0; st < DN / 16; ++st) {
@@ -230,46 +245,91 @@ __global__ __launch_bounds__(P_THREADS, 1) void k_prefill_attn(
 #pragma unroll
   for (int i = 0; i < DV / 32; ++i) o[i] = (f32x16){};
   float m_run = -INFINITY, l_run = 0.f;
-  const int k_lane = 16 * lane;
+  // operand read offsets in a stage (see piece_off): score step st < 8 reads
+  // K_nope row t = swap23(hl) (+32 for the second key half), chunk 2st + g;
+  // step st >= 8 reads k_pe row t, chunk 2(st - 8) + g; value step ks of
+  // value tile dt reads V^T row 32dt + hl, chunk 2ks + g
+  uint32_t kq_off[DN / 16], pq_off[DR / 16], vq_off[4];
+  {
+    const int t = swap23(hl);
+#pragma unroll
+    for (int st = 0; st < DN / 16; ++st) kq_off[st] = t * 256 + (((2 * st + g) ^ (t & 15)) << 4);
+#pragma unroll
+    for (int j = 0; j < DR / 16; ++j) pq_off[j] = PE_OFF + t * 128 + (((2 * j + g) ^ ((t >> 1) & 7)) << 4);
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) vq_off[ks] = V_OFF + hl * 128 + (((2 * ks + g) ^ ((hl >> 1) & 7)) << 4);
+  }
+  // sub-tiles holding a key that one of this wave's queries sees
+  const int n_own = pos_hi < 0 ? 0 : min(n_sub, pos_hi / KS + 1);
+  auto stage = [&](int u) __attribute__((always_inline)) { return (const LDS_AS char*)(lds + (u % P_STAGES) * P_STAGE); };
 
-  for (int u = 0; u < n_sub; ++u) {
-    // wait for sub-tile u, make it visible, refill the stage freed by u - 1
-    const int ahead = min(P_AHEAD - 1, n_sub - 1 - u);
-    if (ahead >= 2) p_wait_vmcnt<2 * P_LOADS>();
-    else if (ahead == 1) p_wait_vmcnt<P_LOADS>();
-    else p_wait_vmcnt<0>();
-    p_lds_barrier();
-    if (u + P_AHEAD < n_sub) load_sub(u + P_AHEAD);
-    const LDS_AS char* st = (const LDS_AS char*)(lds + (u % P_STAGES) * P_STAGE);
-    const int t0 = u * KS;
-    // keys past the wave's last query: the whole sub-tile is masked for it
-    if (t0 > pos_hi) continue;
+  f32x16 sc[2];   // scores of the sub-tile between its score and softmax steps
+  bf16x8_t pf[4]; // its probabilities between the softmax and value steps
 
-    // ---- scores: two 32-key halves, 12 steps each, operands read 2 steps ahead
-    f32x16 sc[2];
-    {
-      const LDS_AS char* kp = st + k_lane;
-      u32x4 ka[3][2];
+  // ---- MFMA step: values of sub-tile u (PV), then scores of sub-tile u + 1
+  // (QK); the first score operands are read during the value MFMAs.
+  // dma_v >= 0: this step also issues this wave's copies of sub-tile dma_v,
+  // spread over its work so the copies reach the texture unit a few at a time
+  auto mfma_step = [&](auto do_pv, auto do_qk, int u, int dma_v) __attribute__((always_inline)) {
+    constexpr bool PV = decltype(do_pv)::value, QK = decltype(do_qk)::value;
+    __builtin_amdgcn_s_setprio(1);
+    const LDS_AS char* kp = stage(u + 1);
+    const LDS_AS char* vp = stage(PV ? u : 0);
+    // score operand of step st, key half kh; value operand of step k = 4dt + ks
+    auto k_read = [&](int st, int kh) __attribute__((always_inline)) {
+      return st < DN / 16 ? *(const LDS_AS u32x4*)(kp + kq_off[st] + kh * 32 * 256)
+                          : *(const LDS_AS u32x4*)(kp + pq_off[st - DN / 16] + kh * 32 * 128);
+    };
+    auto v_read = [&](int k) __attribute__((always_inline)) {
+      return *(const LDS_AS u32x4*)(vp + vq_off[k & 3] + (k >> 2) * 32 * 128);
+    };
+    // operands are read 3 MFMA steps ahead (rings of 4)
+    u32x4 ka[4][2];
+    u32x4 va[4];
+    if constexpr (PV) {
 #pragma unroll
-      for (int s = 0; s < 2; ++s)
+      for (int k = 0; k < 3; ++k) va[k] = v_read(k);
 #pragma unroll
-        for (int kh = 0; kh < 2; ++kh) ka[s][kh] = *(const LDS_AS u32x4*)(kp + (QK_STEPS * kh + s) * K_BLOCK);
+      for (int k = 0; k < 16; ++k) {
+        const int dt = k >> 2, ks = k & 3;
+        if (k + 3 < 16) va[(k + 3) & 3] = v_read(k + 3);
+        if constexpr (QK) {
+          // the first three score steps' operands, over the last value MFMAs
+          if (k >= 10) ka[(k - 10) >> 1][(k - 10) & 1] = k_read((k - 10) >> 1, (k - 10) & 1);
+        }
+        p_mfma(o[dt], p_as_bf16x8(va[k & 3]), pf[ks]);
+        if (k % 3 == 0 && k / 3 < P_LOADS && dma_v >= 0) load_piece(dma_v, k / 3);
+      }
+    } else if constexpr (QK) {
 #pragma unroll
-      for (int s = 0; s < QK_STEPS; ++s) {
-        if (s + 2 < QK_STEPS)
+      for (int st = 0; st < 3; ++st)
 #pragma unroll
-          for (int kh = 0; kh < 2; ++kh)
-            ka[(s + 2) % 3][kh] = *(const LDS_AS u32x4*)(kp + (QK_STEPS * kh + s + 2) * K_BLOCK);
-        if (s == 0) {
+        for (int kh = 0; kh < 2; ++kh) ka[st][kh] = k_read(st, kh);
+    }
+    if constexpr (QK) {
+#pragma unroll
+      for (int st = 0; st < QK_STEPS; ++st) {
+        if (st + 3 < QK_STEPS)
+#pragma unroll
+          for (int kh = 0; kh < 2; ++kh) ka[(st + 3) & 3][kh] = k_read(st + 3, kh);
+        if (st == 0) {
           p_mfma_first(sc[0], p_as_bf16x8(ka[0][0]), qf[0]);
           p_mfma_first(sc[1], p_as_bf16x8(ka[0][1]), qf[0]);
         } else {
-          p_mfma(sc[0], p_as_bf16x8(ka[s % 3][0]), qf[s]);
-          p_mfma(sc[1], p_as_bf16x8(ka[s % 3][1]), qf[s]);
+          p_mfma(sc[0], p_as_bf16x8(ka[st & 3][0]), qf[st]);
+          p_mfma(sc[1], p_as_bf16x8(ka[st & 3][1]), qf[st]);
         }
       }
       p_mfma_done(sc[0], sc[1]);
     }
+    __builtin_amdgcn_s_setprio(0);
+  };
+
+  // ---- softmax step of sub-tile u (log2 domain): the reference max moves
+  // only when the sub-tile's max exceeds it by more than 8; a lane's first
+  // sub-tile sets it
+  auto softmax_step = [&](int u) __attribute__((always_inline)) {
+    const int t0 = u * KS;
     // causal mask (only where the sub-tile reaches past the wave's first
     // query): register r of half kh is key t0 + 32kh + 16(r/8) + 8g + r%8
     if (t0 + KS - 1 > pos_lo) {
@@ -279,8 +339,6 @@ __global__ __launch_bounds__(P_THREADS, 1) void k_prefill_attn(
         for (int r = 0; r < 16; ++r)
           if (t0 + 32 * kh + 16 * (r >> 3) + 8 * g + (r & 7) > pos) sc[kh][r] = -INFINITY;
     }
-    // ---- online softmax (log2 domain): the reference max moves only when the
-    // sub-tile's max exceeds it by more than 8; a lane's first sub-tile sets it
     float mx = sc[0][0];
 #pragma unroll
     for (int kh = 0; kh < 2; ++kh)
@@ -302,31 +360,78 @@ __global__ __launch_bounds__(P_THREADS, 1) void k_prefill_attn(
       p_fence();
     }
     // probabilities: step ks (16 keys) = registers 8(ks % 2) .. +7 of half ks / 2
-    bf16x8_t pf[4];
-    float lsum = 0.f;
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks)
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const float pe = __builtin_amdgcn_exp2f(sc[ks >> 1][8 * (ks & 1) + e] - msub);
-        lsum += pe;
-        pf[ks][e] = (__bf16)pe;
+      for (int e = 0; e < 8; ++e) pf[ks][e] = (__bf16)__builtin_amdgcn_exp2f(sc[ks >> 1][8 * (ks & 1) + e] - msub);
+    // row sum of the probabilities as rounded for the value MFMAs
+    float lsum0 = 0.f, lsum1 = 0.f;
+    typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2_t;
+    const bf16x2_t one2 = {(__bf16)1.f, (__bf16)1.f};
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks)
+#pragma unroll
+      for (int e = 0; e < 8; e += 2) {
+        const bf16x2_t pr = {pf[ks][e], pf[ks][e + 1]};
+        if (ks & 1) lsum1 = __builtin_amdgcn_fdot2_f32_bf16(pr, one2, lsum1, false);
+        else lsum0 = __builtin_amdgcn_fdot2_f32_bf16(pr, one2, lsum0, false);
       }
+    const float lsum = lsum0 + lsum1;
     l_run = l_run * alpha + lsum;
     // wait states between the vector writes of P and the MFMAs reading it
     asm volatile("s_nop 4" : "+v"(pf[0]), "+v"(pf[1]), "+v"(pf[2]), "+v"(pf[3]));
+  };
 
-    // ---- values: 4 value tiles x 4 steps, operands read one step ahead
-    {
-      const LDS_AS char* vp = st + V_OFF + k_lane;
-      u32x4 va[2];
-      va[0] = *(const LDS_AS u32x4*)(vp);
-#pragma unroll
-      for (int k = 0; k < 16; ++k) {
-        const int dt = k >> 2, ks = k & 3;
-        if (k + 1 < 16) va[(k + 1) & 1] = *(const LDS_AS u32x4*)(vp + (k + 1) * K_BLOCK);
-        p_mfma(o[dt], p_as_bf16x8(va[k & 1]), pf[ks]);
-      }
+  // ---- two groups in alternation: waves 0-3 (group 0, one per SIMD) run
+  // the step sequence QK(0), SM(0), M(0), SM(1), M(1), ... (SM = softmax,
+  // M(u) = PV(u) + QK(u+1)); waves 4-7 run the same sequence one phase
+  // later. A barrier closes every phase, so on each SIMD one wave's MFMAs
+  // overlap the other wave's softmax.
+  // Copies: sub-tile k + 2 goes into the stage that sub-tile k - 2 left (its
+  // last reader, group 1's M(k - 2), ran in phase 2k - 1); each group issues
+  // its share piecewise inside its next MFMA step (group 0 in phase 2k, group
+  // 1 in phase 2k + 1). At the end of phase 2k + 1 the copies of sub-tile
+  // k + 1 (read from phase 2k + 2 on) are complete.
+  // closes phase ph: after an odd phase the copies of the sub-tile read from
+  // the next phase on are complete; then the barrier
+  auto phase_end = [&](int ph) __attribute__((always_inline)) {
+    if (ph & 1) {
+      const int v = (ph >> 1) + 1;
+      if (v + 1 < n_sub) p_wait_vmcnt<P_LOADS>();
+      else p_wait_vmcnt<0>();
+    }
+    p_lds_barrier();
+  };
+  using T = std::true_type;
+  using F = std::false_type;
+  if (n_sub > 1) p_wait_vmcnt<P_LOADS>();  // sub-tile 0 landed
+  else p_wait_vmcnt<0>();
+  p_lds_barrier();
+  if (w < 4) {
+    if (2 < n_sub) load_sub(2);
+    if (n_own > 0) mfma_step(F{}, T{}, -1, -1);  // QK(0)
+    phase_end(0);
+    for (int u = 0; u < n_sub; ++u) {
+      if (u < n_own) softmax_step(u);
+      phase_end(2 * u + 1);
+      const int dv = u + 3 < n_sub ? u + 3 : -1;  // copies of phase 2u + 2
+      if (u < n_own) mfma_step(T{}, T{}, u, dv);
+      else if (dv >= 0) load_sub(dv);
+      phase_end(2 * u + 2);
+    }
+    phase_end(2 * n_sub + 1);
+  } else {
+    phase_end(0);
+    if (2 < n_sub) load_sub(2);
+    if (n_own > 0) mfma_step(F{}, T{}, -1, -1);  // QK(0)
+    phase_end(1);
+    for (int u = 0; u < n_sub; ++u) {
+      if (u < n_own) softmax_step(u);
+      phase_end(2 * u + 2);
+      const int dv = u + 3 < n_sub ? u + 3 : -1;  // copies of phase 2u + 3
+      if (u < n_own) mfma_step(T{}, T{}, u, dv);
+      else if (dv >= 0) load_sub(dv);
+      phase_end(2 * u + 3);
     }
   }
 
@@ -335,7 +440,7 @@ __global__ __launch_bounds__(P_THREADS, 1) void k_prefill_attn(
   float l0, l1;
   p_halves(l_run, l0, l1);
   const float lt = l0 + l1;
-  const int s_out = s0 + QW * w + hl;
+  const int s_out = s0 + QW * qb + hl;
   if (s_out >= S) return;
   const float inv = lt > 0.f ? 1.f / lt : 0.f;
   bf16* op = out + (((size_t)b * S + s_out) * H + h) * DV + 4 * g;
