@@ -136,21 +136,41 @@ WsLayout ws_layout(int H, int batch, int splits) {
 }
 
 // ------------------------------------------------------------ k_absorb ----
+// RoPE inverse frequencies base^(-2i/d_rope), formed on the host in double
+struct RopeFreq {
+  double theta[DR / 2];
+};
+
 // grid (H, DC / 64); 4 waves. Block (h, c0) forms Qt[:, h, c0 .. c0+63] for
 // every sequence as the transposed product Qt^T[c, b] = sum_j W_UK[h*128+j, c]
 // q_nope[b, h, j]: the 128 x 64 slice of W_UK,h is staged in LDS and read
 // transposed (as the A operand); each lane then holds 4 consecutive columns of
-// one sequence and stores them with one 8-byte write. The blocks of head h
-// also write its rotated, scaled q_pe slice, each for every 8th sequence.
+// one sequence. Results go through LDS so that every row segment (64 columns,
+// 128 bytes) is written whole. The blocks of head h also write its rotated,
+// scaled q_pe slice, each for every 8th sequence; those loads are issued
+// first.
 __global__ __launch_bounds__(256) void k_absorb(int B, int H, const bf16* __restrict__ q_nope,
                                                 const bf16* __restrict__ q_pe, const bf16* __restrict__ w_uk,
-                                                const int32_t* __restrict__ ctx_lens, float qscale, float base,
+                                                const int32_t* __restrict__ ctx_lens, float qscale, RopeFreq rope,
                                                 bf16* __restrict__ qt) {
   constexpr int LD = 72;  // padded row (144 B) keeps the transposed reads conflict-free
   constexpr int BT_CHUNK = 4;  // sequence tiles whose query loads are in flight together
+  constexpr int LDO = 72;      // staged output row: 64 columns + pad
   __shared__ __attribute__((aligned(16))) bf16 wt[DN * LD];
+  __shared__ __attribute__((aligned(16))) bf16 ot[16 * BT_CHUNK * LDO];
   const int h = blockIdx.x, c0 = blockIdx.y * 64;
   const int w = threadIdx.x >> 6, lane = threadIdx.x & 63, i16 = lane & 15, G = lane >> 4;
+  // RoPE part of this thread: pair i = tid % 32 of sequences b = 8k + y with
+  // k = tid / 32, tid / 32 + 8, ... (first one's inputs requested now)
+  const int rp_i = threadIdx.x & (DR / 2 - 1);
+  const int rp_b0 = (threadIdx.x / (DR / 2)) * (DC / 64) + blockIdx.y;
+  constexpr int RP_STEP = (256 / (DR / 2)) * (DC / 64);
+  int rp_len = 0;
+  uint32_t rp_x = 0;
+  if (rp_b0 < B) {
+    rp_len = ctx_lens[rp_b0];
+    rp_x = *(const uint32_t*)(q_pe + ((size_t)rp_b0 * H + h) * DR + 2 * rp_i);
+  }
   // every independent load first: the W_UK slice and the first chunk of queries
   u32x4 wr[DN * 8 / 256];
 #pragma unroll
@@ -191,39 +211,43 @@ __global__ __launch_bounds__(256) void k_absorb(int B, int H, const bf16* __rest
 #pragma unroll
       for (int ks = 0; ks < DN / 32; ++ks) cur[t][ks] = qv[t][ks];
     if ((bt0 + BT_CHUNK) * 16 < B) load_q(bt0 + BT_CHUNK, qv);
+    if (bt0 > 0) __syncthreads();  // the previous chunk's rows are out of ot
 #pragma unroll
     for (int t = 0; t < BT_CHUNK; ++t) {
-      const int b = (bt0 + t) * 16 + i16;
       f32x4 acc = {};
 #pragma unroll
       for (int ks = 0; ks < DN / 32; ++ks)
         acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[ks], as_bf16x8(cur[t][ks]), acc, 0, 0, 0);
-      if (b < B) {
-        typedef __attribute__((ext_vector_type(4))) __bf16 bf16x4_t;
-        const bf16x4_t v = {(__bf16)(acc[0] * qscale), (__bf16)(acc[1] * qscale), (__bf16)(acc[2] * qscale),
-                            (__bf16)(acc[3] * qscale)};
-        *(bf16x4_t*)(qt + ((size_t)b * H + h) * ROW + c0 + 16 * w + 4 * G) = v;
-      }
+      typedef __attribute__((ext_vector_type(4))) __bf16 bf16x4_t;
+      const bf16x4_t v = {(__bf16)(acc[0] * qscale), (__bf16)(acc[1] * qscale), (__bf16)(acc[2] * qscale),
+                          (__bf16)(acc[3] * qscale)};
+      *(bf16x4_t*)&ot[(16 * t + i16) * LDO + 16 * w + 4 * G] = v;
+    }
+    __syncthreads();
+    // 64 rows of 128 bytes: 8 lanes per row, 16 bytes each
+#pragma unroll
+    for (int rr = 0; rr < 16 * BT_CHUNK / 32; ++rr) {
+      const int r = 32 * rr + (threadIdx.x >> 3), ch = threadIdx.x & 7;
+      const int b = bt0 * 16 + r;
+      if (b < B) *(u32x4*)(qt + ((size_t)b * H + h) * ROW + c0 + 8 * ch) = *(const u32x4*)&ot[r * LDO + 8 * ch];
     }
   }
-  {
-    // the rotated, scaled q_pe slice, spread over the DC / 64 blocks of the
-    // head: thread -> pair i = tid % 32 (fixed); block y takes sequences
-    // 8k + y, thread group tid / 32 every 64th of those
-    const int i = threadIdx.x & (DR / 2 - 1);
-    const double theta = pow((double)base, -2.0 * (double)i / (double)DR);
-    for (int b = (threadIdx.x / (DR / 2)) * (DC / 64) + blockIdx.y; b < B; b += (256 / (DR / 2)) * (DC / 64)) {
-      const double ang = (double)(ctx_lens[b] - 1) * theta;
-      // reduce to [-pi, pi] in double, then single-precision sin/cos
-      const float r = (float)(ang - 6.283185307179586 * rint(ang * 0.15915494309189535));
-      float sn, cs;
-      sincosf(r, &sn, &cs);
-      const bf16* src = q_pe + ((size_t)b * H + h) * DR + 2 * i;
-      const float x0 = bf2f(src[0]), x1 = bf2f(src[1]);
-      typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2_t;
-      const bf16x2_t v = {(__bf16)((x0 * cs - x1 * sn) * qscale), (__bf16)((x0 * sn + x1 * cs) * qscale)};
-      *(bf16x2_t*)(qt + ((size_t)b * H + h) * ROW + DC + 2 * i) = v;
+  // the rotated, scaled q_pe slice: reduce the angle to [-pi, pi] in double,
+  // then single-precision sin/cos
+  const double theta = rope.theta[rp_i];
+  for (int b = rp_b0; b < B; b += RP_STEP) {
+    if (b != rp_b0) {
+      rp_len = ctx_lens[b];
+      rp_x = *(const uint32_t*)(q_pe + ((size_t)b * H + h) * DR + 2 * rp_i);
     }
+    const double ang = (double)(rp_len - 1) * theta;
+    const float r = (float)(ang - 6.283185307179586 * rint(ang * 0.15915494309189535));
+    float sn, cs;
+    sincosf(r, &sn, &cs);
+    const float x0 = __uint_as_float(rp_x << 16), x1 = __uint_as_float(rp_x & 0xFFFF0000u);
+    typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2_t;
+    const bf16x2_t v = {(__bf16)((x0 * cs - x1 * sn) * qscale), (__bf16)((x0 * sn + x1 * cs) * qscale)};
+    *(bf16x2_t*)(qt + ((size_t)b * H + h) * ROW + DC + 2 * rp_i) = v;
   }
 }
 
@@ -760,8 +784,10 @@ hipError_t decode_fast(const mla_dims& d, float scale, int batch, int max_contex
 
   {
     ProfScope ps("mla_decode_absorb", s);
+    RopeFreq rope;
+    for (int i = 0; i < DR / 2; ++i) rope.theta[i] = pow((double)d.rope_base, -2.0 * i / (double)DR);
     hipLaunchKernelGGL(k_absorb, dim3(H, DC / 64), dim3(256), 0, s, batch, H, (const bf16*)q_nope,
-                       (const bf16*)q_pe, (const bf16*)w_uk, c.context_lens, scale * LOG2E, d.rope_base, qt);
+                       (const bf16*)q_pe, (const bf16*)w_uk, c.context_lens, scale * LOG2E, rope, qt);
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;

@@ -5,23 +5,22 @@
 // ("DeepSeek-V2 paper digest" §2.1). For prefill this costs 192 + 128 MACs per
 // (query, key, head) instead of 576 + 512 in the absorbed form of decode.
 //
-// Block = (sequence b, head h, 256 queries): eight waves, two per SIMD, wave w
-// owning queries 32w .. 32w+31, so one wave's softmax runs while the other's
-// MFMAs do. Keys stream in sub-tiles of 64 through a ring of four 40 KB LDS
-// stages (direct 16-byte HBM -> LDS copies, three sub-tiles in flight). Per
-// sub-tile and wave:
+// Block = (sequence b, head h, 256 queries): eight waves, two per SIMD, each
+// owning 32 queries. Keys stream in sub-tiles of 64 through a ring of four
+// 40 KB LDS stages (direct 16-byte HBM -> LDS copies). Per sub-tile and wave:
 //   S^T[t, s] = K[t] . Q[s]           2 key halves x 12 steps of K = 16
 //   online softmax per query (lane column), causal mask on the diagonal
 //   O^T[d, s] += V^T[d, t] P[t, s]    4 value tiles x 4 steps of 16 keys
-// A stage holds the sub-tile in the order the operand reads consume it:
-// 24 score blocks of 1 KB (half kh, step st: lane l's 16 bytes = key
-// 32kh + swap23(l % 32), dims 16st + 8(l / 32) .. +7) and 16 value blocks of
-// 1 KB (value tile dt, step ks: lane l's 16 bytes = V^T row 32dt + l % 32, keys
-// 16ks + 8(l / 32) .. +7, read from the transposed values the GEMM wrote).
-// swap23 exchanges bits 2 and 3 of the key index, so that the score MFMA's
-// output rows (8(r/4) + 4(l/32) + r%4) come out as keys 16(r/8) + 8(l/32) +
-// r%8: each lane's probabilities are then exactly the 8 consecutive keys its
-// value-step B operand needs, with no exchange between lanes.
+// The waves form two groups (one wave of each per SIMD) that alternate, with
+// a barrier per phase: while one group runs the MFMAs of a sub-tile (values of
+// sub-tile u, then scores of u + 1), the other runs a softmax, so each SIMD's
+// matrix core and vector ALU work at the same time.
+// The score operand of half kh, step st is key 32kh + swap23(l % 32), dims
+// 16st + 8(l / 32) .. +7 for lane l; swap23 exchanges bits 2 and 3 of the key
+// index, so that the score MFMA's output rows (8(r/4) + 4(l/32) + r%4) come out
+// as keys 16(r/8) + 8(l/32) + r%8: each lane's probabilities are then exactly
+// the 8 consecutive keys its value-step B operand needs, with no exchange
+// between lanes. Values come from the transposed copy the GEMM wrote.
 // Query s of sequence b sits at position L_b - S + s and sees keys 0 .. that.
 #include <math.h>
 
