@@ -27,15 +27,24 @@
 namespace mla {
 namespace {
 
-constexpr int BM = 256, BN = 128, BK = 64;
+constexpr int BM = 256, BK = 64;
 constexpr int G_THREADS = 256;
 constexpr int A_STAGE = BM * BK * 2;  // 32 KB
-constexpr int B_STAGE = BN * BK * 2;  // 16 KB
-constexpr int STAGE = A_STAGE + B_STAGE;
-constexpr int N_STAGES = 3;
 constexpr int HEAD_W = 128;  // head width of the per-head epilogues
 constexpr int A_LOADS = BM * BK * 2 / 16 / G_THREADS;  // 8 per lane
-constexpr int B_LOADS = BN * BK * 2 / 16 / G_THREADS;  // 4 per lane
+
+// Block tile 256 x BN with BN = 64 NI: each wave owns 128 A-rows x 32 NI
+// B-rows (4 x NI MFMA tiles of 32 x 32). NI = 2: 256 x 128, three 48 KB
+// stages; NI = 4: 256 x 256, two 64 KB stages (half the copies per MFMA).
+template <int NI>
+struct Tile {
+  static constexpr int BN = 64 * NI;
+  static constexpr int B_STAGE = BN * BK * 2;
+  static constexpr int STAGE = A_STAGE + B_STAGE;
+  static constexpr int N_STAGES = NI == 2 ? 3 : 2;
+  static constexpr int B_LOADS = B_STAGE / 16 / G_THREADS;  // 4 or 8 per lane
+  static constexpr int LOADS = A_LOADS + B_LOADS;
+};
 
 template <int N>
 __device__ __forceinline__ void g_wait_vmcnt() {
@@ -71,15 +80,18 @@ __device__ __forceinline__ const bf16* b_row_ptr(const GemmArgs& g, int n) {
   return n < g.n_split ? g.b0 + (size_t)n * g.ldb : g.b1 + (size_t)(n - g.n_split) * g.ldb;
 }
 
-template <int EPI>
+template <int EPI, int NI>
 __global__ __launch_bounds__(G_THREADS, 1) void k_gemm(GemmArgs g) {
+  using TL = Tile<NI>;
+  constexpr int BN = TL::BN, STAGE = TL::STAGE, N_STAGES = TL::N_STAGES, B_LOADS = TL::B_LOADS;
+  constexpr int LOADS = TL::LOADS;
   __shared__ __attribute__((aligned(1024))) char lds[N_STAGES * STAGE];
   const int n_tiles = (g.N + BN - 1) / BN;
   const int bid = blockIdx.x;
   const int mt = bid / n_tiles, nt = bid % n_tiles;
   const int m0 = mt * BM, n0 = nt * BN;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
-  const int wm = w & 1, wn = w >> 1;  // wave covers A rows m0 + 128wm .., B rows n0 + 64wn ..
+  const int wm = w & 1, wn = w >> 1;  // wave covers A rows m0 + 128wm .., B rows n0 + 32 NI wn ..
   const int k_steps = g.K / BK;
 
   // per-lane source rows and LDS positions of the copies (fixed over K)
@@ -97,28 +109,27 @@ __global__ __launch_bounds__(G_THREADS, 1) void k_gemm(GemmArgs g) {
     b_src[k] = b_row_ptr(g, n0 + r) + 8 * (cp ^ g_swz(r));
   }
   const uint32_t lds_base = (uint32_t)(size_t)(LDS_AS char*)lds;
-  auto load_stage = [&](int ks) {
+  // copy q (of LOADS) of this wave for K step ks (A copies first)
+  auto load_one = [&](int ks, int q) __attribute__((always_inline)) {
     const uint32_t st = lds_base + (ks % N_STAGES) * STAGE;
     const int kofs = ks * BK;
-#pragma unroll
-    for (int k = 0; k < A_LOADS; ++k)
-      g_dma16(a_src[k] + kofs, __builtin_amdgcn_readfirstlane(st + (w * A_LOADS + k) * 1024));
-#pragma unroll
-    for (int k = 0; k < B_LOADS; ++k)
-      g_dma16(b_src[k] + kofs, __builtin_amdgcn_readfirstlane(st + A_STAGE + (w * B_LOADS + k) * 1024));
+    if (q < A_LOADS)
+      g_dma16(a_src[q] + kofs, __builtin_amdgcn_readfirstlane(st + (w * A_LOADS + q) * 1024));
+    else
+      g_dma16(b_src[q - A_LOADS] + kofs,
+              __builtin_amdgcn_readfirstlane(st + A_STAGE + (w * B_LOADS + q - A_LOADS) * 1024));
   };
-  constexpr int LOADS = A_LOADS + B_LOADS;
-
-  load_stage(0);
-  if (k_steps > 1) load_stage(1);
+  for (int v = 0; v < N_STAGES - 1 && v < k_steps; ++v)
+#pragma unroll
+    for (int q = 0; q < LOADS; ++q) load_one(v, q);
 
   // operand read offsets inside a stage: MFMA A side = B rows (n), B side = A rows (m)
   //   step s (16 of K) reads chunk 2s + g of its row
   const int hl = lane & 31, gq = lane >> 5;
-  int an_off[2][4], bm_off[4][4];  // [tile][k-step within BK]
+  int an_off[NI][4], bm_off[4][4];  // [tile][k-step within BK]
 #pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    const int r = 64 * wn + 32 * i + hl;
+  for (int i = 0; i < NI; ++i) {
+    const int r = 32 * NI * wn + 32 * i + hl;
 #pragma unroll
     for (int s = 0; s < 4; ++s) an_off[i][s] = A_STAGE + r * 128 + (((2 * s + gq) ^ g_swz(r)) << 4);
   }
@@ -129,31 +140,43 @@ __global__ __launch_bounds__(G_THREADS, 1) void k_gemm(GemmArgs g) {
     for (int s = 0; s < 4; ++s) bm_off[j][s] = r * 128 + (((2 * s + gq) ^ g_swz(r)) << 4);
   }
 
-  f32x16 acc[2][4];  // [n tile][m tile]
+  f32x16 acc[NI][4];  // [n tile][m tile]
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+  for (int i = 0; i < NI; ++i)
 #pragma unroll
     for (int j = 0; j < 4; ++j) acc[i][j] = (f32x16){};
 
+  // Per K step: wait for its stage and publish it with a barrier (which also
+  // frees the stage read in the previous step), then issue the copies of step
+  // ks + N_STAGES - 1 a quarter at a time before each 16-wide sub-step, so the
+  // texture unit drains them behind the MFMAs. Operand fragments are read one
+  // sub-step ahead into a second register set.
+  bf16x8_t fa[2][NI], fb[2][4];
   for (int ks = 0; ks < k_steps; ++ks) {
-    if (ks + 1 < k_steps) g_wait_vmcnt<LOADS>();
+    if (N_STAGES == 3 && ks + 1 < k_steps) g_wait_vmcnt<(N_STAGES == 3 ? LOADS : 0)>();
     else g_wait_vmcnt<0>();
     g_lds_barrier();
-    if (ks + 2 < k_steps) load_stage(ks + 2);
+    const int next = ks + N_STAGES - 1;
     const LDS_AS char* st = (const LDS_AS char*)(lds + (ks % N_STAGES) * STAGE);
+    auto read_frags = [&](int sub, int set) __attribute__((always_inline)) {
+#pragma unroll
+      for (int i = 0; i < NI; ++i) fa[set][i] = g_as_bf16x8(*(const LDS_AS u32x4*)(st + an_off[i][sub]));
+#pragma unroll
+      for (int j = 0; j < 4; ++j) fb[set][j] = g_as_bf16x8(*(const LDS_AS u32x4*)(st + bm_off[j][sub]));
+    };
+    read_frags(0, 0);
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
-      bf16x8_t fa[2], fb[4];
+      if (s < 3) read_frags(s + 1, (s + 1) & 1);
+      if (next < k_steps)
 #pragma unroll
-      for (int i = 0; i < 2; ++i) fa[i] = g_as_bf16x8(*(const LDS_AS u32x4*)(st + an_off[i][s]));
+        for (int q = s * LOADS / 4; q < (s + 1) * LOADS / 4; ++q) load_one(next, q);
 #pragma unroll
-      for (int j = 0; j < 4; ++j) fb[j] = g_as_bf16x8(*(const LDS_AS u32x4*)(st + bm_off[j][s]));
-#pragma unroll
-      for (int i = 0; i < 2; ++i)
+      for (int i = 0; i < NI; ++i)
 #pragma unroll
         for (int j = 0; j < 4; ++j)
-          acc[i][j] = EPI == 2 ? __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[j], fa[i], acc[i][j], 0, 0, 0)
-                               : __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[i], fb[j], acc[i][j], 0, 0, 0);
+          acc[i][j] = EPI == 2 ? __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[s & 1][j], fa[s & 1][i], acc[i][j], 0, 0, 0)
+                               : __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[s & 1][i], fb[s & 1][j], acc[i][j], 0, 0, 0);
     }
   }
 
@@ -166,11 +189,11 @@ __global__ __launch_bounds__(G_THREADS, 1) void k_gemm(GemmArgs g) {
   }
   const int n_heads = g.N / HEAD_W;
   if constexpr (EPI == 2) {
-    // lane holds C[m .. m+3][n] for n = n0 + 64wn + 32i + hl,
+    // lane holds C[m .. m+3][n] for n = n0 + 32 NI wn + 32i + hl,
     // m = m0 + 128wm + 32j + 8q + 4gq (q = r / 4)
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const int n = n0 + 64 * wn + 32 * i + hl;
+    for (int i = 0; i < NI; ++i) {
+      const int n = n0 + 32 * NI * wn + 32 * i + hl;
       if (n >= g.N) continue;
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
@@ -192,7 +215,7 @@ __global__ __launch_bounds__(G_THREADS, 1) void k_gemm(GemmArgs g) {
     return;
   }
   // epilogue: lane holds C[m][n .. n+3] for m = m0 + 128wm + 32j + hl,
-  // n = n0 + 64wn + 32i + 8q + 4gq (q = r / 4)
+  // n = n0 + 32 NI wn + 32i + 8q + 4gq (q = r / 4)
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
     const int m = m0 + 128 * wm + 32 * j + hl;
@@ -205,10 +228,10 @@ __global__ __launch_bounds__(G_THREADS, 1) void k_gemm(GemmArgs g) {
     }
     const int seq_b = seq_of[j >> 1], seq_t = m - seq_b * g.a_seq;
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
+    for (int i = 0; i < NI; ++i)
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
-        const int n = n0 + 64 * wn + 32 * i + 8 * q + 4 * gq;
+        const int n = n0 + 32 * NI * wn + 32 * i + 8 * q + 4 * gq;
         if (n >= g.N) continue;
         float v[4] = {acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]};
         typedef __attribute__((ext_vector_type(4))) __bf16 bf16x4_t;
@@ -246,15 +269,22 @@ bool gemm_fast_supported(int M, int N, int K) { return M > 0 && N > 0 && N % 4 =
 
 hipError_t gemm_fast(const GemmArgs& g, int epi, hipStream_t s) {
   if (epi >= 2 && (g.N % HEAD_W != 0 || g.a_seq % 64 != 0 || g.a_seq < 64)) return hipErrorInvalidValue;
-  const int grid = ((g.M + BM - 1) / BM) * ((g.N + BN - 1) / BN);
-  if (epi == 1)
-    hipLaunchKernelGGL(k_gemm<1>, dim3(grid), dim3(G_THREADS), 0, s, g);
-  else if (epi == 2)
-    hipLaunchKernelGGL(k_gemm<2>, dim3(grid), dim3(G_THREADS), 0, s, g);
-  else if (epi == 3)
-    hipLaunchKernelGGL(k_gemm<3>, dim3(grid), dim3(G_THREADS), 0, s, g);
-  else
-    hipLaunchKernelGGL(k_gemm<0>, dim3(grid), dim3(G_THREADS), 0, s, g);
+  const int m_tiles = (g.M + BM - 1) / BM;
+  // 256-wide tiles where there are enough of them to fill the chip several
+  // times over (and no partial tile); 128-wide otherwise
+  const bool wide = epi != 1 && g.N % 256 == 0 && m_tiles * (g.N / 256) >= 1024;
+  const int grid = m_tiles * (wide ? g.N / 256 : (g.N + 127) / 128);
+  auto go = [&](auto kern) { hipLaunchKernelGGL(kern, dim3(grid), dim3(G_THREADS), 0, s, g); };
+  if (wide) {
+    if (epi == 2) go(k_gemm<2, 4>);
+    else if (epi == 3) go(k_gemm<3, 4>);
+    else go(k_gemm<0, 4>);
+  } else {
+    if (epi == 1) go(k_gemm<1, 2>);
+    else if (epi == 2) go(k_gemm<2, 2>);
+    else if (epi == 3) go(k_gemm<3, 2>);
+    else go(k_gemm<0, 2>);
+  }
   return hipGetLastError();
 }
 
