@@ -444,7 +444,11 @@ __global__ __launch_bounds__(SPLIT_THREADS, 1) void k_split(int H, int B, int sp
     } else if (k == 1) {
 #pragma unroll
       for (int r = 8; r < 16; ++r) sm_mx = fmaxf(sm_mx, sc[r]);
-      sm_mx = fmaxf(sm_mx, __shfl_xor(sm_mx, 32, 64));
+      {
+        // the other half of the head's rows sits 32 lanes away
+        const auto pr = __builtin_amdgcn_permlane32_swap(__float_as_uint(sm_mx), __float_as_uint(sm_mx), false, false);
+        sm_mx = fmaxf(__uint_as_float(pr[0]), __uint_as_float(pr[1]));
+      }
       // first tile: the reference is the exact max (its p is exactly 1);
       // later moves are by whole steps k >= 9
       const bool first = m_run == -INFINITY;
@@ -494,8 +498,18 @@ __global__ __launch_bounds__(SPLIT_THREADS, 1) void k_split(int H, int B, int sp
   // The score MFMAs are interleaved with PV groups 0-3 (9 score steps per
   // group), so the score operands' LDS reads are spread over 52 MFMAs; the
   // softmax of tile i then runs between PV groups 4-7. Issue order is pinned
-  // with scheduling barriers, LDS reads a few MFMAs ahead of their use.
-  auto step = [&](auto do_qk, auto do_pv, int i) {
+  // with scheduling barriers, LDS reads a few MFMAs ahead of their use. The
+  // nine copies of tile dma_i (= i + 2) go out one every fourth score step, so
+  // the texture unit takes them as it frees up instead of in a burst.
+  auto step = [&](auto do_qk, auto do_pv, int i, int dma_i) {
+    // source and destination of this wave's copies of tile dma_i (uniform)
+    const char* dma_src = nullptr;
+    uint32_t dma_dst = 0;
+    if (dma_i >= 0) {
+      const int page = __builtin_amdgcn_readlane(page_of_lane, dma_i >> 1);
+      dma_src = (const char*)(rows + ((size_t)page * PAGE + (dma_i & 1) * TILE) * ROW);
+      dma_dst = __builtin_amdgcn_readfirstlane(lds_base + (dma_i % N_SLOTS) * TILE_BYTES + w * TILE_LOADS * 64 * 16);
+    }
     constexpr bool QK = decltype(do_qk)::value, PV = decltype(do_pv)::value;
     const LDS_AS char* tq = slot(i);
     const LDS_AS char* tv = slot(i - 1);
@@ -530,10 +544,12 @@ __global__ __launch_bounds__(SPLIT_THREADS, 1) void k_split(int H, int B, int sp
     }
     if constexpr (PV) va[0] = va_read(0);
     __builtin_amdgcn_sched_barrier(0);
-    if constexpr (PV) {
-      // sign bits set: the owner moved its reference; decode k from the raw
-      // fragment, then clear the bits (always: a branch that rewrites the
-      // fragments costs more registers than the 16 ANDs)
+    // sign bits set: the owner moved its reference; decode k from the raw
+    // fragment, then clear the bits (always: a branch that rewrites the
+    // fragments costs more registers than the 16 ANDs). With scores in the
+    // step it runs after the first score MFMAs, while their results are
+    // pending, instead of holding them back until the fragments arrive.
+    auto p_flags = [&]() __attribute__((always_inline)) {
       u32x4 raw[4];
       uint32_t flag = 0;
 #pragma unroll
@@ -559,7 +575,8 @@ __global__ __launch_bounds__(SPLIT_THREADS, 1) void k_split(int H, int B, int sp
         }
         rescale_fence();
       }
-    }
+    };
+    if constexpr (PV && !QK) p_flags();
     f32x16 sc;
     if constexpr (QK) {
       __builtin_amdgcn_sched_barrier(0);
@@ -571,7 +588,17 @@ __global__ __launch_bounds__(SPLIT_THREADS, 1) void k_split(int H, int B, int sp
         if (s + QK_AHEAD < QK_STEPS)
           fa[s % QK_AHEAD] = *(const LDS_AS u32x4*)(tq + qk_off[(s + QK_AHEAD) & 3] + ((s + QK_AHEAD) >> 2) * 128);
         __builtin_amdgcn_sched_barrier(0);
+        if (s % 4 == 1 && dma_i >= 0) {
+          const int k = s / 4;
+          const uint32_t off = (k & 1) ? (ld_off[k / 2] >> 16) : (ld_off[k / 2] & 0xFFFFu);
+          dma16s(dma_src, off, dma_dst + k * 64 * 16);
+          __builtin_amdgcn_sched_barrier(0);
+        }
         if constexpr (PV) {
+          if (s == 3) {
+            p_flags();
+            __builtin_amdgcn_sched_barrier(0);
+          }
           if (s % 9 == 8) {
             pv_group(s / 9);
             __builtin_amdgcn_sched_barrier(0);
@@ -610,17 +637,16 @@ __global__ __launch_bounds__(SPLIT_THREADS, 1) void k_split(int H, int B, int sp
   wait_vmcnt<TILE_LOADS>();
   if (n_tiles == 1) wait_vmcnt<0>();
   lds_barrier();
-  if (n_tiles > 2) load_tile(2);
-  step(T{}, F{}, 0);
+  // the copies of tile i + 2 go out during step i (spread over its score MFMAs)
+  step(T{}, F{}, 0, n_tiles > 2 ? 2 : -1);
   for (int i = 1; i < n_tiles; ++i) {
     if (i + 1 < n_tiles) wait_vmcnt<TILE_LOADS>();  // tile i landed, tile i+1 may fly
     else wait_vmcnt<0>();
     lds_barrier();  // tile i and P of tile i-1 visible; slot (i+2)%4 and P buffer i%2 free
-    if (i + 2 < n_tiles) load_tile(i + 2);
-    step(T{}, T{}, i);
+    step(T{}, T{}, i, i + 2 < n_tiles ? i + 2 : -1);
   }
   lds_barrier();
-  step(F{}, T{}, n_tiles);
+  step(F{}, T{}, n_tiles, -1);
 
   // ---- partials: (m, l) by the head owner, O slices by the column owner ----
   l_run += __shfl_xor(l_run, 32, 64);
