@@ -695,29 +695,36 @@ __global__ __launch_bounds__(256) void k_combine_uv(int H, int B, int splits, in
   const int b0 = bt * 16;
   const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
   const int i16 = lane & 15, G = lane >> 4;
-  // W_UV,h fragments of this wave (rows 32w .. 32w+31, all 512 columns) are
-  // independent of everything else: request them first
+  // 1. lane group rr = lane / 16 of wave w owns sequence r = 4w + rr; lane q of
+  // the group takes splits q, q + 16, ...; 16-lane reductions. The context
+  // length and the (m, l) of split q are requested first (they gate the
+  // weights), then the W_UV,h fragments of this wave (rows 32w .. 32w+31, all
+  // 512 columns), which are needed only at the end.
+  const int rr = lane >> 4, q = lane & 15, r = 4 * w + rr, b = b0 + r;
+  const float* ml = part_ml + ((size_t)h * B + (b < B ? b : 0)) * splits * 2;
+  const int len = b < B ? ctx_lens[b] : 0;
+  typedef __attribute__((ext_vector_type(2))) float f32x2_t;
+  f32x2_t ml_q = {-INFINITY, 0.f};
+  if (q < splits && b < B) ml_q = *(const f32x2_t*)(ml + 2 * q);  // used only if q < ns
   const bf16* wv = w_uv + (size_t)h * DV * DC;
   u32x4 wf[DC / 32][2];
 #pragma unroll
   for (int ks = 0; ks < DC / 32; ++ks)
 #pragma unroll
     for (int mt = 0; mt < 2; ++mt) wf[ks][mt] = *(const u32x4*)(wv + (size_t)(32 * w + 16 * mt + i16) * DC + 32 * ks + 8 * G);
-  // 1. lane group rr = lane / 16 of wave w owns sequence r = 4w + rr; lane q of
-  // the group takes splits q, q + 16, ...; 16-lane reductions
   {
-    const int rr = lane >> 4, q = lane & 15, r = 4 * w + rr, b = b0 + r;
-    const int ns = b < B ? ((ctx_lens[b] + PAGE - 1) / PAGE + pps - 1) / pps : 0;
-    const float* ml = part_ml + ((size_t)h * B + (b < B ? b : 0)) * splits * 2;
-    float M = -INFINITY;
-    for (int sp = q; sp < ns; sp += 16) M = fmaxf(M, ml[2 * sp]);
+    const int ns = b < B ? ((len + PAGE - 1) / PAGE + pps - 1) / pps : 0;
+    float M = q < ns ? ml_q[0] : -INFINITY;
+    for (int sp = q + 16; sp < ns; sp += 16) M = fmaxf(M, ml[2 * sp]);
 #pragma unroll
     for (int o = 8; o > 0; o >>= 1) M = fmaxf(M, __shfl_xor(M, o, 64));
     float l = 0.f;
     for (int sp = q; sp < splits; sp += 16) {
-      const float e = sp < ns ? __builtin_amdgcn_exp2f(ml[2 * sp] - M) : 0.f;
+      const float m_sp = sp == q ? ml_q[0] : ml[2 * sp];
+      const float l_sp = sp == q ? ml_q[1] : ml[2 * sp + 1];
+      const float e = sp < ns ? __builtin_amdgcn_exp2f(m_sp - M) : 0.f;
       wgt[r][sp] = e;
-      if (sp < ns) l += e * ml[2 * sp + 1];
+      if (sp < ns) l += e * l_sp;
     }
 #pragma unroll
     for (int o = 8; o > 0; o >>= 1) l += __shfl_xor(l, o, 64);
@@ -767,13 +774,13 @@ __global__ __launch_bounds__(256) void k_combine_uv(int H, int B, int splits, in
     for (int mt = 0; mt < 2; ++mt)
       acc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(wf[ks][mt]), bo, acc[mt], 0, 0, 0);
   }
-  const int b = b0 + i16;
-  if (b < B) {
+  const int bo_seq = b0 + i16;
+  if (bo_seq < B) {
 #pragma unroll
     for (int mt = 0; mt < 2; ++mt) {
       typedef __attribute__((ext_vector_type(4))) __bf16 bf16x4_t;
       const bf16x4_t v = {(__bf16)acc[mt][0], (__bf16)acc[mt][1], (__bf16)acc[mt][2], (__bf16)acc[mt][3]};
-      *(bf16x4_t*)(out + ((size_t)b * H + h) * DV + 32 * w + 16 * mt + 4 * G) = v;
+      *(bf16x4_t*)(out + ((size_t)bo_seq * H + h) * DV + 32 * w + 16 * mt + 4 * G) = v;
     }
   }
 }
