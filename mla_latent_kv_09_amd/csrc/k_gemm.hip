@@ -85,7 +85,11 @@ __global__ __launch_bounds__(G_THREADS, 1) void k_gemm(GemmArgs g) {
   using TL = Tile<NI>;
   constexpr int BN = TL::BN, STAGE = TL::STAGE, N_STAGES = TL::N_STAGES, B_LOADS = TL::B_LOADS;
   constexpr int LOADS = TL::LOADS;
-  __shared__ __attribute__((aligned(1024))) char lds[N_STAGES * STAGE];
+  // the K-step stages, reused at the end to stage the output tile (rows of
+  // 256 columns plus 16 bytes of padding)
+  constexpr int CT_PITCH = 256 + 8;  // bf16 elements per staged row
+  constexpr int LDS_BYTES = N_STAGES * STAGE > 256 * CT_PITCH * 2 ? N_STAGES * STAGE : 256 * CT_PITCH * 2;
+  __shared__ __attribute__((aligned(1024))) char lds[LDS_BYTES];
   const int n_tiles = (g.N + BN - 1) / BN;
   const int bid = blockIdx.x;
   const int mt = bid / n_tiles, nt = bid % n_tiles;
@@ -180,6 +184,63 @@ __global__ __launch_bounds__(G_THREADS, 1) void k_gemm(GemmArgs g) {
     }
   }
 
+  // Plain, head-major and blocked-transposed stores go through LDS: the tile
+  // is staged (as C for EPI 0/3, as C^T for EPI 2) and then written as whole
+  // 16-byte pieces of consecutive output bytes, instead of each store
+  // instruction touching 32 rows.
+  if constexpr (EPI != 1) {
+    const bool aligned16 = g.N % 8 == 0 && g.c_split % 8 == 0 && g.ldc0 % 8 == 0 && g.ldc1 % 8 == 0 &&
+                           ((size_t)g.c0 & 15) == 0 && ((size_t)g.c1 & 15) == 0;
+    if (EPI >= 2 || aligned16) {
+      g_lds_barrier();  // every wave is done with the stages
+      LDS_AS bf16* ct = (LDS_AS bf16*)lds;
+      typedef __attribute__((ext_vector_type(4))) __bf16 bf16x4_t;
+      typedef __attribute__((ext_vector_type(2))) uint32_t u32x2_t;
+#pragma unroll
+      for (int i = 0; i < NI; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const bf16x4_t o = {(__bf16)acc[i][j][4 * q], (__bf16)acc[i][j][4 * q + 1], (__bf16)acc[i][j][4 * q + 2],
+                                (__bf16)acc[i][j][4 * q + 3]};
+            // EPI 2 holds C^T[n][m .. m+3]: staged as rows n; others C[m][n .. n+3]: rows m
+            const int row = EPI == 2 ? 32 * NI * wn + 32 * i + hl : 128 * wm + 32 * j + hl;
+            const int col = EPI == 2 ? 128 * wm + 32 * j + 8 * q + 4 * gq : 32 * NI * wn + 32 * i + 8 * q + 4 * gq;
+            *(LDS_AS u32x2_t*)(ct + row * CT_PITCH + col) = __builtin_bit_cast(u32x2_t, o);
+          }
+      g_lds_barrier();
+      const int n_heads = g.N / HEAD_W;
+      if constexpr (EPI == 2) {
+        // rows n (BN of them) x 256 columns m, in 16-byte pieces of 8 m
+        for (int idx = threadIdx.x; idx < BN * (BM / 8); idx += G_THREADS) {
+          const int r = idx / (BM / 8), ch = idx % (BM / 8);
+          const int n = n0 + r, m = m0 + 8 * ch;
+          if (n >= g.N || m >= g.M) continue;
+          const int b = m / g.a_seq, t = m - b * g.a_seq;
+          bf16* dst = g.c0 + ((((size_t)b * n_heads + n / HEAD_W) * (g.a_seq / 64) + t / 64) * HEAD_W + n % HEAD_W) * 64 +
+                      t % 64;
+          *(u32x4*)dst = *(const LDS_AS u32x4*)(ct + r * CT_PITCH + 8 * ch);
+        }
+      } else {
+        // rows m (256 of them) x BN columns n, in 16-byte pieces of 8 n
+        for (int idx = threadIdx.x; idx < BM * (BN / 8); idx += G_THREADS) {
+          const int r = idx / (BN / 8), ch = idx % (BN / 8);
+          const int m = m0 + r, n = n0 + 8 * ch;
+          if (m >= g.M || n >= g.N) continue;
+          const u32x4 v = *(const LDS_AS u32x4*)(ct + r * CT_PITCH + 8 * ch);
+          if constexpr (EPI == 3) {
+            const int b = m / g.a_seq, t = m - b * g.a_seq;
+            *(u32x4*)(g.c0 + (((size_t)b * n_heads + n / HEAD_W) * g.a_seq + t) * HEAD_W + n % HEAD_W) = v;
+          } else {
+            if (n < g.c_split) *(u32x4*)(g.c0 + (size_t)m * g.ldc0 + n) = v;
+            else *(u32x4*)(g.c1 + (size_t)m * g.ldc1 + (n - g.c_split)) = v;
+          }
+        }
+      }
+      return;
+    }
+  }
   // rows m = (sequence, token): a_seq is a multiple of 64 for the per-head
   // epilogues, so each aligned group of 64 rows belongs to one sequence
   int seq_of[2] = {0, 0};
