@@ -655,18 +655,28 @@ __global__ __launch_bounds__(SPLIT_THREADS, 1) void k_split(int H, int B, int sp
     part_ml[prow * 2] = m_run;
     part_ml[prow * 2 + 1] = l_run;
   }
+  // O rows go out through LDS, 32 heads at a time: each store instruction
+  // then writes 1 KB of one head's row rather than 32-byte pieces of 32 rows.
+  constexpr int OP = DC + 4;  // staged row pitch in floats (2064 bytes)
+  LDS_AS float* ost = (LDS_AS float*)lds;
 #pragma unroll
   for (int ht = 0; ht < 4; ++ht) {
-    const int hh = 32 * ht + hl;
-    if (hh >= H) continue;
-    float* po = part_o + (((size_t)hh * B + b) * splits + split) * DC + 128 * w;
+    lds_barrier();  // the previous rows (or the last step's operands) are read
 #pragma unroll
     for (int ct = 0; ct < 4; ++ct)
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
         const f32x4 v = {o[ct][ht][4 * q], o[ct][ht][4 * q + 1], o[ct][ht][4 * q + 2], o[ct][ht][4 * q + 3]};
-        *(f32x4*)(po + 32 * ct + 8 * q + 4 * g) = v;
+        *(LDS_AS f32x4*)(ost + hl * OP + 128 * w + 32 * ct + 8 * q + 4 * g) = v;
       }
+    lds_barrier();
+#pragma unroll
+    for (int k = 0; k < 16; ++k) {
+      const int row = 2 * k + (threadIdx.x >> 7), c4 = threadIdx.x & 127, hh = 32 * ht + row;
+      if (hh < H)
+        *(f32x4*)(part_o + (((size_t)hh * B + b) * splits + split) * DC + 4 * c4) =
+            *(const LDS_AS f32x4*)(ost + row * OP + 4 * c4);
+    }
   }
 }
 
