@@ -434,15 +434,17 @@ __global__ __launch_bounds__(P_THREADS, 1) void k_prefill_attn(
     }
   }
 
-  // ---- normalise and store: lane holds d = 32dt + 8r' + 4g .. +3 of its query
+  // ---- normalise and store: lane holds d = 32dt + 8r' + 4g .. +3 of its
+  // query. The block's 256 output rows (256 bytes each) go through LDS so that
+  // each store instruction writes four whole rows.
   p_fence();
   float l0, l1;
   p_halves(l_run, l0, l1);
   const float lt = l0 + l1;
-  const int s_out = s0 + QW * qb + hl;
-  if (s_out >= S) return;
   const float inv = lt > 0.f ? 1.f / lt : 0.f;
-  bf16* op = out + (((size_t)b * S + s_out) * H + h) * DV + 4 * g;
+  constexpr int OP = DV + 8;  // staged row pitch in bf16 (272 bytes)
+  LDS_AS bf16* ost = (LDS_AS bf16*)lds;
+  typedef __attribute__((ext_vector_type(2))) uint32_t u32x2_t;
 #pragma unroll
   for (int dt = 0; dt < DV / 32; ++dt)
 #pragma unroll
@@ -450,8 +452,16 @@ __global__ __launch_bounds__(P_THREADS, 1) void k_prefill_attn(
       typedef __attribute__((ext_vector_type(4))) __bf16 bf16x4_t;
       const bf16x4_t v = {(__bf16)(o[dt][4 * r4] * inv), (__bf16)(o[dt][4 * r4 + 1] * inv),
                           (__bf16)(o[dt][4 * r4 + 2] * inv), (__bf16)(o[dt][4 * r4 + 3] * inv)};
-      *(bf16x4_t*)(op + 32 * dt + 8 * r4) = v;
+      *(LDS_AS u32x2_t*)(ost + (QW * qb + hl) * OP + 32 * dt + 8 * r4 + 4 * g) = __builtin_bit_cast(u32x2_t, v);
     }
+  p_lds_barrier();
+#pragma unroll
+  for (int k = 0; k < QT * (DV / 8) / P_THREADS; ++k) {
+    const int idx = threadIdx.x + P_THREADS * k, row = idx / (DV / 8), ch = idx % (DV / 8);
+    const int s_out = s0 + row;
+    if (s_out < S)
+      *(u32x4*)(out + (((size_t)b * S + s_out) * H + h) * DV + 8 * ch) = *(const LDS_AS u32x4*)(ost + row * OP + 8 * ch);
+  }
 }
 
 }  // namespace
