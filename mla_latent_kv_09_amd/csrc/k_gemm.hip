@@ -92,7 +92,17 @@ __global__ __launch_bounds__(G_THREADS, 1) void k_gemm(GemmArgs g) {
   __shared__ __attribute__((aligned(1024))) char lds[LDS_BYTES];
   const int n_tiles = (g.N + BN - 1) / BN;
   const int bid = blockIdx.x;
-  const int mt = bid / n_tiles, nt = bid % n_tiles;
+  // Tile order. Block i runs on XCD i % 8. With few N-tiles per M-tile (the
+  // long-K projections from the hidden state), the N-tiles of one M-tile are
+  // given to one XCD back to back, so its L2 fetches each A slice once for all
+  // of them; otherwise plain row order (A shared across the XCDs).
+  const int m_tiles = (g.M + BM - 1) / BM;
+  int mt = bid / n_tiles, nt = bid % n_tiles;
+  if (NI == 2 && n_tiles <= 16 && m_tiles % 8 == 0) {
+    const int xcd = bid & 7, local = bid >> 3;
+    mt = (local / n_tiles) * 8 + xcd;
+    nt = local % n_tiles;
+  }
   const int m0 = mt * BM, n0 = nt * BN;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
   const int wm = w & 1, wn = w >> 1;  // wave covers A rows m0 + 128wm .., B rows n0 + 32 NI wn ..
