@@ -2,12 +2,15 @@
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload 3]
     python bench.py --workload 5          (prefill: projections + attention)
+    python bench.py --workload 6          (two-token decode)
     python bench.py --copy-bytes N        (known-size copy, for counter scaling)
 
 Decode (workloads 2-4; 3 is the default): one step is one mla_decode call
 (query absorption, split-context attention over the paged latent cache,
 log-sum-exp combine and per-head W_UV) for one new token of every sequence in
 the batch, on seeded synthetic inputs that are already resident in HBM.
+Workload 6 is the same step with two new tokens per sequence (mla_decode_multi,
+q_len 2); its throughput counts both.
 Prefill (workload 5): one step is mla_rope_latent_project (latent rows into
 the cache, query path) followed by causal mla_prefill.
 
@@ -42,6 +45,8 @@ WORKLOAD_NAMES = {
     4: "mla_decode B=32 H=128 L~U[1024,32768] d_c=512 d_rope=64 bf16, shuffled 64-token pages",
     5: "mla_rope_latent_project (latent + query projections) + causal mla_prefill, B=4 S=4096 d_model=7168 "
        "d_q=1536 H=128 bf16",
+    6: "mla_decode_multi B=64 q_len=2 H=128 L=8192 d_c=512 d_rope=64 bf16, 64-token pages (one draft token "
+       "per sequence)",
 }
 
 
@@ -138,21 +143,27 @@ def cpu_baseline(case, budget_s):
     except Exception:  # pragma: no cover
         threads = len(os.sched_getaffinity(0))
     c = case.cache
+    Q = case.q_len
     done, t0 = 0, time.perf_counter()
     order = np.argsort(c.context_lens)[::-1] if case.batch > 1 else [0]
     rows_done = []
     for b in order[: case.batch]:
-        oracle.decode(case.dims, case.q_nope, case.q_pe, case.w_uk, case.w_uv, c.pool, c.block_table,
-                      c.context_lens, batch_rows=[int(b)])
-        done += 1
+        for j in range(Q):
+            # query j of a q_len-token step sees the context minus the later new tokens
+            lens = c.context_lens - (Q - 1 - j)
+            qn = case.q_nope if Q == 1 else case.q_nope[:, j]
+            qp = case.q_pe if Q == 1 else case.q_pe[:, j]
+            oracle.decode(case.dims, qn, qp, case.w_uk, case.w_uv, c.pool, c.block_table, lens, batch_rows=[int(b)])
+            done += 1
         rows_done.append(int(b))
         if time.perf_counter() - t0 >= budget_s:
             break
     dt = time.perf_counter() - t0
     toks = int(sum(int(c.context_lens[b]) for b in rows_done))
+    what = "sequences" if Q == 1 else f"sequences x {Q} new tokens"
     return {"value": done / dt, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
-            "sample": f"{done} of {case.batch} sequences ({toks} cached tokens, all {case.dims.n_heads} heads), "
-                      f"float64 numpy, {dt:.1f} s"}
+            "sample": f"{len(rows_done)} of {case.batch} {what} ({toks} cached tokens, all {case.dims.n_heads} "
+                      f"heads), float64 numpy, {dt:.1f} s"}
 
 
 def cpu_baseline_prefill(case, budget_s):
@@ -289,16 +300,19 @@ def main():
     q_nope, q_pe = to_torch(case.q_nope, dev), to_torch(case.q_pe, dev)
     w_uk, w_uv = to_torch(case.w_uk, dev), to_torch(case.w_uv, dev)
     d = mla.Dims.of(case.dims)
-    B, H = case.batch, d.n_heads
-    ws_bytes = mla.mla_decode_workspace_size(d, B, cache.max_context)
+    B, H, Q = case.batch, d.n_heads, case.q_len
+    ws_bytes = mla.mla_decode_multi_workspace_size(d, B, Q, cache.max_context)
     ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
-    out = torch.empty((B, H, d.d_v), dtype=torch.bfloat16, device=dev)
+    out = torch.empty(tuple(q_nope.shape[:-1]) + (d.d_v,), dtype=torch.bfloat16, device=dev)
     torch.cuda.synchronize()
     print(f"[bench] workload {args.workload}: inputs ready in {time.perf_counter() - t_gen:.1f} s; "
           f"decode path {mla.mla_decode_path(d)}; workspace {ws_bytes / 1e6:.1f} MB", file=sys.stderr, flush=True)
 
     def step():
-        mla.mla_decode(d, q_nope, q_pe, w_uk, w_uv, cache, out=out, workspace=ws)
+        if Q == 1:
+            mla.mla_decode(d, q_nope, q_pe, w_uk, w_uv, cache, out=out, workspace=ws)
+        else:
+            mla.mla_decode_multi(d, q_nope, q_pe, w_uk, w_uv, cache, out=out, workspace=ws)
 
     for _ in range(args.warmup):
         step()
@@ -328,18 +342,38 @@ def main():
     breakdown = profile_end(lib)
 
     sum_l = int(c.context_lens.astype(np.int64).sum())
-    cache_bytes = sum_l * CACHE_ROW_BYTES
+    # key rows seen, over all queries: query j of q_len sees L - (q_len - 1 - j)
+    seen = Q * sum_l - B * Q * (Q - 1) // 2
+    cache_bytes = sum_l * CACHE_ROW_BYTES          # every cached row read once per step
     weight_bytes = 2 * H * 128 * 512 * 2
-    io_bytes = B * H * (128 + 64 + 128) * 2 + B * 4
+    io_bytes = B * Q * H * (128 + 64 + 128) * 2 + B * 4
     step_bytes = cache_bytes + weight_bytes + io_bytes
-    step_flop = 2.0 * H * sum_l * (576 + 512) + 2 * 2.0 * B * H * 128 * 512
+    split_flop = 2.0 * H * seen * (576 + 512)      # scores over 576 columns + latent output over 512
+    step_flop = split_flop + 2 * 2.0 * B * Q * H * 128 * 512
     if split_name not in kern:
         raise RuntimeError(f"no timing for {split_name}: {kern}")
     split_ms = kern[split_name][0] / kern[split_name][1]
-    achieved = cache_bytes / (split_ms * 1e-3) / 1e9
     kernels_us = {k: round(v[0] / v[1] * 1e3, 2) for k, v in breakdown.items()}
+    # the split kernel's bound: whichever of its HBM bytes and MFMA flops takes longer at peak
+    mfma_bound = split_flop / (BF16_PEAK_TFLOPS * 1e12) > cache_bytes / (HBM_PEAK_GBS * 1e9)
+    if mfma_bound:
+        achieved = split_flop / (split_ms * 1e-3) / 1e12
+        roof = {"bound": "mfma", "achieved": round(achieved, 1), "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                "frac": round(achieved / BF16_PEAK_TFLOPS, 4)}
+        rule = {"algorithmic_flop": split_flop,
+                "flop_rule": f"2 x {H} heads x (576 + 512) per (query, visible cached token), {seen} of those"}
+    else:
+        achieved = cache_bytes / (split_ms * 1e-3) / 1e9
+        roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(achieved / HBM_PEAK_GBS, 4)}
+        rule = {"algorithmic_bytes": cache_bytes,
+                "bytes_rule": f"{CACHE_ROW_BYTES} B per cached token x {sum_l} tokens"}
+    qtag = "" if Q == 1 else f"_Q{Q}"
+    roof.update({"traffic": measured_traffic(f"{split_name}_B{B}{qtag}_H{H}_L{int(cache.max_context)}",
+                                             "mla_latent_kv_09_amd/csrc/k_decode.hip"),
+                 "kernel": split_name, "kernel_us": round(split_ms * 1e3, 2), **rule})
 
-    tokens_per_s = B / (ms * 1e-3)
+    tokens_per_s = B * Q / (ms * 1e-3)
     line = {
         "metric": "MLA decode tokens/s + achieved HBM GB/s / MFMA % of peak, 1×MI355X",
         "value": round(tokens_per_s, 1),
@@ -353,16 +387,10 @@ def main():
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic (seeded N(0,1) cache rows and queries, weights std 1/sqrt(512))",
-        "config": {"workload": WORKLOAD_NAMES[args.workload], "batch": B, "heads": H,
+        "config": {"workload": WORKLOAD_NAMES[args.workload], "batch": B, "q_len": Q, "heads": H,
                    "cached_tokens": sum_l, "max_context": int(cache.max_context), "page": 64,
                    "parallelism": "none (1 GPU)"},
-        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(achieved / HBM_PEAK_GBS, 4),
-                     "traffic": measured_traffic(f"{split_name}_B{B}_H{H}_L{int(cache.max_context)}",
-                                                 "mla_latent_kv_09_amd/csrc/k_decode.hip"),
-                     "kernel": split_name, "kernel_us": round(split_ms * 1e3, 2),
-                     "algorithmic_bytes": cache_bytes,
-                     "bytes_rule": f"{CACHE_ROW_BYTES} B per cached token x {sum_l} tokens"},
+        "roofline": roof,
         "step": {"algorithmic_bytes": step_bytes, "algorithmic_flop": step_flop,
                  "hbm_GB_per_s": round(step_bytes / (ms * 1e-3) / 1e9, 1),
                  "hbm_frac": round(step_bytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),

@@ -150,6 +150,26 @@ mla_status mla_decode(const mla_dims* dims, int32_t batch,
                       const mla_cache* cache, void* out,
                       void* workspace, size_t workspace_bytes, void* stream);
 
+/* Multi-token decode: q_len new queries per sequence, the last q_len tokens
+ * of its context, as a draft step of speculative decoding with multi-token
+ * prediction produces them ("DeepSeek 2025 technical report walkthrough" §2.3;
+ * "8.1 DeepSeek architecture" §6). Query j of sequence b sits at position
+ * context_lens[b] - q_len + j and sees cached tokens 0 .. that position (causal
+ * among the new tokens; their rows must already be in the cache). The result
+ * is that of mla_prefill with seq_len = q_len, computed in the absorbed form of
+ * mla_decode, which reads each cached row once per query instead of
+ * up-projecting the context; mla_decode is the case q_len == 1.
+ *   q_nope device [batch, q_len, n_heads, d_nope]
+ *   q_pe   device [batch, q_len, n_heads, d_rope], unrotated
+ *   out    device [batch, q_len, n_heads, d_v]
+ * q_len in [1, 64] and <= max_context, batch * q_len <= 65535, else
+ * MLA_ERR_BAD_SHAPE. context_lens[b] must be >= q_len: a query that sees no
+ * cached token gets a zero output. batch == 0 is a no-op returning MLA_OK. */
+mla_status mla_decode_multi(const mla_dims* dims, int32_t batch, int32_t q_len,
+                            const void* q_nope, const void* q_pe, const void* w_uk, const void* w_uv,
+                            const mla_cache* cache, void* out,
+                            void* workspace, size_t workspace_bytes, void* stream);
+
 /* Causal prefill: seq_len new queries per sequence, the last seq_len tokens of
  * its context. Query s of sequence b sits at position context_lens[b] - seq_len + s
  * and sees cached tokens 0 .. context_lens[b] - seq_len + s. With
@@ -168,6 +188,8 @@ mla_status mla_prefill(const mla_dims* dims, int32_t batch, int32_t seq_len,
 /* Workspace each entry point needs for the given sizes (bytes, 0 possible). */
 mla_status mla_project_workspace_size(const mla_dims* dims, int32_t n_tokens, int32_t d_q, size_t* bytes);
 mla_status mla_decode_workspace_size(const mla_dims* dims, int32_t batch, int32_t max_context, size_t* bytes);
+mla_status mla_decode_multi_workspace_size(const mla_dims* dims, int32_t batch, int32_t q_len,
+                                           int32_t max_context, size_t* bytes);
 mla_status mla_prefill_workspace_size(const mla_dims* dims, int32_t batch, int32_t seq_len,
                                       int32_t max_context, size_t* bytes);
 

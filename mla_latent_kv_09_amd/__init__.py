@@ -19,8 +19,9 @@ import torch
 
 __all__ = [
     "Dims", "Cache", "QProj", "MLAError", "library", "library_path",
-    "mla_rope_latent_project", "mla_decode", "mla_prefill",
-    "mla_project_workspace_size", "mla_decode_workspace_size", "mla_prefill_workspace_size",
+    "mla_rope_latent_project", "mla_decode", "mla_decode_multi", "mla_prefill",
+    "mla_project_workspace_size", "mla_decode_workspace_size", "mla_decode_multi_workspace_size",
+    "mla_prefill_workspace_size",
     "mla_status_string", "mla_decode_path", "mla_prefill_path", "mla_version",
 ]
 
@@ -73,9 +74,11 @@ def library():
         pd, pc, pq = ctypes.POINTER(_Dims), ctypes.POINTER(_Cache), ctypes.POINTER(_QProj)
         lib.mla_rope_latent_project.argtypes = [pd, i32, i32, vp, vp, vp, vp, vp, pc, pq, vp, sz, vp]
         lib.mla_decode.argtypes = [pd, i32, vp, vp, vp, vp, pc, vp, vp, sz, vp]
+        lib.mla_decode_multi.argtypes = [pd, i32, i32, vp, vp, vp, vp, pc, vp, vp, sz, vp]
         lib.mla_prefill.argtypes = [pd, i32, i32, vp, vp, vp, vp, pc, vp, vp, sz, vp]
         lib.mla_project_workspace_size.argtypes = [pd, i32, i32, ctypes.POINTER(sz)]
         lib.mla_decode_workspace_size.argtypes = [pd, i32, i32, ctypes.POINTER(sz)]
+        lib.mla_decode_multi_workspace_size.argtypes = [pd, i32, i32, i32, ctypes.POINTER(sz)]
         lib.mla_prefill_workspace_size.argtypes = [pd, i32, i32, i32, ctypes.POINTER(sz)]
         lib.mla_status_string.argtypes = [ctypes.c_int]
         lib.mla_status_string.restype = ctypes.c_char_p
@@ -83,9 +86,9 @@ def library():
         lib.mla_prefill_path.argtypes = [pd, i32, i32]
         lib.mla_profile_begin.argtypes = []
         lib.mla_profile_only.argtypes = [ctypes.c_char_p]
-        for f in ("mla_rope_latent_project", "mla_decode", "mla_prefill", "mla_project_workspace_size",
-                  "mla_decode_workspace_size", "mla_prefill_workspace_size", "mla_profile_begin",
-                  "mla_profile_only"):
+        for f in ("mla_rope_latent_project", "mla_decode", "mla_decode_multi", "mla_prefill",
+                  "mla_project_workspace_size", "mla_decode_workspace_size", "mla_decode_multi_workspace_size",
+                  "mla_prefill_workspace_size", "mla_profile_begin", "mla_profile_only"):
             getattr(lib, f).restype = ctypes.c_int
         for f in ("mla_decode_path", "mla_prefill_path", "mla_version"):
             getattr(lib, f).restype = ctypes.c_int32
@@ -237,6 +240,13 @@ def mla_decode_workspace_size(dims, batch: int, max_context: int) -> int:
     return n.value
 
 
+def mla_decode_multi_workspace_size(dims, batch: int, q_len: int, max_context: int) -> int:
+    n = ctypes.c_size_t(0)
+    _ok(library().mla_decode_multi_workspace_size(ctypes.byref(Dims.of(dims).c()), batch, q_len, max_context,
+                                                  ctypes.byref(n)), "mla_decode_multi_workspace_size")
+    return n.value
+
+
 def mla_prefill_workspace_size(dims, batch: int, seq_len: int, max_context: int) -> int:
     n = ctypes.c_size_t(0)
     _ok(library().mla_prefill_workspace_size(ctypes.byref(Dims.of(dims).c()), batch, seq_len, max_context,
@@ -304,6 +314,29 @@ def mla_decode(dims, q_nope, q_pe, w_uk, w_uv, cache: Cache, out=None, workspace
     _ok(library().mla_decode(ctypes.byref(d.c()), B, q_nope.data_ptr(), q_pe.data_ptr(), w_uk.data_ptr(),
                              w_uv.data_ptr(), ctypes.byref(cc), out.data_ptr(),
                              ws.data_ptr() if ws is not None else None, nbytes, _stream(stream)), "mla_decode")
+    return out
+
+
+def mla_decode_multi(dims, q_nope, q_pe, w_uk, w_uv, cache: Cache, out=None, workspace=None, stream=None):
+    """q_len new queries per sequence (the last q_len tokens of its context),
+    absorbed form; q_nope is [B, q_len, H, d_nope]; returns out [B, q_len, H, d_v]."""
+    d = Dims.of(dims)
+    B, Q = q_nope.shape[:2]
+    dt = d.torch_dtype
+    _need(q_nope, "q_nope", (B, Q, d.n_heads, d.d_nope), dt)
+    _need(q_pe, "q_pe", (B, Q, d.n_heads, d.d_rope), dt)
+    _need(w_uk, "w_uk", (d.n_heads * d.d_nope, d.d_c), dt)
+    _need(w_uv, "w_uv", (d.n_heads * d.d_v, d.d_c), dt)
+    _check_cache(cache, d, B)
+    if out is None:
+        out = torch.empty((B, Q, d.n_heads, d.d_v), dtype=dt, device=q_nope.device)
+    _need(out, "out", (B, Q, d.n_heads, d.d_v), dt)
+    ws, nbytes = _workspace(mla_decode_multi_workspace_size(d, B, Q, cache.max_context), q_nope.device, workspace)
+    cc = cache.c()
+    _ok(library().mla_decode_multi(ctypes.byref(d.c()), B, Q, q_nope.data_ptr(), q_pe.data_ptr(), w_uk.data_ptr(),
+                                   w_uv.data_ptr(), ctypes.byref(cc), out.data_ptr(),
+                                   ws.data_ptr() if ws is not None else None, nbytes, _stream(stream)),
+        "mla_decode_multi")
     return out
 
 

@@ -135,6 +135,16 @@ WsLayout ws_layout(int H, int batch, int splits) {
   return l;
 }
 
+// Query row v of a step with q_len new tokens per sequence belongs to sequence
+// v / q_len, whose last q_len cached tokens are the new ones; token j = v %
+// q_len sits at position ctx - q_len + j and sees ctx - (q_len - 1 - j) rows.
+// With q_len == 1 this is the sequence's whole context.
+__device__ __forceinline__ int visible_rows(const int32_t* ctx_lens, int v, int q_len) {
+  if (q_len == 1) return ctx_lens[v];
+  const int seq = v / q_len;
+  return ctx_lens[seq] - (q_len - 1 - (v - seq * q_len));
+}
+
 // ------------------------------------------------------------ k_absorb ----
 // RoPE inverse frequencies base^(-2i/d_rope), formed on the host in double
 struct RopeFreq {
@@ -149,7 +159,7 @@ struct RopeFreq {
 // 128 bytes) is written whole. The blocks of head h also write its rotated,
 // scaled q_pe slice, each for every 8th sequence; those loads are issued
 // first.
-__global__ __launch_bounds__(256) void k_absorb(int B, int H, const bf16* __restrict__ q_nope,
+__global__ __launch_bounds__(256) void k_absorb(int B, int H, int q_len, const bf16* __restrict__ q_nope,
                                                 const bf16* __restrict__ q_pe, const bf16* __restrict__ w_uk,
                                                 const int32_t* __restrict__ ctx_lens, float qscale, RopeFreq rope,
                                                 bf16* __restrict__ qt) {
@@ -168,7 +178,7 @@ __global__ __launch_bounds__(256) void k_absorb(int B, int H, const bf16* __rest
   int rp_len = 0;
   uint32_t rp_x = 0;
   if (rp_b0 < B) {
-    rp_len = ctx_lens[rp_b0];
+    rp_len = visible_rows(ctx_lens, rp_b0, q_len);
     rp_x = *(const uint32_t*)(q_pe + ((size_t)rp_b0 * H + h) * DR + 2 * rp_i);
   }
   // every independent load first: the W_UK slice and the first chunk of queries
@@ -237,7 +247,7 @@ __global__ __launch_bounds__(256) void k_absorb(int B, int H, const bf16* __rest
   const double theta = rope.theta[rp_i];
   for (int b = rp_b0; b < B; b += RP_STEP) {
     if (b != rp_b0) {
-      rp_len = ctx_lens[b];
+      rp_len = visible_rows(ctx_lens, b, q_len);
       rp_x = *(const uint32_t*)(q_pe + ((size_t)b * H + h) * DR + 2 * rp_i);
     }
     const double ang = (double)(rp_len - 1) * theta;
@@ -335,15 +345,29 @@ __device__ __forceinline__ void mfma_qk_done(f32x16& acc) {
 // outstanding global loads (vmcnt 0), which would drain the tile prefetch.
 __device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
 
-__global__ __launch_bounds__(SPLIT_THREADS, 1) void k_split(int H, int B, int splits, int pps,
+__global__ __launch_bounds__(SPLIT_THREADS, 1) void k_split(int H, int B, int q_len, bool pair_xcd, int splits,
+                                                            int pps,
                                                             const bf16* __restrict__ qt,
                                                             const bf16* __restrict__ rows,
                                                             const int32_t* __restrict__ block_table,
                                                             int max_blocks, const int32_t* __restrict__ ctx_lens,
                                                             float* __restrict__ part_o, float* __restrict__ part_ml) {
   __shared__ __attribute__((aligned(1024))) char lds[SPLIT_LDS];
-  const int split = blockIdx.x, b = blockIdx.y;
-  const int L = ctx_lens[b];
+  // b is the query row (sequence b / q_len, new token b % q_len)
+  int split = blockIdx.x, b = blockIdx.y;
+  if (pair_xcd) {
+    // the q_len rows of one (sequence, split) read the same pages: give them
+    // consecutive dispatch slots of one XCD (block i runs on XCD i % 8) so
+    // that all but the first find the pages in that XCD's L2. Needs the
+    // number of (sequence, split) units to be a multiple of 8.
+    const int lin = blockIdx.y * gridDim.x + blockIdx.x, local = lin >> 3;
+    const int unit_local = local / q_len, j = local - unit_local * q_len;
+    const int unit = unit_local * 8 + (lin & 7), seq = unit / splits;
+    split = unit - seq * splits;
+    b = seq * q_len + j;
+  }
+  const int seq = b / q_len;
+  const int L = visible_rows(ctx_lens, b, q_len);
   const int t_begin = split * pps * PAGE;
   const int t_end = min(t_begin + pps * PAGE, L);
   if (t_begin >= t_end) return;
@@ -352,7 +376,7 @@ __global__ __launch_bounds__(SPLIT_THREADS, 1) void k_split(int H, int B, int sp
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
   const int hl = lane & 31, g = lane >> 5, i16 = lane & 15, G = lane >> 4;
   const int h_own = w * 32 + hl;  // head of this lane in the score phase
-  const int32_t* table = block_table + (size_t)b * max_blocks;
+  const int32_t* table = block_table + (size_t)seq * max_blocks;
 
   // Streams tile i into ring slot i % 4: 9 direct-to-LDS 16-byte loads per
   // lane. Instruction k of wave w fills slot chunks [(w*9+k)*64, +64) in
@@ -689,7 +713,7 @@ __global__ __launch_bounds__(SPLIT_THREADS, 1) void k_split(int H, int B, int sp
 //      split loads of a thread issued together; bf16 into LDS
 //   3. out^T[v, b] = sum_c W_UV[h*128 + v, c] o_c[b, c] on MFMA; each lane ends
 //      with 4 consecutive outputs of one sequence (one 8-byte store)
-__global__ __launch_bounds__(256) void k_combine_uv(int H, int B, int splits, int pps,
+__global__ __launch_bounds__(256) void k_combine_uv(int H, int B, int q_len, int splits, int pps,
                                                     const int32_t* __restrict__ ctx_lens,
                                                     const float* __restrict__ part_o,
                                                     const float* __restrict__ part_ml,
@@ -712,7 +736,7 @@ __global__ __launch_bounds__(256) void k_combine_uv(int H, int B, int splits, in
   // 512 columns), which are needed only at the end.
   const int rr = lane >> 4, q = lane & 15, r = 4 * w + rr, b = b0 + r;
   const float* ml = part_ml + ((size_t)h * B + (b < B ? b : 0)) * splits * 2;
-  const int len = b < B ? ctx_lens[b] : 0;
+  const int len = b < B ? visible_rows(ctx_lens, b, q_len) : 0;
   typedef __attribute__((ext_vector_type(2))) float f32x2_t;
   f32x2_t ml_q = {-INFINITY, 0.f};
   if (q < splits && b < B) ml_q = *(const f32x2_t*)(ml + 2 * q);  // used only if q < ns
@@ -723,7 +747,7 @@ __global__ __launch_bounds__(256) void k_combine_uv(int H, int B, int splits, in
 #pragma unroll
     for (int mt = 0; mt < 2; ++mt) wf[ks][mt] = *(const u32x4*)(wv + (size_t)(32 * w + 16 * mt + i16) * DC + 32 * ks + 8 * G);
   {
-    const int ns = b < B ? ((len + PAGE - 1) / PAGE + pps - 1) / pps : 0;
+    const int ns = b < B && len > 0 ? ((len + PAGE - 1) / PAGE + pps - 1) / pps : 0;
     float M = q < ns ? ml_q[0] : -INFINITY;
     for (int sp = q + 16; sp < ns; sp += 16) M = fmaxf(M, ml[2 * sp]);
 #pragma unroll
@@ -808,15 +832,16 @@ bool decode_fast_context_ok(int max_context) {
   return plan_splits(1, max_context).pages_per_split <= 64;
 }
 
-size_t decode_fast_workspace(const mla_dims& d, int batch, int max_context) {
-  const Plan p = plan_splits(batch, max_context);
-  return ws_layout(d.n_heads, batch, p.splits).total;
+size_t decode_fast_workspace(const mla_dims& d, int batch, int q_len, int max_context) {
+  const Plan p = plan_splits(batch * q_len, max_context);
+  return ws_layout(d.n_heads, batch * q_len, p.splits).total;
 }
 
-hipError_t decode_fast(const mla_dims& d, float scale, int batch, int max_context, const void* q_nope,
+hipError_t decode_fast(const mla_dims& d, float scale, int n_seq, int q_len, int max_context, const void* q_nope,
                        const void* q_pe, const void* w_uk, const void* w_uv, const CacheView& c, void* out,
                        void* ws, size_t ws_bytes, hipStream_t s) {
   const int H = d.n_heads;
+  const int batch = n_seq * q_len;  // query rows
   const Plan p = plan_splits(batch, max_context);
   const WsLayout l = ws_layout(H, batch, p.splits);
   if (ws_bytes < l.total) return hipErrorInvalidValue;
@@ -829,7 +854,7 @@ hipError_t decode_fast(const mla_dims& d, float scale, int batch, int max_contex
     ProfScope ps("mla_decode_absorb", s);
     RopeFreq rope;
     for (int i = 0; i < DR / 2; ++i) rope.theta[i] = pow((double)d.rope_base, -2.0 * i / (double)DR);
-    hipLaunchKernelGGL(k_absorb, dim3(H, DC / 64), dim3(256), 0, s, batch, H, (const bf16*)q_nope,
+    hipLaunchKernelGGL(k_absorb, dim3(H, DC / 64), dim3(256), 0, s, batch, H, q_len, (const bf16*)q_nope,
                        (const bf16*)q_pe, (const bf16*)w_uk, c.context_lens, scale * LOG2E, rope, qt);
   }
   hipError_t e = hipGetLastError();
@@ -837,7 +862,9 @@ hipError_t decode_fast(const mla_dims& d, float scale, int batch, int max_contex
   const dim3 grid(p.splits, batch);
   {
     ProfScope ps("mla_decode_split", s);
-    hipLaunchKernelGGL(k_split, grid, dim3(SPLIT_THREADS), 0, s, H, batch, p.splits, p.pages_per_split, qt,
+    const bool pair_xcd = q_len > 1 && ((int64_t)n_seq * p.splits) % 8 == 0;
+    hipLaunchKernelGGL(k_split, grid, dim3(SPLIT_THREADS), 0, s, H, batch, q_len, pair_xcd, p.splits,
+                       p.pages_per_split, qt,
                        (const bf16*)c.rows, c.block_table, c.max_blocks, c.context_lens, part_o, part_ml);
   }
   if ((e = hipGetLastError()) != hipSuccess) return e;
@@ -845,7 +872,7 @@ hipError_t decode_fast(const mla_dims& d, float scale, int batch, int max_contex
   const int hpad = (H + 7) / 8 * 8;
   {
     ProfScope ps("mla_decode_combine_uv", s);
-    hipLaunchKernelGGL(k_combine_uv, dim3(hpad * nbt), dim3(256), 0, s, H, batch, p.splits,
+    hipLaunchKernelGGL(k_combine_uv, dim3(hpad * nbt), dim3(256), 0, s, H, batch, q_len, p.splits,
                        p.pages_per_split, c.context_lens, part_o, part_ml, (const bf16*)w_uv, (bf16*)out);
   }
   return hipGetLastError();

@@ -52,8 +52,10 @@ hipError_t attn_generic(const mla_dims& d, float scale, int n_seq, int q_per_seq
 bool decode_fast_supported(const mla_dims& d, const CacheView& c);
 // contexts up to 256 runs of 64 pages (1,048,576 tokens) per sequence
 bool decode_fast_context_ok(int max_context);
-size_t decode_fast_workspace(const mla_dims& d, int batch, int max_context);
-hipError_t decode_fast(const mla_dims& d, float scale, int batch, int max_context,
+// n_seq sequences with q_len new queries each (query j of sequence b at
+// position context_lens[b] - q_len + j); q_len == 1 is plain decode
+size_t decode_fast_workspace(const mla_dims& d, int n_seq, int q_len, int max_context);
+hipError_t decode_fast(const mla_dims& d, float scale, int n_seq, int q_len, int max_context,
                        const void* q_nope, const void* q_pe, const void* w_uk, const void* w_uv,
                        const CacheView& c, void* out, void* ws, size_t ws_bytes, hipStream_t s);
 

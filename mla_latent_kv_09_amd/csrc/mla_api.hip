@@ -65,6 +65,10 @@ mla_status check_ws(void* ws, size_t have, size_t need) {
   return MLA_OK;
 }
 
+// query rows of one decode call (a grid dimension of the split kernel)
+constexpr int64_t MAX_QUERY_ROWS = 65535;
+constexpr int32_t MAX_Q_LEN = 64;
+
 mla_status hip_status(hipError_t e) { return e == hipSuccess ? MLA_OK : MLA_ERR_HIP; }
 
 bool fast_dims(const mla_dims* d) {
@@ -110,15 +114,21 @@ mla_status mla_project_workspace_size(const mla_dims* d, int32_t n_tokens, int32
   return MLA_OK;
 }
 
-mla_status mla_decode_workspace_size(const mla_dims* d, int32_t batch, int32_t max_context, size_t* bytes) {
+mla_status mla_decode_multi_workspace_size(const mla_dims* d, int32_t batch, int32_t q_len, int32_t max_context,
+                                           size_t* bytes) {
   mla_status st = check_dims(d);
   if (st != MLA_OK) return st;
   if (!bytes) return MLA_ERR_NULL_ARG;
-  if (batch < 0 || max_context < 0) return MLA_ERR_BAD_SHAPE;
+  if (batch < 0 || max_context < 0 || q_len < 1 || q_len > MAX_Q_LEN) return MLA_ERR_BAD_SHAPE;
+  if ((int64_t)batch * q_len > MAX_QUERY_ROWS) return MLA_ERR_BAD_SHAPE;
   *bytes = (fast_dims(d) && batch > 0 && max_context > 0 && mla::decode_fast_context_ok(max_context))
-               ? mla::decode_fast_workspace(*d, batch, max_context)
+               ? mla::decode_fast_workspace(*d, batch, q_len, max_context)
                : 0;
   return MLA_OK;
+}
+
+mla_status mla_decode_workspace_size(const mla_dims* d, int32_t batch, int32_t max_context, size_t* bytes) {
+  return mla_decode_multi_workspace_size(d, batch, 1, max_context, bytes);
 }
 
 mla_status mla_prefill_workspace_size(const mla_dims* d, int32_t batch, int32_t seq_len, int32_t max_context,
@@ -194,12 +204,13 @@ mla_status mla_rope_latent_project(const mla_dims* d, int32_t n_tokens, int32_t 
                                          qp->w_qr, hr, qp->d_q, qp->q_pe, hr, s));
 }
 
-mla_status mla_decode(const mla_dims* d, int32_t batch, const void* q_nope, const void* q_pe,
-                      const void* w_uk, const void* w_uv, const mla_cache* cache, void* out, void* ws,
-                      size_t ws_bytes, void* stream) {
+mla_status mla_decode_multi(const mla_dims* d, int32_t batch, int32_t q_len, const void* q_nope, const void* q_pe,
+                            const void* w_uk, const void* w_uv, const mla_cache* cache, void* out, void* ws,
+                            size_t ws_bytes, void* stream) {
   mla_status st = check_dims(d);
   if (st != MLA_OK) return st;
-  if (batch < 0) return MLA_ERR_BAD_SHAPE;
+  if (batch < 0 || q_len < 1 || q_len > MAX_Q_LEN) return MLA_ERR_BAD_SHAPE;
+  if ((int64_t)batch * q_len > MAX_QUERY_ROWS) return MLA_ERR_BAD_SHAPE;
   if (batch == 0) return MLA_OK;
   if (!q_nope || !q_pe || !w_uk || !w_uv || !out) return MLA_ERR_NULL_ARG;
   if (!aligned(q_nope, 16) || !aligned(q_pe, 16) || !aligned(w_uk, 16) || !aligned(w_uv, 16) ||
@@ -207,17 +218,24 @@ mla_status mla_decode(const mla_dims* d, int32_t batch, const void* q_nope, cons
     return MLA_ERR_ALIGNMENT;
   CacheView v{};
   if ((st = check_cache(cache, &v)) != MLA_OK) return st;
+  if (q_len > cache->max_context) return MLA_ERR_BAD_SHAPE;
   const bool fast = mla::decode_fast_supported(*d, v) && mla::decode_fast_context_ok(cache->max_context);
-  const size_t need = fast ? mla::decode_fast_workspace(*d, batch, cache->max_context) : 0;
+  const size_t need = fast ? mla::decode_fast_workspace(*d, batch, q_len, cache->max_context) : 0;
   if ((st = check_ws(ws, ws_bytes, need)) != MLA_OK) return st;
   hipStream_t s = (hipStream_t)stream;
   if (trace_on())
-    fprintf(stderr, "[mla] decode batch=%d heads=%d max_context=%d path=%s ws=%zu\n", batch, d->n_heads,
-            cache->max_context, fast ? "mfma" : "generic", need);
+    fprintf(stderr, "[mla] decode batch=%d q_len=%d heads=%d max_context=%d path=%s ws=%zu\n", batch, q_len,
+            d->n_heads, cache->max_context, fast ? "mfma" : "generic", need);
   if (fast)
-    return hip_status(mla::decode_fast(*d, scale_of(d), batch, cache->max_context, q_nope, q_pe, w_uk, w_uv,
-                                       v, out, ws, ws_bytes, s));
-  return hip_status(mla::attn_generic(*d, scale_of(d), batch, 1, q_nope, q_pe, w_uk, w_uv, v, out, s));
+    return hip_status(mla::decode_fast(*d, scale_of(d), batch, q_len, cache->max_context, q_nope, q_pe, w_uk,
+                                       w_uv, v, out, ws, ws_bytes, s));
+  return hip_status(mla::attn_generic(*d, scale_of(d), batch, q_len, q_nope, q_pe, w_uk, w_uv, v, out, s));
+}
+
+mla_status mla_decode(const mla_dims* d, int32_t batch, const void* q_nope, const void* q_pe,
+                      const void* w_uk, const void* w_uv, const mla_cache* cache, void* out, void* ws,
+                      size_t ws_bytes, void* stream) {
+  return mla_decode_multi(d, batch, 1, q_nope, q_pe, w_uk, w_uv, cache, out, ws, ws_bytes, stream);
 }
 
 mla_status mla_prefill(const mla_dims* d, int32_t batch, int32_t seq_len, const void* q_nope, const void* q_pe,

@@ -15,9 +15,10 @@ exactly.
 
 Named workloads
 ---------------
-``WORKLOADS`` holds the five shapes the library is measured on: a tiny fp32
+``WORKLOADS`` holds the six shapes the library is measured on: a tiny fp32
 case, three decode shapes (uniform 4K, DeepSeek-V3-shaped 8K, ragged long
-context) and a prefill with the latent and query projections.
+context), a prefill with the latent and query projections, and a two-token
+decode (a draft token per sequence) of the 8K shape.
 """
 from __future__ import annotations
 
@@ -133,8 +134,8 @@ def paged_layout(lens: np.ndarray, shuffle_rng: Optional[np.random.Generator]):
 @dataclasses.dataclass
 class DecodeCase:
     dims: Dims
-    q_nope: np.ndarray     # [B, H, d_nope]
-    q_pe: np.ndarray       # [B, H, d_rope] (unrotated)
+    q_nope: np.ndarray     # [B, H, d_nope], or [B, q_len, H, d_nope] for q_len > 1
+    q_pe: np.ndarray       # [B, H, d_rope] / [B, q_len, H, d_rope] (unrotated)
     w_uk: np.ndarray       # [H*d_nope, d_c]
     w_uv: np.ndarray       # [H*d_v, d_c]
     cache: PagedCache      # rows already hold rotated k_pe
@@ -143,6 +144,10 @@ class DecodeCase:
     @property
     def batch(self) -> int:
         return self.q_nope.shape[0]
+
+    @property
+    def q_len(self) -> int:
+        return 1 if self.q_nope.ndim == 3 else self.q_nope.shape[1]
 
 
 @dataclasses.dataclass
@@ -174,16 +179,19 @@ class ProjectCase:
 
 
 def make_decode_case(seed: int, batch: int, dims: Dims, lens, paged: bool = True,
-                     shuffle: bool = False, w_std: Optional[float] = None) -> DecodeCase:
+                     shuffle: bool = False, w_std: Optional[float] = None, q_len: int = 1) -> DecodeCase:
     """Decode inputs: q drawn N(0,1); W_UK, W_UV std 1/sqrt(d_c) (unless given);
-    cache rows (c_KV || k_pe) drawn N(0,1), k_pe taken as already rotated."""
+    cache rows (c_KV || k_pe) drawn N(0,1), k_pe taken as already rotated.
+    With q_len > 1 there are q_len queries per sequence (the last q_len tokens
+    of its context) and the query arrays gain a q_len axis after the batch."""
     d = _Draw(seed, dims.dtype)
     H = dims.n_heads
     std = (1.0 / math.sqrt(dims.d_c)) if w_std is None else w_std
     w_uk = d.normal((H * dims.d_nope, dims.d_c), std)
     w_uv = d.normal((H * dims.d_v, dims.d_c), std)
-    q_nope = d.normal((batch, H, dims.d_nope))
-    q_pe = d.normal((batch, H, dims.d_rope))
+    qshape = (batch,) if q_len == 1 else (batch, q_len)
+    q_nope = d.normal(qshape + (H, dims.d_nope))
+    q_pe = d.normal(qshape + (H, dims.d_rope))
     lens = np.asarray(lens, dtype=np.int64)
     if lens.ndim == 0:
         lens = np.full(batch, int(lens), dtype=np.int64)
@@ -250,7 +258,7 @@ V3 = dict(d_c=512, d_rope=64, d_nope=128, d_v=128)
 
 
 def workload(k: int):
-    """Inputs of named workload k (1..5)."""
+    """Inputs of named workload k (1..6)."""
     seed = 1000 + k
     if k == 1:   # tiny fp32, contiguous cache, rows made by the projection
         dims = Dims(n_heads=4, d_c=32, d_rope=8, d_nope=16, d_v=16, dtype="f32")
@@ -265,6 +273,9 @@ def workload(k: int):
     if k == 5:   # causal prefill with latent and query projections
         return make_project_case(seed, batch=4, seq_len=4096, d_model=7168,
                                  dims=Dims(n_heads=128, **V3), d_q=1536)
+    if k == 6:   # two-token decode (one draft token per sequence), DeepSeek-V3 shape
+        return make_decode_case(seed, 64, Dims(n_heads=128, **V3, softmax_scale=1.0 / math.sqrt(192.0)), 8192,
+                                q_len=2)
     raise ValueError(k)
 
 
@@ -274,6 +285,7 @@ WORKLOADS = {
     3: "bf16 decode, DeepSeek-V3 shape: B=64 H=128 d_c=512 d_rope=64 L=8192, 64-token pages",
     4: "bf16 ragged decode: B=32 H=128 L~U[1024,32768], shuffled 64-token pages",
     5: "bf16 causal prefill: B=4 S=4096 d_model=7168 d_q=1536 H=128, projections + attention",
+    6: "bf16 two-token decode, DeepSeek-V3 shape: B=64 q_len=2 H=128 d_c=512 d_rope=64 L=8192, 64-token pages",
 }
 
 

@@ -118,6 +118,32 @@ def test_prefill_errors():
     assert pf(out=None) == NULL
 
 
+def test_decode_multi_errors():
+    lib = mla.library()
+    c = cache()
+
+    def dm(batch=4, q_len=2, cc=c, ptrs=(P, P, P, P), out=P, ws=P, wsb=1 << 30):
+        return lib.mla_decode_multi(ctypes.byref(V3()), batch, q_len, *ptrs, ctypes.byref(cc), out, ws, wsb, None)
+    assert dm(q_len=0) == SHAPE and dm(q_len=-1) == SHAPE
+    assert dm(q_len=65) == SHAPE                          # above the documented q_len bound
+    assert dm(batch=-1) == SHAPE
+    assert dm(batch=1100, q_len=60) == SHAPE              # 66,000 query rows
+    assert dm(batch=0) == OK
+    assert dm(q_len=8, cc=cache(max_context=4, max_blocks_per_seq=1)) == SHAPE  # q_len > max_context
+    assert dm(ptrs=(P, P, None, P)) == NULL
+    assert dm(out=None) == NULL
+    assert dm(ptrs=(P, P + 2, P, P)) == ALIGN
+    need = mla.mla_decode_multi_workspace_size(V3(), 4, 2, 8192)
+    assert need > 0
+    assert dm(wsb=need - 1) == WS
+    assert dm(ws=None, wsb=need) == NULL
+    # query rows are what the workspace scales with: 4 x 2 rows need what 8 x 1 rows do
+    assert need == mla.mla_decode_workspace_size(V3(), 8, 8192)
+    assert mla.mla_decode_multi_workspace_size(V3(), 4, 1, 8192) == mla.mla_decode_workspace_size(V3(), 4, 8192)
+    with pytest.raises(mla.MLAError):
+        mla.mla_decode_multi_workspace_size(V3(), 4, 0, 8192)
+
+
 def test_project_errors():
     lib = mla.library()
     d = V3()

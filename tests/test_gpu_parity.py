@@ -234,6 +234,92 @@ def test_decode_large_score_growth_takes_the_rescale_branch():
     assert_parity(run_decode(case), oracle_decode(case), "bf16", "rescale")
 
 
+# ---------------------------------------------------- multi-token decode --
+
+def oracle_multi(case, seqs=None):
+    """Query j of q_len sits at position L - q_len + j: the oracle's decode of
+    that single query over the first L - (q_len - 1 - j) cached tokens."""
+    c = case.cache
+    Q = case.q_len
+    seqs = list(range(case.batch)) if seqs is None else seqs
+    out = np.empty((len(seqs), Q, case.dims.n_heads, case.dims.d_v))
+    for j in range(Q):
+        lens = c.context_lens - (Q - 1 - j)
+        out[:, j] = oracle.decode(case.dims, case.q_nope[:, j], case.q_pe[:, j], case.w_uk, case.w_uv, c.pool,
+                                  c.block_table, lens, batch_rows=seqs)
+    return out
+
+
+def run_multi(case):
+    c = device_cache(case.cache)
+    out = mla.mla_decode_multi(case.dims, to_torch(case.q_nope), to_torch(case.q_pe), to_torch(case.w_uk),
+                               to_torch(case.w_uv), c)
+    torch.cuda.synchronize()
+    return from_torch(out)
+
+
+MULTI = [
+    # 8 sequences: (sequence, split) units a multiple of 8, so the q_len rows of a unit share an XCD
+    ("H16 q2 ragged", 16, 2, [2, 3, 63, 64, 65, 130, 700, 1000], True),
+    ("H128 q4 ragged", 128, 4, [4, 64, 65, 127, 128, 129, 1500, 2047], True),
+    # 3 sequences of at most 11 pages: 3 splits, 9 units, plain block order
+    ("H128 q3 few units", 128, 3, [3, 129, 700], True),
+    ("H32 q7 long", 32, 7, [5000, 7], True),
+    ("H128 q2 identity pages", 128, 2, [64, 2047], False),
+]
+
+
+@pytest.mark.parametrize("name,H,Q,lens,shuffle", MULTI, ids=[m[0] for m in MULTI])
+def test_decode_multi_small_bf16(name, H, Q, lens, shuffle):
+    _log(f"multi-token decode {name}")
+    case = make_decode_case(300 + H + Q, len(lens), Dims(H, **V3), lens, shuffle=shuffle, q_len=Q)
+    assert_parity(run_multi(case), oracle_multi(case), "bf16", name)
+
+
+def test_decode_multi_q1_matches_decode_bitwise():
+    _log("multi-token decode with q_len 1 is mla_decode")
+    case = make_decode_case(41, 5, Dims(64, **V3), [1, 64, 300, 999, 4000], shuffle=True)
+    got = run_decode(case)
+    c = device_cache(case.cache)
+    multi = mla.mla_decode_multi(case.dims, to_torch(case.q_nope)[:, None], to_torch(case.q_pe)[:, None],
+                                 to_torch(case.w_uk), to_torch(case.w_uv), c)
+    torch.cuda.synchronize()
+    assert np.array_equal(from_torch(multi)[:, 0], got)
+
+
+def test_decode_multi_fp32_generic_path():
+    _log("multi-token decode, fp32 generic kernels")
+    dims = Dims(4, 32, 8, 16, 16, dtype="f32")
+    case = make_decode_case(42, 3, dims, [3, 70, 200], shuffle=True, q_len=3)
+    assert mla.mla_decode_path(dims) == 0
+    assert_parity(run_multi(case), oracle_multi(case), "f32", "fp32 q_len 3")
+
+
+def test_decode_multi_short_context_gives_zeros():
+    """A context shorter than q_len leaves the earliest queries with no
+    visible token: their outputs are zero, the others are normal."""
+    _log("multi-token decode, context shorter than q_len")
+    case = make_decode_case(43, 2, Dims(16, **V3), [2, 300], shuffle=True, q_len=4)
+    got = run_multi(case)
+    assert np.all(got[0, :2] == 0.0)
+    ref = oracle_multi(case, seqs=[1])
+    assert_parity(got[1:], ref, "bf16", "normal sequence")
+    c = case.cache
+    for j in (2, 3):
+        lens = c.context_lens - (3 - j)
+        r = oracle.decode(case.dims, case.q_nope[:, j], case.q_pe[:, j], case.w_uk, case.w_uv, c.pool,
+                          c.block_table, lens, batch_rows=[0])
+        assert_parity(got[0, j][None], r, "bf16", f"short sequence, query {j}")
+
+
+def test_workload6_two_token_decode_full_size_sampled():
+    _log("workload 6 (B=64 q_len=2 H=128 L=8192): full size on the GPU, oracle on sampled sequences")
+    case = workload(6)
+    got = run_multi(case)
+    sample = [0, 37, case.batch - 1]
+    assert_parity(got[sample], oracle_multi(case, seqs=sample), "bf16", "workload 6")
+
+
 # ------------------------------------------------ MFMA projection/prefill --
 
 def _project_and_prefill(case, dims, d_q):
