@@ -107,11 +107,15 @@ struct Plan {
   int splits;
 };
 
-Plan plan_splits(int batch, int max_context) {
+// batch counts query rows; q_len > 1 rows per sequence share their pages
+Plan plan_splits(int batch, int max_context, int q_len) {
   const int max_pages = (max_context + PAGE - 1) / PAGE;
-  // aim for one workgroup per compute unit across the batch, 4..32 pages each
+  // aim for one workgroup per compute unit across the batch, 4..32 pages each;
+  // with several rows per sequence up to 64, which halves the fp32 partials
+  // (one per row and run) where the rows alone fill the chip
+  const int cap = q_len > 1 ? 64 : 32;
   int pps = (int)(((int64_t)batch * max_pages + 255) / 256);
-  pps = pps < 4 ? 4 : (pps > 32 ? 32 : pps);
+  pps = pps < 4 ? 4 : (pps > cap ? cap : pps);
   const int min_pps = (max_pages + MAX_SPLITS - 1) / MAX_SPLITS;
   if (pps < min_pps) pps = min_pps;
   Plan p;
@@ -829,11 +833,11 @@ bool decode_fast_supported(const mla_dims& d, const CacheView& c) {
 
 bool decode_fast_context_ok(int max_context) {
   // a run's page numbers are held one per lane of a wave
-  return plan_splits(1, max_context).pages_per_split <= 64;
+  return plan_splits(1, max_context, 1).pages_per_split <= 64;
 }
 
 size_t decode_fast_workspace(const mla_dims& d, int batch, int q_len, int max_context) {
-  const Plan p = plan_splits(batch * q_len, max_context);
+  const Plan p = plan_splits(batch * q_len, max_context, q_len);
   return ws_layout(d.n_heads, batch * q_len, p.splits).total;
 }
 
@@ -842,7 +846,7 @@ hipError_t decode_fast(const mla_dims& d, float scale, int n_seq, int q_len, int
                        void* ws, size_t ws_bytes, hipStream_t s) {
   const int H = d.n_heads;
   const int batch = n_seq * q_len;  // query rows
-  const Plan p = plan_splits(batch, max_context);
+  const Plan p = plan_splits(batch, max_context, q_len);
   const WsLayout l = ws_layout(H, batch, p.splits);
   if (ws_bytes < l.total) return hipErrorInvalidValue;
   char* base = (char*)ws;
