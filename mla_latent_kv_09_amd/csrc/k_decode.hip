@@ -415,6 +415,25 @@ __global__ __launch_bounds__(SPLIT_THREADS, 1) void k_split(int H, int B, int q_
     }
   };
 
+  // Rows past the context in the last tile hold whatever the page holds
+  // beyond the sequence, possibly non-finite bit patterns. The score step
+  // masks them (a select), but in the value product 0 * NaN is NaN, so before
+  // that tile's value step each lane zeroes the chunks its own copies brought
+  // in for those rows. A wave still in the tile's score step may read either
+  // value there; it discards both.
+  auto clear_tail = [&](int i) {
+    const int valid = t_end - (t_begin + i * TILE);
+    if (valid >= TILE) return;
+    // copy k of this lane filled chunk pos = (9w + k) * 64 + lane, of row pos / 72
+    // (the lane index is recomputed here so that nothing stays live across the loop)
+    const int first = w * TILE_LOADS * 64 + (int)__builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u));
+    const int lim = valid * ROW_CHUNKS - first;  // chunk pos is past the context iff 64 k >= lim
+    LDS_AS char* base = (LDS_AS char*)lds + (i % N_SLOTS) * TILE_BYTES + first * 16;
+#pragma unroll
+    for (int k = 0; k < TILE_LOADS; ++k)
+      if (64 * k >= lim) *(LDS_AS u32x4*)(base + k * 1024) = (u32x4){0, 0, 0, 0};
+  };
+
   // query of this lane's head: Qt[b, h_own, 16s + 8g .. +7], s < 36 (lanes of
   // heads >= H read head H-1; nothing of theirs is stored)
   bf16x8_t qf[QK_STEPS];
@@ -673,6 +692,7 @@ __global__ __launch_bounds__(SPLIT_THREADS, 1) void k_split(int H, int B, int q_
     lds_barrier();  // tile i and P of tile i-1 visible; slot (i+2)%4 and P buffer i%2 free
     step(T{}, T{}, i, i + 2 < n_tiles ? i + 2 : -1);
   }
+  clear_tail(n_tiles - 1);
   lds_barrier();
   step(F{}, T{}, n_tiles, -1);
 

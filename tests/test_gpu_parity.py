@@ -234,6 +234,49 @@ def test_decode_large_score_growth_takes_the_rescale_branch():
     assert_parity(run_decode(case), oracle_decode(case), "bf16", "rescale")
 
 
+def _poison_tails(case):
+    """Fills every cache row past a sequence's context in its last page with
+    NaN or infinity bit patterns, as a reused page may hold."""
+    c = case.cache
+    for b, L in enumerate(c.context_lens):
+        L = int(L)
+        if L % 64:
+            page = c.block_table[b, (L - 1) // 64]
+            c.pool[page, L % 64:, :] = (0x7FC0, 0x7F80, 0xFF80)[b % 3]
+
+
+def test_decode_ignores_non_finite_rows_past_the_context():
+    _log("decode with NaN/Inf rows past the context")
+    case = make_decode_case(44, 4, Dims(128, **V3), [1, 33, 100, 1000], shuffle=True)
+    _poison_tails(case)
+    got = run_decode(case)
+    assert np.all(np.isfinite(got))
+    assert_parity(got, oracle_decode(case), "bf16", "poisoned tails")
+
+
+def test_chunked_prefill_ignores_non_finite_rows_past_the_context():
+    _log("chunked prefill with NaN/Inf rows past the context")
+    dims = Dims(16, **V3)
+    case = make_decode_case(45, 3, dims, [70, 129, 200], shuffle=True)
+    _poison_tails(case)
+    S = 70
+    rng = np.random.default_rng(4)
+    from synth import f32_to_bf16_bits
+    qn = f32_to_bf16_bits(rng.standard_normal((3, S, 16, 128)).astype(np.float32))
+    qp = f32_to_bf16_bits(rng.standard_normal((3, S, 16, 64)).astype(np.float32))
+    out = mla.mla_prefill(dims, to_torch(qn), to_torch(qp), to_torch(case.w_uk), to_torch(case.w_uv),
+                          device_cache(case.cache))
+    torch.cuda.synchronize()
+    got = from_torch(out)
+    assert np.all(np.isfinite(got))
+    lens0 = case.cache.context_lens
+    for s in (0, 37, 69):
+        lens = lens0 - (S - 1 - s)
+        ref = oracle.decode(dims, qn[:, s], qp[:, s], case.w_uk, case.w_uv, case.cache.pool, case.cache.block_table,
+                            lens)
+        assert_parity(got[:, s], ref, "bf16", f"poisoned tails, query {s}")
+
+
 # ---------------------------------------------------- multi-token decode --
 
 def oracle_multi(case, seqs=None):
@@ -274,6 +317,15 @@ def test_decode_multi_small_bf16(name, H, Q, lens, shuffle):
     _log(f"multi-token decode {name}")
     case = make_decode_case(300 + H + Q, len(lens), Dims(H, **V3), lens, shuffle=shuffle, q_len=Q)
     assert_parity(run_multi(case), oracle_multi(case), "bf16", name)
+
+
+def test_decode_multi_ignores_non_finite_rows_past_the_context():
+    _log("multi-token decode with NaN/Inf rows past the context")
+    case = make_decode_case(46, 8, Dims(32, **V3), [3, 40, 64, 65, 97, 200, 513, 1000], shuffle=True, q_len=3)
+    _poison_tails(case)
+    got = run_multi(case)
+    assert np.all(np.isfinite(got))
+    assert_parity(got, oracle_multi(case), "bf16", "poisoned tails")
 
 
 def test_decode_multi_q1_matches_decode_bitwise():
