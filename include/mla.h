@@ -170,6 +170,42 @@ mla_status mla_decode_multi(const mla_dims* dims, int32_t batch, int32_t q_len,
                             const mla_cache* cache, void* out,
                             void* workspace, size_t workspace_bytes, void* stream);
 
+/* FP8 latent cache ("DeepSeek core techniques: MoE and MLA attention" §6.3:
+ * the KV cache is quantised to FP8 dynamically for deployment; "8.1 DeepSeek
+ * architecture" §5: one scale per block, not one global scale).
+ * Format: E4M3 codes (OCP "fn": largest value 448, round to nearest even)
+ * with one power-of-two scale per token. A page of block_size tokens is
+ * block_size rows of [d_c code bytes || d_rope bf16 values of k_pe (kept
+ * unquantised)], then block_size scale bytes E (scale 2^(E - 127)), then
+ * padding to a multiple of 16 bytes (mla_fp8_page_bytes; 41,024 bytes for the
+ * DeepSeek-V3 shape with 64-token pages, against 73,728 in bf16). A token's
+ * scale is the smallest 2^e, e >= -127, with max|c_KV| <= 448 * 2^e; its
+ * codes are RNE(c_KV / 2^e), so no code saturates. */
+mla_status mla_fp8_page_bytes(const mla_dims* dims, int32_t block_size, size_t* bytes);
+
+/* Quantises n_rows bf16 cache rows [n_rows, d_c + d_rope] (the layout
+ * mla_rope_latent_project writes) into FP8 pages: row r goes to slot slots[r]
+ * (slot r when slots is NULL), i.e. page slot / block_size, offset
+ * slot % block_size. Only that row's bytes and scale byte are written (not the
+ * padding). dims->dtype must be MLA_BF16. block_size in [1, 4096]. pool is
+ * device memory of whole pages, 16-byte aligned. n_rows == 0 is a no-op. */
+mla_status mla_quantize_fp8(const mla_dims* dims, int32_t n_rows, const void* rows, const int32_t* slots,
+                            int32_t block_size, void* pool, void* stream);
+
+/* mla_decode_multi over an FP8 cache: cache->rows is the FP8 page pool, the
+ * block table and lengths as for mla_decode. The scores use the FP8 matrix
+ * core with the query q~ quantised like a cache row (one scale per head, its
+ * RoPE slice in bf16), and P is rounded to FP8 for the value product, so the
+ * result differs from the bf16 path's by FP8 rounding (a few percent of the
+ * output, relative). Requires the DeepSeek-V3 latent shape (d_c 512, d_rope
+ * 64, d_nope = d_v = 128, n_heads <= 128), bf16 queries and weights, 64-token
+ * pages and a paged cache; other shapes return MLA_ERR_UNSUPPORTED. q_len and
+ * batch bounds as for mla_decode_multi. */
+mla_status mla_decode_fp8(const mla_dims* dims, int32_t batch, int32_t q_len,
+                          const void* q_nope, const void* q_pe, const void* w_uk, const void* w_uv,
+                          const mla_cache* cache, void* out,
+                          void* workspace, size_t workspace_bytes, void* stream);
+
 /* Causal prefill: seq_len new queries per sequence, the last seq_len tokens of
  * its context. Query s of sequence b sits at position context_lens[b] - seq_len + s
  * and sees cached tokens 0 .. context_lens[b] - seq_len + s. With
@@ -190,6 +226,8 @@ mla_status mla_project_workspace_size(const mla_dims* dims, int32_t n_tokens, in
 mla_status mla_decode_workspace_size(const mla_dims* dims, int32_t batch, int32_t max_context, size_t* bytes);
 mla_status mla_decode_multi_workspace_size(const mla_dims* dims, int32_t batch, int32_t q_len,
                                            int32_t max_context, size_t* bytes);
+mla_status mla_decode_fp8_workspace_size(const mla_dims* dims, int32_t batch, int32_t q_len,
+                                         int32_t max_context, size_t* bytes);
 mla_status mla_prefill_workspace_size(const mla_dims* dims, int32_t batch, int32_t seq_len,
                                       int32_t max_context, size_t* bytes);
 

@@ -21,7 +21,8 @@ __all__ = [
     "Dims", "Cache", "QProj", "MLAError", "library", "library_path",
     "mla_rope_latent_project", "mla_decode", "mla_decode_multi", "mla_prefill",
     "mla_project_workspace_size", "mla_decode_workspace_size", "mla_decode_multi_workspace_size",
-    "mla_prefill_workspace_size",
+    "mla_prefill_workspace_size", "Fp8Cache", "mla_fp8_page_bytes", "mla_quantize_fp8", "mla_decode_fp8",
+    "mla_decode_fp8_workspace_size",
     "mla_status_string", "mla_decode_path", "mla_prefill_path", "mla_version",
 ]
 
@@ -76,6 +77,10 @@ def library():
         lib.mla_decode.argtypes = [pd, i32, vp, vp, vp, vp, pc, vp, vp, sz, vp]
         lib.mla_decode_multi.argtypes = [pd, i32, i32, vp, vp, vp, vp, pc, vp, vp, sz, vp]
         lib.mla_prefill.argtypes = [pd, i32, i32, vp, vp, vp, vp, pc, vp, vp, sz, vp]
+        lib.mla_decode_fp8.argtypes = [pd, i32, i32, vp, vp, vp, vp, pc, vp, vp, sz, vp]
+        lib.mla_quantize_fp8.argtypes = [pd, i32, vp, vp, i32, vp, vp]
+        lib.mla_fp8_page_bytes.argtypes = [pd, i32, ctypes.POINTER(sz)]
+        lib.mla_decode_fp8_workspace_size.argtypes = [pd, i32, i32, i32, ctypes.POINTER(sz)]
         lib.mla_project_workspace_size.argtypes = [pd, i32, i32, ctypes.POINTER(sz)]
         lib.mla_decode_workspace_size.argtypes = [pd, i32, i32, ctypes.POINTER(sz)]
         lib.mla_decode_multi_workspace_size.argtypes = [pd, i32, i32, i32, ctypes.POINTER(sz)]
@@ -88,7 +93,8 @@ def library():
         lib.mla_profile_only.argtypes = [ctypes.c_char_p]
         for f in ("mla_rope_latent_project", "mla_decode", "mla_decode_multi", "mla_prefill",
                   "mla_project_workspace_size", "mla_decode_workspace_size", "mla_decode_multi_workspace_size",
-                  "mla_prefill_workspace_size", "mla_profile_begin", "mla_profile_only"):
+                  "mla_prefill_workspace_size", "mla_profile_begin", "mla_profile_only", "mla_decode_fp8",
+                  "mla_quantize_fp8", "mla_fp8_page_bytes", "mla_decode_fp8_workspace_size"):
             getattr(lib, f).restype = ctypes.c_int
         for f in ("mla_decode_path", "mla_prefill_path", "mla_version"):
             getattr(lib, f).restype = ctypes.c_int32
@@ -156,6 +162,28 @@ class Cache:
         if self.block_table is None:
             return _Cache(self.rows.data_ptr(), 0, 0, None, 0, self.context_lens.data_ptr(), int(self.max_context))
         return _Cache(self.rows.data_ptr(), self.rows.shape[0], self.rows.shape[1], self.block_table.data_ptr(),
+                      self.block_table.shape[1], self.context_lens.data_ptr(), int(self.max_context))
+
+
+@dataclasses.dataclass
+class Fp8Cache:
+    """FP8 latent cache on the device (format in include/mla.h).
+
+    pages: uint8 [num_blocks, mla_fp8_page_bytes(dims, block_size)];
+    block_table: int32 [batch, max_blocks]; context_lens: int32 [batch].
+    """
+    pages: torch.Tensor
+    context_lens: torch.Tensor
+    max_context: int
+    block_table: torch.Tensor
+    block_size: int = 64
+
+    @property
+    def batch(self) -> int:
+        return self.context_lens.shape[0]
+
+    def c(self) -> _Cache:
+        return _Cache(self.pages.data_ptr(), self.pages.shape[0], self.block_size, self.block_table.data_ptr(),
                       self.block_table.shape[1], self.context_lens.data_ptr(), int(self.max_context))
 
 
@@ -337,6 +365,64 @@ def mla_decode_multi(dims, q_nope, q_pe, w_uk, w_uv, cache: Cache, out=None, wor
                                    w_uv.data_ptr(), ctypes.byref(cc), out.data_ptr(),
                                    ws.data_ptr() if ws is not None else None, nbytes, _stream(stream)),
         "mla_decode_multi")
+    return out
+
+
+def mla_fp8_page_bytes(dims, block_size: int = 64) -> int:
+    n = ctypes.c_size_t(0)
+    _ok(library().mla_fp8_page_bytes(ctypes.byref(Dims.of(dims).c()), block_size, ctypes.byref(n)),
+        "mla_fp8_page_bytes")
+    return n.value
+
+
+def mla_quantize_fp8(dims, rows, pages, slots=None, block_size: int = 64, stream=None):
+    """Quantises bf16 cache rows [n, d_c + d_rope] into the FP8 pages at
+    slots (int32 [n]; row r to slot r when None)."""
+    d = Dims.of(dims)
+    n = rows.shape[0]
+    _need(rows, "rows", (n, d.row), torch.bfloat16)
+    pb = mla_fp8_page_bytes(d, block_size)
+    _need(pages, "pages", (pages.shape[0], pb), torch.uint8)
+    if slots is not None:
+        _need(slots, "slots", (n,), torch.int32)
+    _ok(library().mla_quantize_fp8(ctypes.byref(d.c()), n, rows.data_ptr(),
+                                   slots.data_ptr() if slots is not None else None, block_size, pages.data_ptr(),
+                                   _stream(stream)), "mla_quantize_fp8")
+    return pages
+
+
+def mla_decode_fp8_workspace_size(dims, batch: int, q_len: int, max_context: int) -> int:
+    n = ctypes.c_size_t(0)
+    _ok(library().mla_decode_fp8_workspace_size(ctypes.byref(Dims.of(dims).c()), batch, q_len, max_context,
+                                                ctypes.byref(n)), "mla_decode_fp8_workspace_size")
+    return n.value
+
+
+def mla_decode_fp8(dims, q_nope, q_pe, w_uk, w_uv, cache: Fp8Cache, out=None, workspace=None, stream=None):
+    """Decode over an FP8 cache. q_nope [B, H, d_nope] (one new token per
+    sequence) or [B, q_len, H, d_nope]; out has the same leading shape."""
+    d = Dims.of(dims)
+    multi = q_nope.dim() == 4
+    B = q_nope.shape[0]
+    Q = q_nope.shape[1] if multi else 1
+    lead = (B, Q) if multi else (B,)
+    dt = d.torch_dtype
+    _need(q_nope, "q_nope", lead + (d.n_heads, d.d_nope), dt)
+    _need(q_pe, "q_pe", lead + (d.n_heads, d.d_rope), dt)
+    _need(w_uk, "w_uk", (d.n_heads * d.d_nope, d.d_c), dt)
+    _need(w_uv, "w_uv", (d.n_heads * d.d_v, d.d_c), dt)
+    _need(cache.context_lens, "context_lens", (B,), torch.int32)
+    _need(cache.pages, "pages", (cache.pages.shape[0], mla_fp8_page_bytes(d, cache.block_size)), torch.uint8)
+    _need(cache.block_table, "block_table", (B, cache.block_table.shape[1]), torch.int32)
+    if out is None:
+        out = torch.empty(lead + (d.n_heads, d.d_v), dtype=dt, device=q_nope.device)
+    _need(out, "out", lead + (d.n_heads, d.d_v), dt)
+    ws, nbytes = _workspace(mla_decode_fp8_workspace_size(d, B, Q, cache.max_context), q_nope.device, workspace)
+    cc = cache.c()
+    _ok(library().mla_decode_fp8(ctypes.byref(d.c()), B, Q, q_nope.data_ptr(), q_pe.data_ptr(), w_uk.data_ptr(),
+                                 w_uv.data_ptr(), ctypes.byref(cc), out.data_ptr(),
+                                 ws.data_ptr() if ws is not None else None, nbytes, _stream(stream)),
+        "mla_decode_fp8")
     return out
 
 

@@ -851,6 +851,35 @@ bool decode_fast_supported(const mla_dims& d, const CacheView& c) {
          c.block_size == PAGE;
 }
 
+void decode_plan(int rows, int max_context, int q_len, int* pages_per_split, int* splits) {
+  const Plan p = plan_splits(rows, max_context, q_len);
+  *pages_per_split = p.pages_per_split;
+  *splits = p.splits;
+}
+
+hipError_t decode_absorb(const mla_dims& d, float scale, int rows, int q_len, const void* q_nope, const void* q_pe,
+                         const void* w_uk, const int32_t* ctx_lens, void* qt, const char* prof_name, hipStream_t s) {
+  ProfScope ps(prof_name, s);
+  RopeFreq rope;
+  for (int i = 0; i < DR / 2; ++i) rope.theta[i] = pow((double)d.rope_base, -2.0 * i / (double)DR);
+  hipLaunchKernelGGL(k_absorb, dim3(d.n_heads, DC / 64), dim3(256), 0, s, rows, d.n_heads, q_len,
+                     (const bf16*)q_nope, (const bf16*)q_pe, (const bf16*)w_uk, ctx_lens, scale * LOG2E, rope,
+                     (bf16*)qt);
+  return hipGetLastError();
+}
+
+hipError_t decode_combine(const mla_dims& d, int rows, int q_len, int splits, int pps, const int32_t* ctx_lens,
+                          const float* part_o, const float* part_ml, const void* w_uv, void* out,
+                          const char* prof_name, hipStream_t s) {
+  const int H = d.n_heads;
+  const int nbt = (rows + 15) / 16;
+  const int hpad = (H + 7) / 8 * 8;
+  ProfScope ps(prof_name, s);
+  hipLaunchKernelGGL(k_combine_uv, dim3(hpad * nbt), dim3(256), 0, s, H, rows, q_len, splits, pps, ctx_lens, part_o,
+                     part_ml, (const bf16*)w_uv, (bf16*)out);
+  return hipGetLastError();
+}
+
 bool decode_fast_context_ok(int max_context) {
   // a run's page numbers are held one per lane of a wave
   return plan_splits(1, max_context, 1).pages_per_split <= 64;
@@ -874,14 +903,7 @@ hipError_t decode_fast(const mla_dims& d, float scale, int n_seq, int q_len, int
   float* part_o = (float*)(base + l.part_o);
   float* part_ml = (float*)(base + l.part_ml);
 
-  {
-    ProfScope ps("mla_decode_absorb", s);
-    RopeFreq rope;
-    for (int i = 0; i < DR / 2; ++i) rope.theta[i] = pow((double)d.rope_base, -2.0 * i / (double)DR);
-    hipLaunchKernelGGL(k_absorb, dim3(H, DC / 64), dim3(256), 0, s, batch, H, q_len, (const bf16*)q_nope,
-                       (const bf16*)q_pe, (const bf16*)w_uk, c.context_lens, scale * LOG2E, rope, qt);
-  }
-  hipError_t e = hipGetLastError();
+  hipError_t e = decode_absorb(d, scale, batch, q_len, q_nope, q_pe, w_uk, c.context_lens, qt, "mla_decode_absorb", s);
   if (e != hipSuccess) return e;
   const dim3 grid(p.splits, batch);
   {
@@ -892,14 +914,8 @@ hipError_t decode_fast(const mla_dims& d, float scale, int n_seq, int q_len, int
                        (const bf16*)c.rows, c.block_table, c.max_blocks, c.context_lens, part_o, part_ml);
   }
   if ((e = hipGetLastError()) != hipSuccess) return e;
-  const int nbt = (batch + 15) / 16;
-  const int hpad = (H + 7) / 8 * 8;
-  {
-    ProfScope ps("mla_decode_combine_uv", s);
-    hipLaunchKernelGGL(k_combine_uv, dim3(hpad * nbt), dim3(256), 0, s, H, batch, q_len, p.splits,
-                       p.pages_per_split, c.context_lens, part_o, part_ml, (const bf16*)w_uv, (bf16*)out);
-  }
-  return hipGetLastError();
+  return decode_combine(d, batch, q_len, p.splits, p.pages_per_split, c.context_lens, part_o, part_ml, w_uv, out,
+                        "mla_decode_combine_uv", s);
 }
 
 }  // namespace mla

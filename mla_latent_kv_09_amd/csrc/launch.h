@@ -59,6 +59,29 @@ hipError_t decode_fast(const mla_dims& d, float scale, int n_seq, int q_len, int
                        const void* q_nope, const void* q_pe, const void* w_uk, const void* w_uv,
                        const CacheView& c, void* out, void* ws, size_t ws_bytes, hipStream_t s);
 
+// Pieces of the decode path that the FP8-cache decode shares (rows = query
+// rows, n_seq * q_len). decode_absorb writes q~ [rows, H, 576] bf16;
+// decode_combine merges per-split partials [H][rows][splits][512] fp32 and
+// (m, l) [H][rows][splits][2] and applies W_UV.
+void decode_plan(int rows, int max_context, int q_len, int* pages_per_split, int* splits);
+hipError_t decode_absorb(const mla_dims& d, float scale, int rows, int q_len, const void* q_nope, const void* q_pe,
+                         const void* w_uk, const int32_t* ctx_lens, void* qt, const char* prof_name, hipStream_t s);
+hipError_t decode_combine(const mla_dims& d, int rows, int q_len, int splits, int pps, const int32_t* ctx_lens,
+                          const float* part_o, const float* part_ml, const void* w_uv, void* out,
+                          const char* prof_name, hipStream_t s);
+
+// ---- FP8 latent cache (E4M3 codes, one power-of-two scale per token) ------
+// Page of P tokens: P rows of [d_c codes || d_rope bf16 k_pe], then P scale
+// bytes (value 2^(E - 127)), padded to 16 bytes.
+size_t fp8_page_bytes(int page, int d_c, int d_rope);
+hipError_t quant_fp8(const mla_dims& d, int n_rows, const void* src, const int32_t* slots, int page, void* dst,
+                     hipStream_t s);
+bool decode_fp8_supported(const mla_dims& d, const CacheView& c);
+size_t decode_fp8_workspace(const mla_dims& d, int n_seq, int q_len, int max_context);
+hipError_t decode_fp8(const mla_dims& d, float scale, int n_seq, int q_len, int max_context, const void* q_nope,
+                      const void* q_pe, const void* w_uk, const void* w_uv, const CacheView& c, void* out, void* ws,
+                      size_t ws_bytes, hipStream_t s);
+
 // ---- MFMA GEMM (bf16, K multiple of 64, N multiple of 4) -----------------
 // C[m, n] = sum_k A[m, k] B[n, k]; A and B rows are K-contiguous.
 struct GemmArgs {

@@ -238,6 +238,73 @@ mla_status mla_decode(const mla_dims* d, int32_t batch, const void* q_nope, cons
   return mla_decode_multi(d, batch, 1, q_nope, q_pe, w_uk, w_uv, cache, out, ws, ws_bytes, stream);
 }
 
+mla_status mla_fp8_page_bytes(const mla_dims* d, int32_t block_size, size_t* bytes) {
+  mla_status st = check_dims(d);
+  if (st != MLA_OK) return st;
+  if (!bytes) return MLA_ERR_NULL_ARG;
+  if (block_size < 1 || block_size > 4096) return MLA_ERR_BAD_SHAPE;
+  *bytes = mla::fp8_page_bytes(block_size, d->d_c, d->d_rope);
+  return MLA_OK;
+}
+
+mla_status mla_quantize_fp8(const mla_dims* d, int32_t n_rows, const void* rows, const int32_t* slots,
+                            int32_t block_size, void* pool, void* stream) {
+  mla_status st = check_dims(d);
+  if (st != MLA_OK) return st;
+  if (d->dtype != MLA_BF16) return MLA_ERR_BAD_DTYPE;
+  if (n_rows < 0 || block_size < 1 || block_size > 4096) return MLA_ERR_BAD_SHAPE;
+  if (n_rows == 0) return MLA_OK;
+  if (!rows || !pool) return MLA_ERR_NULL_ARG;
+  if (!aligned(rows, 16) || !aligned(pool, 16) || (slots && !aligned(slots, 4))) return MLA_ERR_ALIGNMENT;
+  hipStream_t s = (hipStream_t)stream;
+  if (trace_on()) fprintf(stderr, "[mla] quantize_fp8 n_rows=%d block_size=%d\n", n_rows, block_size);
+  return hip_status(mla::quant_fp8(*d, n_rows, rows, slots, block_size, pool, s));
+}
+
+mla_status mla_decode_fp8_workspace_size(const mla_dims* d, int32_t batch, int32_t q_len, int32_t max_context,
+                                         size_t* bytes) {
+  mla_status st = check_dims(d);
+  if (st != MLA_OK) return st;
+  if (!bytes) return MLA_ERR_NULL_ARG;
+  if (batch < 0 || max_context < 0 || q_len < 1 || q_len > MAX_Q_LEN) return MLA_ERR_BAD_SHAPE;
+  if ((int64_t)batch * q_len > MAX_QUERY_ROWS) return MLA_ERR_BAD_SHAPE;
+  mla::CacheView v{};
+  v.paged = 1;
+  v.block_size = 64;
+  *bytes = (mla::decode_fp8_supported(*d, v) && batch > 0 && max_context > 0 &&
+            mla::decode_fast_context_ok(max_context))
+               ? mla::decode_fp8_workspace(*d, batch, q_len, max_context)
+               : 0;
+  return MLA_OK;
+}
+
+mla_status mla_decode_fp8(const mla_dims* d, int32_t batch, int32_t q_len, const void* q_nope, const void* q_pe,
+                          const void* w_uk, const void* w_uv, const mla_cache* cache, void* out, void* ws,
+                          size_t ws_bytes, void* stream) {
+  mla_status st = check_dims(d);
+  if (st != MLA_OK) return st;
+  if (batch < 0 || q_len < 1 || q_len > MAX_Q_LEN) return MLA_ERR_BAD_SHAPE;
+  if ((int64_t)batch * q_len > MAX_QUERY_ROWS) return MLA_ERR_BAD_SHAPE;
+  if (batch == 0) return MLA_OK;
+  if (!q_nope || !q_pe || !w_uk || !w_uv || !out) return MLA_ERR_NULL_ARG;
+  if (!aligned(q_nope, 16) || !aligned(q_pe, 16) || !aligned(w_uk, 16) || !aligned(w_uv, 16) ||
+      !aligned(out, 16))
+    return MLA_ERR_ALIGNMENT;
+  CacheView v{};
+  if ((st = check_cache(cache, &v)) != MLA_OK) return st;
+  if (q_len > cache->max_context) return MLA_ERR_BAD_SHAPE;
+  if (!mla::decode_fp8_supported(*d, v) || !mla::decode_fast_context_ok(cache->max_context))
+    return MLA_ERR_UNSUPPORTED;
+  const size_t need = mla::decode_fp8_workspace(*d, batch, q_len, cache->max_context);
+  if ((st = check_ws(ws, ws_bytes, need)) != MLA_OK) return st;
+  hipStream_t s = (hipStream_t)stream;
+  if (trace_on())
+    fprintf(stderr, "[mla] decode_fp8 batch=%d q_len=%d heads=%d max_context=%d ws=%zu\n", batch, q_len, d->n_heads,
+            cache->max_context, need);
+  return hip_status(mla::decode_fp8(*d, scale_of(d), batch, q_len, cache->max_context, q_nope, q_pe, w_uk, w_uv, v,
+                                    out, ws, ws_bytes, s));
+}
+
 mla_status mla_prefill(const mla_dims* d, int32_t batch, int32_t seq_len, const void* q_nope, const void* q_pe,
                        const void* w_uk, const void* w_uv, const mla_cache* cache, void* out, void* ws,
                        size_t ws_bytes, void* stream) {

@@ -23,9 +23,20 @@ def run_decode(case, device="cuda", workspace=None):
 
 
 def bar(dtype):
-    """(max-abs, normwise-relative, max-abs relative to max|ref|) bars."""
+    """(max-abs, normwise-relative, max-abs relative to max|ref|) bars.
+
+    "fp8" is decode over an FP8 cache against the oracle's decode over the
+    same (dequantised) cache: the kernel also rounds the absorbed query and
+    the probabilities to E4M3, whose unit roundoff is 2^-4. Each score then
+    carries a relative error of about 2^-4 / sqrt(3) of its spread and each
+    weight the same again, so the output's normwise error sits near 3 %
+    (measured 2-4 % on the oracle with those roundings); the bar allows
+    8 % = 1.3 * 2^-4, and 15 % of max|ref| for the largest element. There is
+    no absolute bar: short contexts have outputs near 1."""
     if dtype == "f32":
         return 1e-4, 1e-4, 1e-4
+    if dtype == "fp8":
+        return float("inf"), 8e-2, 0.15
     return 2e-2, 1e-2, 5e-2
 
 

@@ -144,6 +144,37 @@ def test_decode_multi_errors():
         mla.mla_decode_multi_workspace_size(V3(), 4, 0, 8192)
 
 
+def test_fp8_entry_points_errors_and_sizes():
+    lib = mla.library()
+    assert mla.mla_fp8_page_bytes(V3(), 64) == 41024          # 64 x 640 + 64
+    assert mla.mla_fp8_page_bytes(_Dims(4, 32, 8, 16, 16, 0.0, 10000.0, 1), 16) == 16 * 48 + 16
+    assert mla.mla_fp8_page_bytes(_Dims(4, 40, 8, 16, 16, 0.0, 10000.0, 1), 3) == 176   # 3 x 56 + 3 -> 176
+    with pytest.raises(mla.MLAError):
+        mla.mla_fp8_page_bytes(V3(), 0)
+
+    def q(n=8, rows=P, slots=P, bs=64, pool=P, d=None):
+        d = V3() if d is None else d
+        return lib.mla_quantize_fp8(ctypes.byref(d), n, rows, slots, bs, pool, None)
+    assert q(n=0) == OK
+    assert q(n=-1) == SHAPE and q(bs=0) == SHAPE and q(bs=5000) == SHAPE
+    assert q(rows=None) == NULL and q(pool=None) == NULL
+    assert q(rows=P + 8) == ALIGN and q(pool=P + 4) == ALIGN and q(slots=P + 2) == ALIGN
+    assert q(d=V3(dtype=0)) == DTYPE                           # rows must be bf16
+
+    def d8(batch=4, q_len=1, d=None, c=None, ptrs=(P, P, P, P), out=P, ws=P, wsb=1 << 30):
+        d = V3() if d is None else d
+        c = cache() if c is None else c
+        return lib.mla_decode_fp8(ctypes.byref(d), batch, q_len, *ptrs, ctypes.byref(c), out, ws, wsb, None)
+    assert d8(batch=0) == OK
+    assert d8(q_len=0) == SHAPE and d8(q_len=65) == SHAPE and d8(batch=-2) == SHAPE
+    assert d8(ptrs=(None, P, P, P)) == NULL and d8(out=None) == NULL
+    assert d8(d=_Dims(4, 32, 8, 16, 16, 0.0, 10000.0, 1)) == UNSUP       # not the DeepSeek-V3 shape
+    assert d8(c=cache(block_table=None)) == UNSUP                          # contiguous cache
+    need = mla.mla_decode_fp8_workspace_size(V3(), 4, 2, 8192)
+    assert need > 0 and d8(q_len=2, wsb=need - 1) == WS
+    assert mla.mla_decode_fp8_workspace_size(_Dims(4, 32, 8, 16, 16, 0.0, 10000.0, 1), 4, 1, 64) == 0
+
+
 def test_project_errors():
     lib = mla.library()
     d = V3()
