@@ -3,6 +3,7 @@
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload 3]
     python bench.py --workload 5          (prefill: projections + attention)
     python bench.py --workload 6          (two-token decode)
+    python bench.py --workload 7          (decode over an FP8 cache)
     python bench.py --copy-bytes N        (known-size copy, for counter scaling)
 
 Decode (workloads 2-4; 3 is the default): one step is one mla_decode call
@@ -10,7 +11,8 @@ Decode (workloads 2-4; 3 is the default): one step is one mla_decode call
 log-sum-exp combine and per-head W_UV) for one new token of every sequence in
 the batch, on seeded synthetic inputs that are already resident in HBM.
 Workload 6 is the same step with two new tokens per sequence (mla_decode_multi,
-q_len 2); its throughput counts both.
+q_len 2); its throughput counts both. Workload 7 is workload 3's step over an
+FP8 copy of its cache (mla_decode_fp8), quantised on the GPU before timing.
 Prefill (workload 5): one step is mla_rope_latent_project (latent rows into
 the cache, query path) followed by causal mla_prefill.
 
@@ -47,7 +49,10 @@ WORKLOAD_NAMES = {
        "d_q=1536 H=128 bf16",
     6: "mla_decode_multi B=64 q_len=2 H=128 L=8192 d_c=512 d_rope=64 bf16, 64-token pages (one draft token "
        "per sequence)",
+    7: "mla_decode_fp8 B=64 H=128 L=8192 d_c=512 d_rope=64, FP8 (E4M3, per-token scale) cache of workload 3, "
+       "64-token pages",
 }
+FP8_TOKEN_BYTES = 641          # one cached token in the FP8 cache: 512 codes + 64 bf16 + 1 scale byte
 
 
 def parse():
@@ -133,10 +138,13 @@ def copy_calibration(nbytes):
                       "GB_per_s_read_plus_write": round(2 * nbytes / (ms * 1e-3) / 1e9, 1)}), flush=True)
 
 
-def cpu_baseline(case, budget_s):
+def cpu_baseline(case, budget_s, fp8_cache=False):
     """The oracle as it stands, on whole sequences of the same workload, until
-    the time budget is spent (at least one sequence)."""
+    the time budget is spent (at least one sequence). With an FP8 cache the
+    oracle first quantises the sequence's pages, then decodes over the
+    dequantised rows."""
     import oracle
+    from oracle import fp8
     try:
         from threadpoolctl import threadpool_info
         threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
@@ -148,12 +156,20 @@ def cpu_baseline(case, budget_s):
     order = np.argsort(c.context_lens)[::-1] if case.batch > 1 else [0]
     rows_done = []
     for b in order[: case.batch]:
+        pool, table = c.pool, c.block_table
+        if fp8_cache:
+            n = (int(c.context_lens[b]) + 63) // 64
+            used = c.block_table[b, :n]
+            pool = fp8.dequantize_pool(fp8.quantize_pool(oracle.widen(c.pool[used]), case.dims.d_c), 64,
+                                       case.dims.d_c, case.dims.d_rope)
+            table = np.zeros_like(c.block_table)
+            table[b, :n] = np.arange(n)
         for j in range(Q):
             # query j of a q_len-token step sees the context minus the later new tokens
             lens = c.context_lens - (Q - 1 - j)
             qn = case.q_nope if Q == 1 else case.q_nope[:, j]
             qp = case.q_pe if Q == 1 else case.q_pe[:, j]
-            oracle.decode(case.dims, qn, qp, case.w_uk, case.w_uv, c.pool, c.block_table, lens, batch_rows=[int(b)])
+            oracle.decode(case.dims, qn, qp, case.w_uk, case.w_uv, pool, table, lens, batch_rows=[int(b)])
             done += 1
         rows_done.append(int(b))
         if time.perf_counter() - t0 >= budget_s:
@@ -293,15 +309,22 @@ def main():
 
     dev = "cuda:0"
     t_gen = time.perf_counter()
-    case = workload(args.workload)
+    fp8_cache = args.workload == 7
+    case = workload(3 if fp8_cache else args.workload)
     c = case.cache
     cache = mla.Cache(to_torch(c.pool, dev), to_torch(c.context_lens, dev), int(c.context_lens.max()),
                       to_torch(c.block_table, dev))
+    if fp8_cache:
+        nb, P, R = c.pool.shape
+        pages = torch.empty((nb, mla.mla_fp8_page_bytes(case.dims, P)), dtype=torch.uint8, device=dev)
+        mla.mla_quantize_fp8(case.dims, cache.rows.view(nb * P, R), pages, None, P)
+        cache = mla.Fp8Cache(pages, cache.context_lens, cache.max_context, cache.block_table, P)
     q_nope, q_pe = to_torch(case.q_nope, dev), to_torch(case.q_pe, dev)
     w_uk, w_uv = to_torch(case.w_uk, dev), to_torch(case.w_uv, dev)
     d = mla.Dims.of(case.dims)
     B, H, Q = case.batch, d.n_heads, case.q_len
-    ws_bytes = mla.mla_decode_multi_workspace_size(d, B, Q, cache.max_context)
+    ws_bytes = (mla.mla_decode_fp8_workspace_size(d, B, Q, cache.max_context) if fp8_cache
+                else mla.mla_decode_multi_workspace_size(d, B, Q, cache.max_context))
     ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
     out = torch.empty(tuple(q_nope.shape[:-1]) + (d.d_v,), dtype=torch.bfloat16, device=dev)
     torch.cuda.synchronize()
@@ -309,7 +332,9 @@ def main():
           f"decode path {mla.mla_decode_path(d)}; workspace {ws_bytes / 1e6:.1f} MB", file=sys.stderr, flush=True)
 
     def step():
-        if Q == 1:
+        if fp8_cache:
+            mla.mla_decode_fp8(d, q_nope, q_pe, w_uk, w_uv, cache, out=out, workspace=ws)
+        elif Q == 1:
             mla.mla_decode(d, q_nope, q_pe, w_uk, w_uv, cache, out=out, workspace=ws)
         else:
             mla.mla_decode_multi(d, q_nope, q_pe, w_uk, w_uv, cache, out=out, workspace=ws)
@@ -320,7 +345,7 @@ def main():
 
     lib = mla.library()
     stream = torch.cuda.current_stream()
-    split_name = "mla_decode_split"
+    split_name = "mla_decode8_split" if fp8_cache else "mla_decode_split"
     ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     # timed region: events around the dominant kernel only (two per step)
     lib.mla_profile_only(split_name.encode())
@@ -344,7 +369,8 @@ def main():
     sum_l = int(c.context_lens.astype(np.int64).sum())
     # key rows seen, over all queries: query j of q_len sees L - (q_len - 1 - j)
     seen = Q * sum_l - B * Q * (Q - 1) // 2
-    cache_bytes = sum_l * CACHE_ROW_BYTES          # every cached row read once per step
+    row_bytes = FP8_TOKEN_BYTES if fp8_cache else CACHE_ROW_BYTES
+    cache_bytes = sum_l * row_bytes                # every cached row read once per step
     weight_bytes = 2 * H * 128 * 512 * 2
     io_bytes = B * Q * H * (128 + 64 + 128) * 2 + B * 4
     step_bytes = cache_bytes + weight_bytes + io_bytes
@@ -355,7 +381,9 @@ def main():
     split_ms = kern[split_name][0] / kern[split_name][1]
     kernels_us = {k: round(v[0] / v[1] * 1e3, 2) for k, v in breakdown.items()}
     # the split kernel's bound: whichever of its HBM bytes and MFMA flops takes longer at peak
-    mfma_bound = split_flop / (BF16_PEAK_TFLOPS * 1e12) > cache_bytes / (HBM_PEAK_GBS * 1e9)
+    # (FP8 cache: 1024 of the 1088 columns run at the FP8 rate, twice bf16's)
+    mfma_s = split_flop / (BF16_PEAK_TFLOPS * 1e12) * ((64 + 1024 / 2) / 1088 if fp8_cache else 1.0)
+    mfma_bound = mfma_s > cache_bytes / (HBM_PEAK_GBS * 1e9)
     if mfma_bound:
         achieved = split_flop / (split_ms * 1e-3) / 1e12
         roof = {"bound": "mfma", "achieved": round(achieved, 1), "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
@@ -367,10 +395,11 @@ def main():
         roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(achieved / HBM_PEAK_GBS, 4)}
         rule = {"algorithmic_bytes": cache_bytes,
-                "bytes_rule": f"{CACHE_ROW_BYTES} B per cached token x {sum_l} tokens"}
-    qtag = "" if Q == 1 else f"_Q{Q}"
+                "bytes_rule": f"{row_bytes} B per cached token x {sum_l} tokens"}
+    qtag = ("" if Q == 1 else f"_Q{Q}") + ("_fp8" if fp8_cache else "")
     roof.update({"traffic": measured_traffic(f"{split_name}_B{B}{qtag}_H{H}_L{int(cache.max_context)}",
-                                             "mla_latent_kv_09_amd/csrc/k_decode.hip"),
+                                             "mla_latent_kv_09_amd/csrc/k_fp8.hip" if fp8_cache
+                                             else "mla_latent_kv_09_amd/csrc/k_decode.hip"),
                  "kernel": split_name, "kernel_us": round(split_ms * 1e3, 2), **rule})
 
     tokens_per_s = B * Q / (ms * 1e-3)
@@ -385,7 +414,7 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16",
+        "dtype": "fp8 e4m3 (cache codes, q~, P; k_pe and weights bf16)" if fp8_cache else "bf16",
         "data": "synthetic (seeded N(0,1) cache rows and queries, weights std 1/sqrt(512))",
         "config": {"workload": WORKLOAD_NAMES[args.workload], "batch": B, "q_len": Q, "heads": H,
                    "cached_tokens": sum_l, "max_context": int(cache.max_context), "page": 64,
@@ -399,7 +428,7 @@ def main():
                  "kernels_us": kernels_us},
     }
     if not args.no_cpu:
-        line["cpu_baseline"] = cpu_baseline(case, args.cpu_seconds)
+        line["cpu_baseline"] = cpu_baseline(case, args.cpu_seconds, fp8_cache)
     print(json.dumps(line), flush=True)
 
 

@@ -355,26 +355,84 @@ __global__ __launch_bounds__(THREADS, 1) void k_split8(int H, int B, int q_len, 
     }
   };
 
-  int e_page = 127, k_shift = 0;  // of the page in the score step
+  int e_page = 127;  // of the page in the score step
 
-  // ---- one pipeline step: values of page i - 1, then scores + softmax of
-  // page i with the copies of page dma_i spread over the score MFMAs ----
+  // ---- one pipeline step: scores of page i (the copies of page dma_i spread
+  // over them), then the value product of page i - 1 with the softmax of page
+  // i between its MFMAs (the two are independent) ----
   auto step = [&](auto do_qk, auto do_pv, int i, int dma_i) {
     constexpr bool QK = decltype(do_qk)::value, PV = decltype(do_pv)::value;
+    const uint32_t tq = slot_addr(i), tv = slot_addr(i - 1);
+    // P fragments of page i - 1: head 32ht + hl, tokens 32g .. 32g+31 (read
+    // first: the score MFMAs cover their latency)
+    i32x8 pf[4];
     if constexpr (PV) {
-      const uint32_t tv = slot_addr(i - 1), pb = pb_addr(i - 1);
-      uint32_t a_pr0 = o_pr[0], a_pr1 = o_pr[1], a_tv = o_tv;
+      const uint32_t pb = pb_addr(i - 1);
+      uint32_t a_pr0 = o_pr[0], a_pr1 = o_pr[1];
       opq(a_pr0);
       opq(a_pr1);
-      opq(a_tv);
-      a_pr0 += pb;
-      a_pr1 += pb;
-      a_tv += tv;
-      // P fragments: head 32ht + hl, tokens 32g .. 32g+31; a moved reference
-      // of the head's owner travels in the sign bits of tokens 0..7
-      i32x8 pf[4];
 #pragma unroll
-      for (int ht = 0; ht < 4; ++ht) pf[ht] = cat8(r128(a_pr0 + 2048 * ht), r128(a_pr1 + 2048 * ht));
+      for (int ht = 0; ht < 4; ++ht) pf[ht] = cat8(r128(pb + a_pr0 + 2048 * ht), r128(pb + a_pr1 + 2048 * ht));
+    }
+    f32x16 sc[2];
+    int e_t[2] = {0, 0}, ep = 0;
+    uint32_t ew[8];  // scale bytes of this lane's tokens 32rb + 8a + 4g .. +3, as [4rb + a]
+    if constexpr (QK) {
+      // scale bytes, read ahead of their use: the score rows', this lane's
+      // tokens', and one per lane for the page scale
+#pragma unroll
+      for (int rb = 0; rb < 2; ++rb) e_t[rb] = (int)*(const LDS_AS uint8_t*)(size_t)(tq + SCALE_OFF + 32 * rb + hl);
+      ep = (int)*(const LDS_AS uint8_t*)(size_t)(tq + SCALE_OFF + lane);
+#pragma unroll
+      for (int k = 0; k < 8; ++k)
+        ew[k] = *(const LDS_AS uint32_t*)(size_t)(tq + SCALE_OFF + 4 * g + 32 * (k >> 2) + 8 * (k & 3));
+      const bool dma = dma_i >= 0;
+      const char* dsrc = dma ? copy_src(dma_i) : nullptr;
+      const uint32_t ddst = dma ? copy_dst(dma_i) : 0u;
+      // 24 score MFMAs: per half page rb, 4 over k_pe (bf16, operand op 12rb + s)
+      // then 8 over the codes (FP8, op 12rb + 4 + ks), one accumulator per half
+      // page. Operands are read AHEAD MFMAs before their use.
+      auto a_read = [&](int op, u32x4 (&f)[2]) {
+        const int rb = op / 12, k = op % 12;
+        if (k < 4) {
+          uint32_t o1 = o_pe[k];
+          opq(o1);
+          f[0] = r128(tq + o1 + rb * 32 * ROW8);
+        } else {
+          const int ks = k - 4;
+          uint32_t oa = o_qa[2 * (ks & 1)], ob = o_qa[2 * (ks & 1) + 1];
+          opq(oa);
+          opq(ob);
+          const uint32_t c0 = tq + rb * 32 * ROW8 + (ks >> 1) * 128;
+          f[0] = r128(c0 + oa);
+          f[1] = r128(c0 + ob);
+        }
+      };
+      constexpr int AHEAD = 2;
+      u32x4 fa[AHEAD][2];
+#pragma unroll
+      for (int op = 0; op < AHEAD; ++op) a_read(op, fa[op]);
+#pragma unroll
+      for (int op = 0; op < 24; ++op) {
+        const int rb = op / 12, k = op % 12;
+        const u32x4 f0 = fa[op % AHEAD][0], f1 = fa[op % AHEAD][1];
+        if (op + AHEAD < 24) a_read(op + AHEAD, fa[op % AHEAD]);
+        if (k < 4) {
+          const bf16x8_t a = __builtin_bit_cast(bf16x8_t, f0);
+          if (k == 0) qk16_first(sc[rb], a, qp[k]);
+          else qk16(sc[rb], a, qp[k]);
+          if (k == 3) mfma_switch(sc[rb]);
+        } else {
+          qk8(sc[rb], cat8(f0, f1), qf[k - 4], e_t[rb], e_q);
+        }
+        // copies: after ops 1, 3, 5, ... (11 of them)
+        if ((op & 1) && dma && (op >> 1) < COPIES) copy_one(dsrc, ddst, op >> 1);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+    if constexpr (PV) {
+      // a moved reference of a head's owner travels in the sign bits of
+      // tokens 0..7 of its P row: decode, clear, rescale that head's columns
       uint32_t flag = 0;
 #pragma unroll
       for (int ht = 0; ht < 4; ++ht) flag |= ((uint32_t)pf[ht][0] | (uint32_t)pf[ht][1]) & 0x80808080u;
@@ -397,55 +455,12 @@ __global__ __launch_bounds__(THREADS, 1) void k_split8(int H, int B, int q_len, 
         }
         rescale_fence();
       }
-#pragma unroll
-      for (int ct = 0; ct < 4; ++ct) {
-        uint32_t tx = o_tx[ct];
-        opq(tx);
-        const uint32_t a0 = a_tv + tx, a1 = a_tv + (tx ^ 64);
-        i32x2 r[4];
-#pragma unroll
-        for (int q = 0; q < 4; ++q) r[q] = tr8((const LDS_AS char*)(size_t)((q & 1) ? a1 : a0) + q * 8 * ROW8);
-        const i32x8 va = {r[0][0], r[0][1], r[1][0], r[1][1], r[2][0], r[2][1], r[3][0], r[3][1]};
-#pragma unroll
-        for (int ht = 0; ht < 4; ++ht) o[ct][ht] = mfma8(va, pf[ht], o[ct][ht], 127, e_prev);
-        __builtin_amdgcn_sched_barrier(0);
-      }
     }
+    // ---- softmax of page i, head h_own: tile max, reference, shift ----
+    float alpha = 1.f, lsum = 0.f;
+    uint32_t flag_bits = 0, pw = 0;
     if constexpr (QK) {
-      const uint32_t tq = slot_addr(i);
-      // copies of page dma_i: one after every second score MFMA
-      const bool dma = dma_i >= 0;
-      const char* dsrc = dma ? copy_src(dma_i) : nullptr;
-      const uint32_t ddst = dma ? copy_dst(dma_i) : 0u;
-      f32x16 sc[2];
-#pragma unroll
-      for (int rb = 0; rb < 2; ++rb) {
-        const int e_t = (int)*(const LDS_AS uint8_t*)(size_t)(tq + SCALE_OFF + 32 * rb + hl);
-        // k_pe part first (bf16), then the codes (FP8) into the same accumulator
-#pragma unroll
-        for (int s = 0; s < 4; ++s) {
-          uint32_t op = o_pe[s];
-          opq(op);
-          const bf16x8_t a = __builtin_bit_cast(bf16x8_t, r128(tq + op + rb * 32 * ROW8));
-          if (s == 0) qk16_first(sc[rb], a, qp[s]);
-          else qk16(sc[rb], a, qp[s]);
-          if (s == 1 && dma && rb * 6 + 5 < COPIES) copy_one(dsrc, ddst, rb * 6 + 5);
-          if (s == 3 && dma) copy_one(dsrc, ddst, rb * 6 + 4);
-          __builtin_amdgcn_sched_barrier(0);
-        }
-        mfma_switch(sc[rb]);
-#pragma unroll
-        for (int ks = 0; ks < 8; ++ks) {
-          uint32_t oa = o_qa[2 * (ks & 1)], ob = o_qa[2 * (ks & 1) + 1];
-          opq(oa);
-          opq(ob);
-          const uint32_t c0 = tq + rb * 32 * ROW8 + (ks >> 1) * 128;
-          qk8(sc[rb], cat8(r128(c0 + oa), r128(c0 + ob)), qf[ks], e_t, e_q);
-          if ((ks & 1) && dma) copy_one(dsrc, ddst, rb * 6 + (ks >> 1));
-          __builtin_amdgcn_sched_barrier(0);
-        }
-        score_done(sc[rb]);
-      }
+      score_done(sc[1]);
       // mask rows past the context; lane rows of half page rb: 32rb + 8(r/4) + 4g + r%4
       const int valid = t_end - (t_begin + i * PAGE);
       if (valid < PAGE) {
@@ -458,7 +473,7 @@ __global__ __launch_bounds__(THREADS, 1) void k_split8(int H, int B, int q_len, 
       // page scale: the largest scale byte of the valid tokens
       // (bit by bit from the top, one ballot per bit: no lane shuffles)
       {
-        const int ep = lane < valid ? (int)*(const LDS_AS uint8_t*)(size_t)(tq + SCALE_OFF + lane) : 0;
+        if (lane >= valid) ep = 0;
         int m = 0;
 #pragma unroll
         for (int bit = 7; bit >= 0; --bit)
@@ -477,41 +492,66 @@ __global__ __launch_bounds__(THREADS, 1) void k_split8(int H, int B, int q_len, 
       const bool first = m_run == -INFINITY;
       const bool up = !first && mx > m_run + 8.f;
       const float kf = up ? fminf(ceilf(mx - m_run), 255.f) : 0.f;
-      k_shift = (int)kf;
-      const float alpha = __builtin_amdgcn_ldexpf(1.f, -k_shift);
+      const int k_shift = (int)kf;
+      alpha = __builtin_amdgcn_ldexpf(1.f, -k_shift);
       m_run = first ? mx : m_run + kf;
       // a moved reference: bit j of the shift in the sign bit of token j's byte
       // (tokens 0..7: rb 0, a 0 of both lane halves)
-      uint32_t flag_bits = 0;
       if (__ballot(k_shift != 0)) {
 #pragma unroll
         for (int q = 0; q < 4; ++q) flag_bits |= (((uint32_t)k_shift >> (4 * g + q)) & 1u) << (8 * q + 7);
       }
-      // P' of page i, four tokens per word (32rb + 8a + 4g .. +3), published
-      // as produced into head h_own's row of the P buffer
-      const uint32_t pw = pb_addr(i);
-      float lsum = 0.f;
-#pragma unroll
-      for (int rb = 0; rb < 2; ++rb)
-#pragma unroll
-        for (int a = 0; a < 4; ++a) {
-          const uint32_t ew = *(const LDS_AS uint32_t*)(size_t)(tq + SCALE_OFF + 4 * g + 32 * rb + 8 * a);
-          float pv[4];
-#pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            const float p = __builtin_amdgcn_exp2f(sc[rb][4 * a + q] - m_run);
-            lsum += p;
-            pv[q] = __builtin_amdgcn_ldexpf(p, (int)((ew >> (8 * q)) & 0xFFu) - e_page);
-          }
-          int wv = __builtin_amdgcn_cvt_pk_fp8_f32(pv[0], pv[1], 0, false);
-          wv = __builtin_amdgcn_cvt_pk_fp8_f32(pv[2], pv[3], wv, true);
-          if (rb == 0 && a == 0) wv |= (int)flag_bits;
-          uint32_t ow = o_pw[2 * rb + (a >> 1)];
-          opq(ow);
-          *(LDS_AS int*)(size_t)(pw + ow + 8 * (a & 1)) = wv;
-        }
-      l_run = l_run * alpha + lsum;
+      pw = pb_addr(i);
     }
+    // P' of page i for tokens 32rb + 8a + 4g .. +3 (group 4rb + a), published
+    // as produced into head h_own's row of the P buffer
+    auto p_group = [&](int grp) {
+      const int rb = grp >> 2, a = grp & 3;
+      float pv[4];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const float p = __builtin_amdgcn_exp2f(sc[rb][4 * a + q] - m_run);
+        lsum += p;
+        pv[q] = __builtin_amdgcn_ldexpf(p, (int)((ew[grp] >> (8 * q)) & 0xFFu) - e_page);
+      }
+      int wv = __builtin_amdgcn_cvt_pk_fp8_f32(pv[0], pv[1], 0, false);
+      wv = __builtin_amdgcn_cvt_pk_fp8_f32(pv[2], pv[3], wv, true);
+      if (grp == 0) wv |= (int)flag_bits;
+      uint32_t ow = o_pw[2 * rb + (a >> 1)];
+      opq(ow);
+      *(LDS_AS int*)(size_t)(pw + ow + 8 * (a & 1)) = wv;
+    };
+    if constexpr (PV) {
+      uint32_t a_tv = o_tv;
+      opq(a_tv);
+      a_tv += tv;
+      auto va_read = [&](int ct) {
+        uint32_t tx = o_tx[ct];
+        opq(tx);
+        const uint32_t a0 = a_tv + tx, a1 = a_tv + (tx ^ 64);
+        i32x2 r[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) r[q] = tr8((const LDS_AS char*)(size_t)((q & 1) ? a1 : a0) + q * 8 * ROW8);
+        return (i32x8){r[0][0], r[0][1], r[1][0], r[1][1], r[2][0], r[2][1], r[3][0], r[3][1]};
+      };
+      i32x8 va[2];
+      va[0] = va_read(0);
+#pragma unroll
+      for (int ct = 0; ct < 4; ++ct) {
+        if (ct + 1 < 4) va[(ct + 1) & 1] = va_read(ct + 1);
+#pragma unroll
+        for (int ht = 0; ht < 4; ++ht) o[ct][ht] = mfma8(va[ct & 1], pf[ht], o[ct][ht], 127, e_prev);
+        if constexpr (QK) {
+          p_group(2 * ct);
+          p_group(2 * ct + 1);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    } else if constexpr (QK) {
+#pragma unroll
+      for (int grp = 0; grp < 8; ++grp) p_group(grp);
+    }
+    if constexpr (QK) l_run = l_run * alpha + lsum;
   };
 
   using T = std::true_type;

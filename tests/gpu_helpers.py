@@ -49,6 +49,7 @@ def assert_parity(got, ref, dtype, what=""):
     max_abs, rel_bar, peak_bar = bar(dtype)
     rel = np.linalg.norm(got - ref) / max(np.linalg.norm(ref), 1e-30)
     msg = f"{what}: max|d|={d.max():.3e} rel={rel:.3e} max|ref|={np.abs(ref).max():.3e}"
+    print(f"[parity] {msg}", flush=True)
     assert d.max() <= max_abs, msg
     assert rel <= rel_bar, msg
     assert d.max() <= peak_bar * np.abs(ref).max(), msg
