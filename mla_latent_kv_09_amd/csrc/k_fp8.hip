@@ -357,26 +357,57 @@ __global__ __launch_bounds__(THREADS, 1) void k_split8(int H, int B, int q_len, 
 
   int e_page = 127;  // of the page in the score step
 
-  // ---- one pipeline step: scores of page i (the copies of page dma_i spread
-  // over them), then the value product of page i - 1 with the softmax of page
-  // i between its MFMAs (the two are independent) ----
+  // ---- one pipeline step. Scores of page i (24 MFMAs, their operands read
+  // two ahead, the copies of page dma_i after every second), then the
+  // softmax of page i. The value product of page i - 1 (16 MFMAs) is spread
+  // over both: one after every third score MFMA and one per softmax group, so
+  // that the score operands' LDS reads (40 KB per wave and page) overlap
+  // MFMAs that read little. ----
   auto step = [&](auto do_qk, auto do_pv, int i, int dma_i) {
     constexpr bool QK = decltype(do_qk)::value, PV = decltype(do_pv)::value;
     const uint32_t tq = slot_addr(i), tv = slot_addr(i - 1);
-    // P fragments of page i - 1: head 32ht + hl, tokens 32g .. 32g+31 (read
-    // first: the score MFMAs cover their latency)
+    // P fragments of page i - 1: head 32ht + hl, tokens 32g .. 32g+31
     i32x8 pf[4];
     if constexpr (PV) {
       const uint32_t pb = pb_addr(i - 1);
-      uint32_t a_pr0 = o_pr[0], a_pr1 = o_pr[1];
+      uint32_t a_pr0 = pb + o_pr[0], a_pr1 = pb + o_pr[1];
       opq(a_pr0);
       opq(a_pr1);
 #pragma unroll
-      for (int ht = 0; ht < 4; ++ht) pf[ht] = cat8(r128(pb + a_pr0 + 2048 * ht), r128(pb + a_pr1 + 2048 * ht));
+      for (int ht = 0; ht < 4; ++ht) pf[ht] = cat8(r128(a_pr0 + 2048 * ht), r128(a_pr1 + 2048 * ht));
     }
     f32x16 sc[2];
     int e_t[2] = {0, 0}, ep = 0;
     uint32_t ew[8];  // scale bytes of this lane's tokens 32rb + 8a + 4g .. +3, as [4rb + a]
+    constexpr int AHEAD = 2;
+    u32x4 fa[AHEAD][2];
+    // score operand op: half page rb = op / 12; k = op % 12 < 4: k_pe step k
+    // (bf16, 16 bytes), else code step k - 4 (FP8, 32 bytes)
+    // lane bases of this step's accesses, formed once (opaque to the
+    // compiler, so it neither re-forms them per access nor keeps one register
+    // per access across the page loop); the rest of each address is an
+    // instruction immediate
+    uint32_t b_qa[4], b_pe[4];
+    if constexpr (QK) {
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        b_qa[u] = tq + o_qa[u];
+        opq(b_qa[u]);
+        b_pe[u] = tq + o_pe[u];
+        opq(b_pe[u]);
+      }
+    }
+    auto a_read = [&](int op, u32x4 (&f)[2]) {
+      const int rb = op / 12, k = op % 12;
+      if (k < 4) {
+        f[0] = r128(b_pe[k] + rb * 32 * ROW8);
+      } else {
+        const int ks = k - 4;
+        const uint32_t imm = rb * 32 * ROW8 + (ks >> 1) * 128;
+        f[0] = r128(b_qa[2 * (ks & 1)] + imm);
+        f[1] = r128(b_qa[2 * (ks & 1) + 1] + imm);
+      }
+    };
     if constexpr (QK) {
       // scale bytes, read ahead of their use: the score rows', this lane's
       // tokens', and one per lane for the page scale
@@ -386,51 +417,29 @@ __global__ __launch_bounds__(THREADS, 1) void k_split8(int H, int B, int q_len, 
 #pragma unroll
       for (int k = 0; k < 8; ++k)
         ew[k] = *(const LDS_AS uint32_t*)(size_t)(tq + SCALE_OFF + 4 * g + 32 * (k >> 2) + 8 * (k & 3));
-      const bool dma = dma_i >= 0;
-      const char* dsrc = dma ? copy_src(dma_i) : nullptr;
-      const uint32_t ddst = dma ? copy_dst(dma_i) : 0u;
-      // 24 score MFMAs: per half page rb, 4 over k_pe (bf16, operand op 12rb + s)
-      // then 8 over the codes (FP8, op 12rb + 4 + ks), one accumulator per half
-      // page. Operands are read AHEAD MFMAs before their use.
-      auto a_read = [&](int op, u32x4 (&f)[2]) {
-        const int rb = op / 12, k = op % 12;
-        if (k < 4) {
-          uint32_t o1 = o_pe[k];
-          opq(o1);
-          f[0] = r128(tq + o1 + rb * 32 * ROW8);
-        } else {
-          const int ks = k - 4;
-          uint32_t oa = o_qa[2 * (ks & 1)], ob = o_qa[2 * (ks & 1) + 1];
-          opq(oa);
-          opq(ob);
-          const uint32_t c0 = tq + rb * 32 * ROW8 + (ks >> 1) * 128;
-          f[0] = r128(c0 + oa);
-          f[1] = r128(c0 + ob);
-        }
-      };
-      constexpr int AHEAD = 2;
-      u32x4 fa[AHEAD][2];
 #pragma unroll
       for (int op = 0; op < AHEAD; ++op) a_read(op, fa[op]);
+    }
+    // value operand of column tile ct: four transposing reads of 8 rows each
+    uint32_t b_tv[4][2];  // [column tile][read parity]
+    if constexpr (PV) {
 #pragma unroll
-      for (int op = 0; op < 24; ++op) {
-        const int rb = op / 12, k = op % 12;
-        const u32x4 f0 = fa[op % AHEAD][0], f1 = fa[op % AHEAD][1];
-        if (op + AHEAD < 24) a_read(op + AHEAD, fa[op % AHEAD]);
-        if (k < 4) {
-          const bf16x8_t a = __builtin_bit_cast(bf16x8_t, f0);
-          if (k == 0) qk16_first(sc[rb], a, qp[k]);
-          else qk16(sc[rb], a, qp[k]);
-          if (k == 3) mfma_switch(sc[rb]);
-        } else {
-          qk8(sc[rb], cat8(f0, f1), qf[k - 4], e_t[rb], e_q);
-        }
-        // copies: after ops 1, 3, 5, ... (11 of them)
-        if ((op & 1) && dma && (op >> 1) < COPIES) copy_one(dsrc, ddst, op >> 1);
-        __builtin_amdgcn_sched_barrier(0);
+      for (int ct = 0; ct < 4; ++ct) {
+        b_tv[ct][0] = tv + o_tv + o_tx[ct];
+        b_tv[ct][1] = tv + o_tv + (o_tx[ct] ^ 64);
+        opq(b_tv[ct][0]);
+        opq(b_tv[ct][1]);
       }
     }
+    auto va_read = [&](int ct) {
+      i32x2 r[4];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) r[q] = tr8((const LDS_AS char*)(size_t)(b_tv[ct][q & 1] + q * 8 * ROW8));
+      return (i32x8){r[0][0], r[0][1], r[1][0], r[1][1], r[2][0], r[2][1], r[3][0], r[3][1]};
+    };
+    i32x8 va[2];
     if constexpr (PV) {
+      va[0] = va_read(0);
       // a moved reference of a head's owner travels in the sign bits of
       // tokens 0..7 of its P row: decode, clear, rescale that head's columns
       uint32_t flag = 0;
@@ -454,6 +463,38 @@ __global__ __launch_bounds__(THREADS, 1) void k_split8(int H, int B, int q_len, 
           pf[ht][1] = (int)((uint32_t)pf[ht][1] & 0x7F7F7F7Fu);
         }
         rescale_fence();
+      }
+    }
+    // value MFMA m of 16: column tile m / 4, head tile m % 4; the next column
+    // tile's operand is read when a tile starts
+    auto pv_mfma = [&](int m) {
+      const int ct = m >> 2, ht = m & 3;
+      if (ht == 0 && ct + 1 < 4) va[(ct + 1) & 1] = va_read(ct + 1);
+      o[ct][ht] = mfma8(va[ct & 1], pf[ht], o[ct][ht], 127, e_prev);
+    };
+    if constexpr (QK) {
+      const bool dma = dma_i >= 0;
+      const char* dsrc = dma ? copy_src(dma_i) : nullptr;
+      const uint32_t ddst = dma ? copy_dst(dma_i) : 0u;
+#pragma unroll
+      for (int op = 0; op < 24; ++op) {
+        const int rb = op / 12, k = op % 12;
+        const u32x4 f0 = fa[op % AHEAD][0], f1 = fa[op % AHEAD][1];
+        if (op + AHEAD < 24) a_read(op + AHEAD, fa[op % AHEAD]);
+        if (k < 4) {
+          const bf16x8_t a = __builtin_bit_cast(bf16x8_t, f0);
+          if (k == 0) qk16_first(sc[rb], a, qp[k]);
+          else qk16(sc[rb], a, qp[k]);
+          if (k == 3) mfma_switch(sc[rb]);
+        } else {
+          qk8(sc[rb], cat8(f0, f1), qf[k - 4], e_t[rb], e_q);
+        }
+        // copies: after ops 1, 3, 5, ... (11 of them)
+        if ((op & 1) && dma && (op >> 1) < COPIES) copy_one(dsrc, ddst, op >> 1);
+        if constexpr (PV) {
+          if (op % 3 == 2) pv_mfma(op / 3);
+        }
+        __builtin_amdgcn_sched_barrier(0);
       }
     }
     // ---- softmax of page i, head h_own: tile max, reference, shift ----
@@ -503,6 +544,14 @@ __global__ __launch_bounds__(THREADS, 1) void k_split8(int H, int B, int q_len, 
       }
       pw = pb_addr(i);
     }
+    uint32_t b_pw[4];
+    if constexpr (QK) {
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        b_pw[c] = pw + o_pw[c];
+        opq(b_pw[c]);
+      }
+    }
     // P' of page i for tokens 32rb + 8a + 4g .. +3 (group 4rb + a), published
     // as produced into head h_own's row of the P buffer
     auto p_group = [&](int grp) {
@@ -517,35 +566,20 @@ __global__ __launch_bounds__(THREADS, 1) void k_split8(int H, int B, int q_len, 
       int wv = __builtin_amdgcn_cvt_pk_fp8_f32(pv[0], pv[1], 0, false);
       wv = __builtin_amdgcn_cvt_pk_fp8_f32(pv[2], pv[3], wv, true);
       if (grp == 0) wv |= (int)flag_bits;
-      uint32_t ow = o_pw[2 * rb + (a >> 1)];
-      opq(ow);
-      *(LDS_AS int*)(size_t)(pw + ow + 8 * (a & 1)) = wv;
+      *(LDS_AS int*)(size_t)(b_pw[2 * rb + (a >> 1)] + 8 * (a & 1)) = wv;
     };
-    if constexpr (PV) {
-      uint32_t a_tv = o_tv;
-      opq(a_tv);
-      a_tv += tv;
-      auto va_read = [&](int ct) {
-        uint32_t tx = o_tx[ct];
-        opq(tx);
-        const uint32_t a0 = a_tv + tx, a1 = a_tv + (tx ^ 64);
-        i32x2 r[4];
+    if constexpr (PV && QK) {
 #pragma unroll
-        for (int q = 0; q < 4; ++q) r[q] = tr8((const LDS_AS char*)(size_t)((q & 1) ? a1 : a0) + q * 8 * ROW8);
-        return (i32x8){r[0][0], r[0][1], r[1][0], r[1][1], r[2][0], r[2][1], r[3][0], r[3][1]};
-      };
-      i32x8 va[2];
-      va[0] = va_read(0);
-#pragma unroll
-      for (int ct = 0; ct < 4; ++ct) {
-        if (ct + 1 < 4) va[(ct + 1) & 1] = va_read(ct + 1);
-#pragma unroll
-        for (int ht = 0; ht < 4; ++ht) o[ct][ht] = mfma8(va[ct & 1], pf[ht], o[ct][ht], 127, e_prev);
-        if constexpr (QK) {
-          p_group(2 * ct);
-          p_group(2 * ct + 1);
-        }
+      for (int grp = 0; grp < 8; ++grp) {
+        pv_mfma(8 + grp);
+        p_group(grp);
         __builtin_amdgcn_sched_barrier(0);
+      }
+    } else if constexpr (PV) {
+#pragma unroll
+      for (int m = 0; m < 16; ++m) {
+        pv_mfma(m);
+        if ((m & 3) == 3) __builtin_amdgcn_sched_barrier(0);
       }
     } else if constexpr (QK) {
 #pragma unroll
