@@ -44,7 +44,8 @@ constexpr int COPIES = (PAGE8_CHUNKS + THREADS - 1) / THREADS;  // 11; the last 
 constexpr int N_SLOTS = 3;
 constexpr int MAX_HEADS = 128;
 constexpr int PB_BYTES = MAX_HEADS * PAGE;  // P of one page, fp8: [head][64 tokens]
-constexpr int SPLIT8_LDS = N_SLOTS * PAGE8 + 2 * PB_BYTES;
+constexpr int KB_BYTES = MAX_HEADS;        // reference shift per head, [head % 32][head / 32]
+constexpr int SPLIT8_LDS = N_SLOTS * PAGE8 + 2 * PB_BYTES + 2 * KB_BYTES;
 static_assert(SPLIT8_LDS <= 160 * 1024, "LDS budget of one workgroup");
 constexpr int MAX_SPLITS = 256;
 
@@ -115,16 +116,19 @@ __global__ __launch_bounds__(256) void k_quant_fp8(int n, int d_c, int d_rope, c
 //            plus 4 bf16 MFMAs over k_pe. The query's codes (64 VGPRs), its
 //            bf16 k_pe slice (16) and scale byte stay in registers.
 //   softmax  log2 domain, reference max per head moved lazily by whole steps
-//            (as in the bf16 kernel). P' = P * 2^(E_t - E_page) with E_page
-//            the largest scale of the page's valid tokens, rounded to FP8.
+//            k (as in the bf16 kernel); the owner publishes k beside P, and
+//            the other waves rescale that head's columns by 2^-k (rare).
+//            P' = P * 2^(E_t - E_page) with E_page the largest scale of the
+//            page's valid tokens, rounded to FP8.
 //   values   wave w owns latent columns 128w .. 128w+127 of every head:
 //            O^T[c, h] += sum_t code[t, c] P'[t, h] * 2^(E_page - 127), one
 //            MX-scaled MFMA (K = 64 tokens) per (column tile, head tile). The
 //            value operand is read transposed from the row-major page with
 //            ds_read_b64_tr_b8.
 // Pipeline: a ring of three page slots (page i - 1 in the value step, page i
-// in the score step, page i + 1 in flight) and two P buffers; one barrier per
-// page. Partials are those of the bf16 kernel, merged by the same combine.
+// in the score step, page i + 1 in flight) and two P (and shift) buffers; one
+// barrier per page. Partials are those of the bf16 kernel, merged by the same
+// combine.
 //
 // LDS layout of a page: row t at t * 640, its 16-byte chunk j at position
 // j ^ sw(t) inside its aligned group of 8 (rows 0..15 reading one chunk then
@@ -337,6 +341,7 @@ __global__ __launch_bounds__(THREADS, 1) void k_split8(int H, int B, int q_len, 
   auto opq = [](uint32_t& v) { asm volatile("" : "+v"(v)); };
   auto slot_addr = [&](int i) { return (uint32_t)(lds_base + ((i + N_SLOTS) % N_SLOTS) * PAGE8); };
   auto pb_addr = [&](int i) { return (uint32_t)(lds_base + N_SLOTS * PAGE8 + (i & 1) * PB_BYTES); };
+  auto kb_addr = [&](int i) { return (uint32_t)(lds_base + N_SLOTS * PAGE8 + 2 * PB_BYTES + (i & 1) * KB_BYTES); };
   auto r128 = [](uint32_t a) { return *(const LDS_AS u32x4*)(size_t)a; };
 
   // rows past the context in the last page: zero their codes before the
@@ -366,7 +371,11 @@ __global__ __launch_bounds__(THREADS, 1) void k_split8(int H, int B, int q_len, 
   auto step = [&](auto do_qk, auto do_pv, int i, int dma_i) {
     constexpr bool QK = decltype(do_qk)::value, PV = decltype(do_pv)::value;
     const uint32_t tq = slot_addr(i), tv = slot_addr(i - 1);
-    // P fragments of page i - 1: head 32ht + hl, tokens 32g .. 32g+31
+    // the reference shifts of heads 32ht + hl (ht = byte), published with P
+    // of page i - 1 by the heads' owners (read first: it alone gates the
+    // rescale test), then the P fragments: head 32ht + hl, tokens 32g .. +31
+    uint32_t kword = 0;
+    if constexpr (PV) kword = *(const LDS_AS uint32_t*)(size_t)(kb_addr(i - 1) + 4 * hl);
     i32x8 pf[4];
     if constexpr (PV) {
       const uint32_t pb = pb_addr(i - 1);
@@ -438,33 +447,21 @@ __global__ __launch_bounds__(THREADS, 1) void k_split8(int H, int B, int q_len, 
       return (i32x8){r[0][0], r[0][1], r[1][0], r[1][1], r[2][0], r[2][1], r[3][0], r[3][1]};
     };
     i32x8 va[2];
-    if constexpr (PV) {
-      va[0] = va_read(0);
-      // a moved reference of a head's owner travels in the sign bits of
-      // tokens 0..7 of its P row: decode, clear, rescale that head's columns
-      uint32_t flag = 0;
-#pragma unroll
-      for (int ht = 0; ht < 4; ++ht) flag |= ((uint32_t)pf[ht][0] | (uint32_t)pf[ht][1]) & 0x80808080u;
-      if (__ballot(flag != 0)) {
+    if constexpr (PV) va[0] = va_read(0);
+    // a head's owner moved its reference by k: rescale that head's columns
+    // by 2^-k (rare)
+    auto p_flags = [&]() {
+      if (__ballot(kword != 0)) {
         rescale_fence();
 #pragma unroll
         for (int ht = 0; ht < 4; ++ht) {
-          int kk = 0;
-#pragma unroll
-          for (int j = 0; j < 8; ++j) kk |= (int)(((uint32_t)pf[ht][j >> 2] >> (8 * (j & 3) + 7)) & 1u) << j;
-          // lanes g = 1 hold tokens 32..63 (no flag bits): the swap hands every
-          // lane its own value and its partner's, and the OR keeps the flagged one
-          const auto pr = __builtin_amdgcn_permlane32_swap((uint32_t)kk, (uint32_t)kk, false, false);
-          kk = (int)(pr[0] | pr[1]);
-          const float al = __builtin_amdgcn_ldexpf(1.f, -kk);
+          const float al = __builtin_amdgcn_ldexpf(1.f, -(int)((kword >> (8 * ht)) & 0xFFu));
 #pragma unroll
           for (int ct = 0; ct < 4; ++ct) scale_tile(o[ct][ht], al);
-          pf[ht][0] = (int)((uint32_t)pf[ht][0] & 0x7F7F7F7Fu);
-          pf[ht][1] = (int)((uint32_t)pf[ht][1] & 0x7F7F7F7Fu);
         }
         rescale_fence();
       }
-    }
+    };
     // value MFMA m of 16: column tile m / 4, head tile m % 4; the next column
     // tile's operand is read when a tile starts
     auto pv_mfma = [&](int m) {
@@ -472,6 +469,7 @@ __global__ __launch_bounds__(THREADS, 1) void k_split8(int H, int B, int q_len, 
       if (ht == 0 && ct + 1 < 4) va[(ct + 1) & 1] = va_read(ct + 1);
       o[ct][ht] = mfma8(va[ct & 1], pf[ht], o[ct][ht], 127, e_prev);
     };
+    if constexpr (PV && QK) p_flags();
     if constexpr (QK) {
       const bool dma = dma_i >= 0;
       const char* dsrc = dma ? copy_src(dma_i) : nullptr;
@@ -498,8 +496,8 @@ __global__ __launch_bounds__(THREADS, 1) void k_split8(int H, int B, int q_len, 
       }
     }
     // ---- softmax of page i, head h_own: tile max, reference, shift ----
-    float alpha = 1.f, lsum = 0.f;
-    uint32_t flag_bits = 0, pw = 0;
+    float alpha = 1.f, lsum2[2] = {0.f, 0.f};
+    uint32_t pw = 0;
     if constexpr (QK) {
       score_done(sc[1]);
       // mask rows past the context; lane rows of half page rb: 32rb + 8(r/4) + 4g + r%4
@@ -536,12 +534,8 @@ __global__ __launch_bounds__(THREADS, 1) void k_split8(int H, int B, int q_len, 
       const int k_shift = (int)kf;
       alpha = __builtin_amdgcn_ldexpf(1.f, -k_shift);
       m_run = first ? mx : m_run + kf;
-      // a moved reference: bit j of the shift in the sign bit of token j's byte
-      // (tokens 0..7: rb 0, a 0 of both lane halves)
-      if (__ballot(k_shift != 0)) {
-#pragma unroll
-        for (int q = 0; q < 4; ++q) flag_bits |= (((uint32_t)k_shift >> (4 * g + q)) & 1u) << (8 * q + 7);
-      }
+      // the shift goes to the other waves beside P
+      if (g == 0) *(LDS_AS uint8_t*)(size_t)(kb_addr(i) + 4 * hl + w) = (uint8_t)k_shift;
       pw = pb_addr(i);
     }
     uint32_t b_pw[4];
@@ -556,16 +550,17 @@ __global__ __launch_bounds__(THREADS, 1) void k_split8(int H, int B, int q_len, 
     // as produced into head h_own's row of the P buffer
     auto p_group = [&](int grp) {
       const int rb = grp >> 2, a = grp & 3;
-      float pv[4];
+      float p[4], pv[4];
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
-        const float p = __builtin_amdgcn_exp2f(sc[rb][4 * a + q] - m_run);
-        lsum += p;
-        pv[q] = __builtin_amdgcn_ldexpf(p, (int)((ew[grp] >> (8 * q)) & 0xFFu) - e_page);
+        p[q] = __builtin_amdgcn_exp2f(sc[rb][4 * a + q] - m_run);
+        pv[q] = __builtin_amdgcn_ldexpf(p[q], (int)((ew[grp] >> (8 * q)) & 0xFFu) - e_page);
       }
-      int wv = __builtin_amdgcn_cvt_pk_fp8_f32(pv[0], pv[1], 0, false);
+      // row sum: a short tree per group, two running sums (no long serial chain)
+      lsum2[grp & 1] += (p[0] + p[1]) + (p[2] + p[3]);
+      // (the first conversion's upper half is overwritten by the second)
+      int wv = __builtin_amdgcn_cvt_pk_fp8_f32(pv[0], pv[1], (int)ew[grp], false);
       wv = __builtin_amdgcn_cvt_pk_fp8_f32(pv[2], pv[3], wv, true);
-      if (grp == 0) wv |= (int)flag_bits;
       *(LDS_AS int*)(size_t)(b_pw[2 * rb + (a >> 1)] + 8 * (a & 1)) = wv;
     };
     if constexpr (PV && QK) {
@@ -576,6 +571,7 @@ __global__ __launch_bounds__(THREADS, 1) void k_split8(int H, int B, int q_len, 
         __builtin_amdgcn_sched_barrier(0);
       }
     } else if constexpr (PV) {
+      p_flags();
 #pragma unroll
       for (int m = 0; m < 16; ++m) {
         pv_mfma(m);
@@ -585,7 +581,7 @@ __global__ __launch_bounds__(THREADS, 1) void k_split8(int H, int B, int q_len, 
 #pragma unroll
       for (int grp = 0; grp < 8; ++grp) p_group(grp);
     }
-    if constexpr (QK) l_run = l_run * alpha + lsum;
+    if constexpr (QK) l_run = l_run * alpha + (lsum2[0] + lsum2[1]);
   };
 
   using T = std::true_type;
