@@ -238,12 +238,13 @@ __global__ __launch_bounds__(256) void k_absorb(int B, int H, int q_len, const b
       *(bf16x4_t*)&ot[(16 * t + i16) * LDO + 16 * w + 4 * G] = v;
     }
     __syncthreads();
-    // 64 rows of 128 bytes: 8 lanes per row, 16 bytes each
+    // 16 * BT_CHUNK rows of 128 bytes: 8 lanes per row, 16 bytes each
 #pragma unroll
-    for (int rr = 0; rr < 16 * BT_CHUNK / 32; ++rr) {
+    for (int rr = 0; rr < (16 * BT_CHUNK + 31) / 32; ++rr) {
       const int r = 32 * rr + (threadIdx.x >> 3), ch = threadIdx.x & 7;
       const int b = bt0 * 16 + r;
-      if (b < B) *(u32x4*)(qt + ((size_t)b * H + h) * ROW + c0 + 8 * ch) = *(const u32x4*)&ot[r * LDO + 8 * ch];
+      if (r < 16 * BT_CHUNK && b < B)
+        *(u32x4*)(qt + ((size_t)b * H + h) * ROW + c0 + 8 * ch) = *(const u32x4*)&ot[r * LDO + 8 * ch];
     }
   }
   // the rotated, scaled q_pe slice: reduce the angle to [-pi, pi] in double,
