@@ -111,7 +111,7 @@ struct Plan {
 Plan plan_splits(int batch, int max_context, int q_len) {
   const int max_pages = (max_context + PAGE - 1) / PAGE;
   // aim for one workgroup per compute unit across the batch, 4..32 pages each;
-  // with several rows per sequence up to 64, which halves the fp32 partials
+  // with several rows per sequence up to 64, which halves the partials
   // (one per row and run) where the rows alone fill the chip
   const int cap = q_len > 1 ? 64 : 32;
   int pps = (int)(((int64_t)batch * max_pages + 255) / 256);
@@ -134,7 +134,7 @@ WsLayout ws_layout(int H, int batch, int splits) {
   WsLayout l;
   l.qt = 0;
   l.part_o = align256((size_t)batch * H * ROW * 2);
-  l.part_ml = l.part_o + align256((size_t)H * batch * splits * DC * 4);
+  l.part_ml = l.part_o + align256((size_t)H * batch * splits * DC * 2);
   l.total = l.part_ml + align256((size_t)H * batch * splits * 2 * 4);
   return l;
 }
@@ -295,8 +295,10 @@ __global__ __launch_bounds__(256) void k_absorb(int B, int H, int q_len, const b
 // otherwise clear); the readers test them, and in the rare case decode k,
 // clear the bits and rescale.
 //
-// Partials per (head, sequence, split): O (512 fp32, unnormalised, relative to
-// the head's reference max m) and (m, l), both in the log2 domain.
+// Partials per (head, sequence, split): O (512 values, unnormalised, relative
+// to the head's reference max m; accumulated in fp32, stored as bf16, which
+// halves the partials' HBM traffic for one bf16 rounding of each partial) and
+// (m, l) in fp32, both in the log2 domain.
 constexpr int TILE = 32;                                  // rows per tile
 constexpr int TILE_BYTES = TILE * ROW_BYTES;              // 36864
 constexpr int TILE_LOADS = TILE * ROW_CHUNKS / SPLIT_THREADS;  // 9 per lane
@@ -356,7 +358,7 @@ __global__ __launch_bounds__(SPLIT_THREADS, 1) void k_split(int H, int B, int q_
                                                             const bf16* __restrict__ rows,
                                                             const int32_t* __restrict__ block_table,
                                                             int max_blocks, const int32_t* __restrict__ ctx_lens,
-                                                            float* __restrict__ part_o, float* __restrict__ part_ml) {
+                                                            bf16* __restrict__ part_o, float* __restrict__ part_ml) {
   __shared__ __attribute__((aligned(1024))) char lds[SPLIT_LDS];
   // b is the query row (sequence b / q_len, new token b % q_len)
   int split = blockIdx.x, b = blockIdx.y;
@@ -719,12 +721,17 @@ __global__ __launch_bounds__(SPLIT_THREADS, 1) void k_split(int H, int B, int q_
         *(LDS_AS f32x4*)(ost + hl * OP + 128 * w + 32 * ct + 8 * q + 4 * g) = v;
       }
     lds_barrier();
+    // rows of 512 values as bf16: 64 lanes per row, 8 values (16 bytes) each
 #pragma unroll
-    for (int k = 0; k < 16; ++k) {
-      const int row = 2 * k + (threadIdx.x >> 7), c4 = threadIdx.x & 127, hh = 32 * ht + row;
-      if (hh < H)
-        *(f32x4*)(part_o + (((size_t)hh * B + b) * splits + split) * DC + 4 * c4) =
-            *(const LDS_AS f32x4*)(ost + row * OP + 4 * c4);
+    for (int k = 0; k < 8; ++k) {
+      const int row = 4 * k + (threadIdx.x >> 6), c8 = threadIdx.x & 63, hh = 32 * ht + row;
+      if (hh < H) {
+        const f32x4 x = *(const LDS_AS f32x4*)(ost + row * OP + 8 * c8);
+        const f32x4 y = *(const LDS_AS f32x4*)(ost + row * OP + 8 * c8 + 4);
+        *(bf16x8_t*)(part_o + (((size_t)hh * B + b) * splits + split) * DC + 8 * c8) =
+            (bf16x8_t){(__bf16)x[0], (__bf16)x[1], (__bf16)x[2], (__bf16)x[3],
+                       (__bf16)y[0], (__bf16)y[1], (__bf16)y[2], (__bf16)y[3]};
+      }
     }
   }
 }
@@ -740,7 +747,7 @@ __global__ __launch_bounds__(SPLIT_THREADS, 1) void k_split(int H, int B, int q_
 //      with 4 consecutive outputs of one sequence (one 8-byte store)
 __global__ __launch_bounds__(256) void k_combine_uv(int H, int B, int q_len, int splits, int pps,
                                                     const int32_t* __restrict__ ctx_lens,
-                                                    const float* __restrict__ part_o,
+                                                    const bf16* __restrict__ part_o,
                                                     const float* __restrict__ part_ml,
                                                     const bf16* __restrict__ w_uv, bf16* __restrict__ out) {
   constexpr int LDO = DC + 8;
@@ -791,36 +798,41 @@ __global__ __launch_bounds__(256) void k_combine_uv(int H, int B, int q_len, int
   }
   __syncthreads();
   {
-    const int r = tid >> 4, q = tid & 15, b = b0 + r;  // 16 threads per sequence, 8 float4 each
-    f32x4 acc[8] = {};
+    // 16 threads per sequence; thread q takes columns 8q + 128u .. +7 (u < 4)
+    const int r = tid >> 4, q = tid & 15, b = b0 + r;
+    float acc[4][8] = {};
     if (b < B) {
-      const float* po = part_o + ((size_t)h * B + b) * splits * DC + 4 * q;
+      const bf16* po = part_o + ((size_t)h * B + b) * splits * DC + 8 * q;
       // two splits' loads in flight per step; splits past the context were
       // never written, so their (arbitrary) values are selected away, not scaled
       for (int s = 0; s < splits; s += 2) {
-        f32x4 v[2][8];
+        u32x4 v[2][4];
 #pragma unroll
         for (int d = 0; d < 2; ++d)
 #pragma unroll
-          for (int u = 0; u < 8; ++u)
-            v[d][u] = s + d < splits ? *(const f32x4*)(po + (size_t)(s + d) * DC + 64 * u) : (f32x4){0, 0, 0, 0};
+          for (int u = 0; u < 4; ++u)
+            v[d][u] = s + d < splits ? *(const u32x4*)(po + (size_t)(s + d) * DC + 128 * u) : (u32x4){0, 0, 0, 0};
 #pragma unroll
         for (int d = 0; d < 2; ++d) {
           const float e = s + d < splits ? wgt[r][s + d] : 0.f;
 #pragma unroll
-          for (int u = 0; u < 8; ++u)
+          for (int u = 0; u < 4; ++u)
 #pragma unroll
-            for (int x = 0; x < 4; ++x) acc[u][x] += e != 0.f ? e * v[d][u][x] : 0.f;
+            for (int x = 0; x < 4; ++x) {
+              const float lo = __uint_as_float(v[d][u][x] << 16), hi = __uint_as_float(v[d][u][x] & 0xFFFF0000u);
+              acc[u][2 * x] += e != 0.f ? e * lo : 0.f;
+              acc[u][2 * x + 1] += e != 0.f ? e * hi : 0.f;
+            }
         }
       }
     }
     const float il = inv_l[r];
 #pragma unroll
-    for (int u = 0; u < 8; ++u) {
-      typedef __attribute__((ext_vector_type(4))) __bf16 bf16x4_t;
-      const bf16x4_t v = {(__bf16)(acc[u][0] * il), (__bf16)(acc[u][1] * il), (__bf16)(acc[u][2] * il),
-                          (__bf16)(acc[u][3] * il)};
-      *(bf16x4_t*)&oc[r * LDO + 4 * q + 64 * u] = v;
+    for (int u = 0; u < 4; ++u) {
+      bf16x8_t v;
+#pragma unroll
+      for (int x = 0; x < 8; ++x) v[x] = (__bf16)(acc[u][x] * il);
+      *(bf16x8_t*)&oc[r * LDO + 8 * q + 128 * u] = v;
     }
   }
   __syncthreads();
@@ -870,14 +882,14 @@ hipError_t decode_absorb(const mla_dims& d, float scale, int rows, int q_len, co
 }
 
 hipError_t decode_combine(const mla_dims& d, int rows, int q_len, int splits, int pps, const int32_t* ctx_lens,
-                          const float* part_o, const float* part_ml, const void* w_uv, void* out,
+                          const void* part_o, const float* part_ml, const void* w_uv, void* out,
                           const char* prof_name, hipStream_t s) {
   const int H = d.n_heads;
   const int nbt = (rows + 15) / 16;
   const int hpad = (H + 7) / 8 * 8;
   ProfScope ps(prof_name, s);
-  hipLaunchKernelGGL(k_combine_uv, dim3(hpad * nbt), dim3(256), 0, s, H, rows, q_len, splits, pps, ctx_lens, part_o,
-                     part_ml, (const bf16*)w_uv, (bf16*)out);
+  hipLaunchKernelGGL(k_combine_uv, dim3(hpad * nbt), dim3(256), 0, s, H, rows, q_len, splits, pps, ctx_lens,
+                     (const bf16*)part_o, part_ml, (const bf16*)w_uv, (bf16*)out);
   return hipGetLastError();
 }
 
@@ -901,7 +913,7 @@ hipError_t decode_fast(const mla_dims& d, float scale, int n_seq, int q_len, int
   if (ws_bytes < l.total) return hipErrorInvalidValue;
   char* base = (char*)ws;
   bf16* qt = (bf16*)(base + l.qt);
-  float* part_o = (float*)(base + l.part_o);
+  bf16* part_o = (bf16*)(base + l.part_o);
   float* part_ml = (float*)(base + l.part_ml);
 
   hipError_t e = decode_absorb(d, scale, batch, q_len, q_nope, q_pe, w_uk, c.context_lens, qt, "mla_decode_absorb", s);

@@ -217,7 +217,7 @@ __global__ __launch_bounds__(THREADS, 1) void k_split8(int H, int B, int q_len, 
                                                        const uint8_t* __restrict__ pages,
                                                        const int32_t* __restrict__ block_table, int max_blocks,
                                                        const int32_t* __restrict__ ctx_lens,
-                                                       float* __restrict__ part_o, float* __restrict__ part_ml) {
+                                                       bf16* __restrict__ part_o, float* __restrict__ part_ml) {
   __shared__ __attribute__((aligned(1024))) char lds[SPLIT8_LDS];
   int split = blockIdx.x, b = blockIdx.y;
   if (pair_xcd) {
@@ -626,11 +626,14 @@ __global__ __launch_bounds__(THREADS, 1) void k_split8(int H, int B, int q_len, 
 #pragma unroll
     for (int rr = 0; rr < 8; ++rr) {
       const int hh = rr * 4 + w, h = 32 * ht + hh;
-      if (h < H)
-#pragma unroll
-        for (int c4 = lane; c4 < DC / 4; c4 += 64)
-          *(f32x4*)(part_o + (((size_t)h * B + b) * splits + split) * DC + 4 * c4) =
-              *(const LDS_AS f32x4*)(ost + hh * OP + 4 * c4);
+      if (h < H) {
+        // 512 values as bf16: 8 per lane
+        const f32x4 x = *(const LDS_AS f32x4*)(ost + hh * OP + 8 * lane);
+        const f32x4 y = *(const LDS_AS f32x4*)(ost + hh * OP + 8 * lane + 4);
+        *(bf16x8_t*)(part_o + (((size_t)h * B + b) * splits + split) * DC + 8 * lane) =
+            (bf16x8_t){(__bf16)x[0], (__bf16)x[1], (__bf16)x[2], (__bf16)x[3],
+                       (__bf16)y[0], (__bf16)y[1], (__bf16)y[2], (__bf16)y[3]};
+      }
     }
   }
 }
@@ -666,7 +669,7 @@ Ws8 ws8_layout(int H, int rows, int q_len, int max_context) {
   l.qt = 0;
   l.qt8 = al256((size_t)rows * H * (DC + DR) * 2);
   l.part_o = l.qt8 + al256((size_t)rows * l.q_page);
-  l.part_ml = l.part_o + al256((size_t)H * rows * l.splits * DC * 4);
+  l.part_ml = l.part_o + al256((size_t)H * rows * l.splits * DC * 2);
   l.total = l.part_ml + al256((size_t)H * rows * l.splits * 2 * 4);
   return l;
 }
@@ -685,7 +688,7 @@ hipError_t decode_fp8(const mla_dims& d, float scale, int n_seq, int q_len, int 
   char* base = (char*)ws;
   void* qt = base + l.qt;
   uint8_t* qt8 = (uint8_t*)(base + l.qt8);
-  float* part_o = (float*)(base + l.part_o);
+  bf16* part_o = (bf16*)(base + l.part_o);
   float* part_ml = (float*)(base + l.part_ml);
   hipError_t e = decode_absorb(d, scale, rows, q_len, q_nope, q_pe, w_uk, c.context_lens, qt, "mla_decode8_absorb", s);
   if (e != hipSuccess) return e;

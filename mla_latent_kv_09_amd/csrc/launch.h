@@ -61,13 +61,13 @@ hipError_t decode_fast(const mla_dims& d, float scale, int n_seq, int q_len, int
 
 // Pieces of the decode path that the FP8-cache decode shares (rows = query
 // rows, n_seq * q_len). decode_absorb writes q~ [rows, H, 576] bf16;
-// decode_combine merges per-split partials [H][rows][splits][512] fp32 and
+// decode_combine merges per-split partials [H][rows][splits][512] bf16 and
 // (m, l) [H][rows][splits][2] and applies W_UV.
 void decode_plan(int rows, int max_context, int q_len, int* pages_per_split, int* splits);
 hipError_t decode_absorb(const mla_dims& d, float scale, int rows, int q_len, const void* q_nope, const void* q_pe,
                          const void* w_uk, const int32_t* ctx_lens, void* qt, const char* prof_name, hipStream_t s);
 hipError_t decode_combine(const mla_dims& d, int rows, int q_len, int splits, int pps, const int32_t* ctx_lens,
-                          const float* part_o, const float* part_ml, const void* w_uv, void* out,
+                          const void* part_o, const float* part_ml, const void* w_uv, void* out,
                           const char* prof_name, hipStream_t s);
 
 // ---- FP8 latent cache (E4M3 codes, one power-of-two scale per token) ------
