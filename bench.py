@@ -16,6 +16,11 @@ FP8 copy of its cache (mla_decode_fp8), quantised on the GPU before timing.
 Prefill (workload 5): one step is mla_rope_latent_project (latent rows into
 the cache, query path) followed by causal mla_prefill.
 
+By default the decode workloads run 200 untimed steps and then time 300, so
+that the timed region sees the chip's settled clock (it takes about 100 decode
+steps to settle); prefill runs 10 + 50. Explicit --warmup / --steps are used
+as given.
+
 Prints one JSON line with the throughput, the roofline position of the
 dominant kernel (timed with HIP events recorded around each library launch
 during the timed region; HBM traffic from the committed counter summary when

@@ -1,0 +1,31 @@
+"""Host-side checks of bench.py's command line: the default warm-up and timed
+step counts per workload, explicit values taken as given, and the one-GPU
+guard."""
+import subprocess
+import sys
+
+import pytest
+
+import bench
+
+
+def _parse(argv, monkeypatch):
+    monkeypatch.setattr(sys, "argv", ["bench.py", *argv])
+    return bench.parse()
+
+
+@pytest.mark.parametrize("workload,steps,warmup", [(3, 300, 200), (6, 300, 200), (7, 300, 200), (5, 50, 10)])
+def test_default_steps_per_workload(workload, steps, warmup, monkeypatch):
+    a = _parse(["--workload", str(workload)], monkeypatch)
+    assert (a.steps, a.warmup) == (steps, warmup)
+
+
+def test_explicit_steps_are_used_as_given(monkeypatch):
+    a = _parse(["--steps", "7", "--warmup", "0"], monkeypatch)
+    assert (a.steps, a.warmup, a.gpus, a.workload) == (7, 0, 1, 3)
+
+
+def test_more_than_one_gpu_is_refused():
+    r = subprocess.run([sys.executable, "bench.py", "--gpus", "2"], capture_output=True, text=True,
+                       cwd=bench.os.path.dirname(bench.os.path.abspath(bench.__file__)), timeout=120)
+    assert r.returncode == 2 and "one GPU only" in r.stderr
