@@ -112,6 +112,13 @@ def source_digest(rel):
         return hashlib.sha256(f.read()).hexdigest()
 
 
+def split_traffic_name(split_name, batch, q_len, heads, max_context, fp8):
+    """Name of the counter summary (profiles/<name>_hbm_traffic.md) of a
+    decode workload's split kernel."""
+    q = "" if q_len == 1 else f"_Q{q_len}"
+    return f"{split_name}_B{batch}{q}_H{heads}_L{max_context}" + ("_fp8" if fp8 else "")
+
+
 def measured_traffic(name, source):
     """HBM bytes per launch of a kernel from its committed counter summary
     (profiles/<name>_hbm_traffic.md): FETCH_SIZE and WRITE_SIZE (KiB per
@@ -411,8 +418,7 @@ def main():
                 "frac": round(achieved / HBM_PEAK_GBS, 4)}
         rule = {"algorithmic_bytes": cache_bytes,
                 "bytes_rule": f"{row_bytes} B per cached token x {sum_l} tokens"}
-    qtag = ("" if Q == 1 else f"_Q{Q}") + ("_fp8" if fp8_cache else "")
-    roof.update({"traffic": measured_traffic(f"{split_name}_B{B}{qtag}_H{H}_L{int(cache.max_context)}",
+    roof.update({"traffic": measured_traffic(split_traffic_name(split_name, B, Q, H, int(cache.max_context), fp8_cache),
                                              "mla_latent_kv_09_amd/csrc/k_fp8.hip" if fp8_cache
                                              else "mla_latent_kv_09_amd/csrc/k_decode.hip"),
                  "kernel": split_name, "kernel_us": round(split_ms * 1e3, 2), **rule})

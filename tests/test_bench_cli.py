@@ -29,3 +29,14 @@ def test_more_than_one_gpu_is_refused():
     r = subprocess.run([sys.executable, "bench.py", "--gpus", "2"], capture_output=True, text=True,
                        cwd=bench.os.path.dirname(bench.os.path.abspath(bench.__file__)), timeout=120)
     assert r.returncode == 2 and "one GPU only" in r.stderr
+
+
+@pytest.mark.parametrize("split_name,q_len,fp8", [("mla_decode_split", 1, False), ("mla_decode_split", 2, False),
+                                                  ("mla_decode8_split", 1, True)])
+def test_decode_traffic_summaries_are_found_under_the_names_the_bench_builds(split_name, q_len, fp8):
+    name = bench.split_traffic_name(split_name, 64, q_len, 128, 8192, fp8)
+    assert bench.os.path.exists(bench.os.path.join(bench.PROFILES, f"{name}_hbm_traffic.md")), name
+
+
+def test_prefill_traffic_summary_is_found_under_the_name_the_bench_builds():
+    assert bench.os.path.exists(bench.os.path.join(bench.PROFILES, "mla_prefill_attn_B4_S4096_H128_hbm_traffic.md"))
