@@ -118,6 +118,7 @@ SMALL = [
     ("H100", 100, 1, [129, 1, 640], True),
     ("H128 q2 pairs", 128, 2, [2, 64, 65, 127, 128, 129, 1500, 2047], True),
     ("H32 q3 few units", 32, 3, [3, 129, 700], True),
+    ("H8 q64 max", 8, 64, [64, 65, 100, 300, 700, 64, 1000, 129], True),
 ]
 
 

@@ -309,6 +309,8 @@ MULTI = [
     ("H128 q3 few units", 128, 3, [3, 129, 700], True),
     ("H32 q7 long", 32, 7, [5000, 7], True),
     ("H128 q2 identity pages", 128, 2, [64, 2047], False),
+    # the largest q_len the library accepts; 8 sequences, so paired XCD order
+    ("H8 q64 max", 8, 64, [64, 65, 100, 300, 700, 64, 1000, 129], True),
 ]
 
 
