@@ -210,8 +210,10 @@ def test_mfma_path_is_selected_for_the_v3_shape():
     assert mla.mla_decode_path(Dims(4, 32, 8, 16, 16, dtype="f32")) == 0
 
 
-@pytest.mark.parametrize("H", [1, 48, 100])
+@pytest.mark.parametrize("H", [1, 48, 100, 129, 256])
 def test_decode_odd_head_counts(H):
+    """Up to 128 heads the MFMA path runs; 129 .. 256 (the largest head count
+    the library accepts) take the generic kernels."""
     _log(f"decode H={H}")
     case = make_decode_case(200 + H, 3, Dims(H, **V3), [129, 1, 640], shuffle=True)
     assert_parity(run_decode(case), oracle_decode(case), "bf16", f"H={H}")
