@@ -170,6 +170,8 @@ def test_fp8_entry_points_errors_and_sizes():
     assert d8(ptrs=(None, P, P, P)) == NULL and d8(out=None) == NULL
     assert d8(d=_Dims(4, 32, 8, 16, 16, 0.0, 10000.0, 1)) == UNSUP       # not the DeepSeek-V3 shape
     assert d8(c=cache(block_table=None)) == UNSUP                          # contiguous cache
+    assert d8(d=V3(n_heads=129)) == UNSUP                                  # more heads than the FP8 kernel holds
+    assert d8(d=V3(n_heads=257)) == SHAPE                                  # beyond any path
     need = mla.mla_decode_fp8_workspace_size(V3(), 4, 2, 8192)
     assert need > 0 and d8(q_len=2, wsb=need - 1) == WS
     assert mla.mla_decode_fp8_workspace_size(_Dims(4, 32, 8, 16, 16, 0.0, 10000.0, 1), 4, 1, 64) == 0
