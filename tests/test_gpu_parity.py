@@ -162,16 +162,18 @@ def test_project_with_query_path_then_prefill_small():
     assert_parity(from_torch(out), ref, "bf16", "prefill")
 
 
-def test_chunked_prefill_over_a_cached_prefix():
-    """Queries that are the last S tokens of a longer context see the prefix."""
-    _log("chunked prefill")
-    dims = Dims(16, **V3)
+@pytest.mark.parametrize("H", [16, 256])
+def test_chunked_prefill_over_a_cached_prefix(H):
+    """Queries that are the last S tokens of a longer context see the prefix
+    (256: the largest head count the library accepts)."""
+    _log(f"chunked prefill H={H}")
+    dims = Dims(H, **V3)
     L, S = 300, 70
     case = make_decode_case(12, 2, dims, [L, L], shuffle=True)
     rng = np.random.default_rng(3)
     from synth import f32_to_bf16_bits
-    qn = f32_to_bf16_bits(rng.standard_normal((2, S, 16, 128)).astype(np.float32))
-    qp = f32_to_bf16_bits(rng.standard_normal((2, S, 16, 64)).astype(np.float32))
+    qn = f32_to_bf16_bits(rng.standard_normal((2, S, H, 128)).astype(np.float32))
+    qp = f32_to_bf16_bits(rng.standard_normal((2, S, H, 64)).astype(np.float32))
     c = device_cache(case.cache)
     out = mla.mla_prefill(dims, to_torch(qn), to_torch(qp), to_torch(case.w_uk), to_torch(case.w_uv), c)
     torch.cuda.synchronize()
