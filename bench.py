@@ -160,6 +160,32 @@ def copy_calibration(nbytes):
                       "GB_per_s_read_plus_write": round(2 * nbytes / (ms * 1e-3) / 1e9, 1)}), flush=True)
 
 
+def host_cpu():
+    """(cores this process may run on, CPU model name). The oracle's BLAS and
+    torch thread pools are set to that core count."""
+    cores = len(os.sched_getaffinity(0))
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:  # pragma: no cover
+        pass
+    try:
+        from threadpoolctl import threadpool_limits
+        threadpool_limits(cores)
+    except Exception:  # pragma: no cover
+        pass
+    try:
+        import torch
+        torch.set_num_threads(cores)
+    except Exception:  # pragma: no cover
+        pass
+    return cores, model
+
+
 def cpu_baseline(case, budget_s, fp8_cache=False):
     """The oracle as it stands, on whole sequences of the same workload, until
     the time budget is spent (at least one sequence). With an FP8 cache the
@@ -167,11 +193,7 @@ def cpu_baseline(case, budget_s, fp8_cache=False):
     dequantised rows."""
     import oracle
     from oracle import fp8
-    try:
-        from threadpoolctl import threadpool_info
-        threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
-    except Exception:  # pragma: no cover
-        threads = len(os.sched_getaffinity(0))
+    threads, cpu_model = host_cpu()
     c = case.cache
     Q = case.q_len
     done, t0 = 0, time.perf_counter()
@@ -199,7 +221,7 @@ def cpu_baseline(case, budget_s, fp8_cache=False):
     dt = time.perf_counter() - t0
     toks = int(sum(int(c.context_lens[b]) for b in rows_done))
     what = "sequences" if Q == 1 else f"sequences x {Q} new tokens"
-    return {"value": done / dt, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
+    return {"value": done / dt, "unit": "tokens/s", "cores": int(threads), "cpu_model": cpu_model, "kind": "oracle",
             "sample": f"{len(rows_done)} of {case.batch} {what} ({toks} cached tokens, all {case.dims.n_heads} "
                       f"heads), float64 numpy, {dt:.1f} s"}
 
@@ -210,11 +232,7 @@ def cpu_baseline_prefill(case, budget_s):
     explicit per-head keys and values, for the first n tokens, with n doubled
     from 64 while the budget lasts."""
     import oracle
-    try:
-        from threadpoolctl import threadpool_info
-        threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
-    except Exception:  # pragma: no cover
-        threads = len(os.sched_getaffinity(0))
+    threads, cpu_model = host_cpu()
     dims = case.dims
     n, best, t_all = 64, None, time.perf_counter()
     while n <= case.seq_len:
@@ -230,10 +248,41 @@ def cpu_baseline_prefill(case, budget_s):
             break
         n *= 2
     n, dt = best
-    return {"value": n / dt, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
+    return {"value": n / dt, "unit": "tokens/s", "cores": int(threads), "cpu_model": cpu_model, "kind": "oracle",
             "sample": f"first {n} of {case.seq_len} tokens of sequence 0 (all {dims.n_heads} heads; projections "
                       f"+ causal attention with explicit K/V), float64 numpy, {dt:.1f} s; the attention cost per "
                       f"token grows with position, so the full sequence runs slower per token"}
+
+
+FLUSH_BYTES = 512 << 20   # twice the 256 MB last-level cache (MALL)
+
+
+def cold_pass(step, lib, kernel_name, n):
+    """Cold-cache timing, after the timed region: n steps, each preceded by an
+    untimed write of a 512 MiB scratch buffer (so no input is left in the
+    MALL or L2), each bracketed by its own events. Returns the median and
+    minimum step time and the median time of kernel_name (HIP events around
+    that kernel's launch), in microseconds."""
+    import torch
+    flush = torch.empty(FLUSH_BYTES, dtype=torch.uint8, device="cuda:0")
+    stream = torch.cuda.current_stream()
+    steps_us, kern_us = [], []
+    for i in range(n):
+        flush.fill_(i & 0xFF)
+        ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        lib.mla_profile_only(kernel_name.encode())
+        lib.mla_profile_begin()
+        ev0.record(stream)
+        step()
+        ev1.record(stream)
+        torch.cuda.synchronize()
+        k = profile_end(lib)
+        steps_us.append(ev0.elapsed_time(ev1) * 1e3)
+        kern_us.append(k[kernel_name][0] / k[kernel_name][1] * 1e3)
+    lib.mla_profile_only(None)
+    del flush
+    return {"steps": n, "flush_bytes": FLUSH_BYTES, "step_us_median": round(float(np.median(steps_us)), 2),
+            "step_us_min": round(float(np.min(steps_us)), 2), "split_us_median": round(float(np.median(kern_us)), 2)}
 
 
 def prefill_bench(args):
@@ -387,6 +436,7 @@ def main():
         step()
     torch.cuda.synchronize()
     breakdown = profile_end(lib)
+    cold = cold_pass(step, lib, split_name, min(args.steps, 50))
 
     sum_l = int(c.context_lens.astype(np.int64).sum())
     # key rows seen, over all queries: query j of q_len sees L - (q_len - 1 - j)
@@ -447,6 +497,8 @@ def main():
                  "mfma_TFLOP_per_s": round(step_flop / (ms * 1e-3) / 1e12, 1),
                  "mfma_frac": round(step_flop / (ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 4),
                  "kernels_us": kernels_us},
+        "cold": {**cold, "tokens_per_s": round(B * Q / (cold["step_us_median"] * 1e-6), 1),
+                 "split_frac": round(cache_bytes / (cold["split_us_median"] * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)},
     }
     if not args.no_cpu:
         line["cpu_baseline"] = cpu_baseline(case, args.cpu_seconds, fp8_cache)

@@ -360,7 +360,16 @@ hipError_t gemm_fast(const GemmArgs& g, int epi, hipStream_t s) {
 }
 
 bool project_fast_supported(const mla_dims& d, int d_model, int d_q) {
-  return d.dtype == MLA_BF16 && d_model % BK == 0 && d.d_rope % 4 == 0 && (d_q == 0 || d_q % BK == 0);
+  // The epilogues store 4 (register path) or 8 (staged path) consecutive
+  // columns at once. The latent GEMM's column groups stay inside c_KV or k_pe
+  // when d_c % 8 == 0 (checked with the dims) and d_rope % 4 == 0; the query
+  // GEMM's groups must not straddle the q_nope / q_pe split or a row end, so
+  // both widths are multiples of 8.
+  const int n_latent = d.d_c + d.d_rope;
+  const bool latent_ok = d.d_rope % 4 == 0 && gemm_fast_supported(1, n_latent, d_model);
+  const bool query_ok = d_q == 0 || (gemm_fast_supported(1, d_q, d_model) && d_q % BK == 0 &&
+                                     (d.n_heads * d.d_nope) % 8 == 0 && (d.n_heads * d.d_rope) % 8 == 0);
+  return d.dtype == MLA_BF16 && latent_ok && query_ok;
 }
 
 // Latent rows (RoPE + scatter epilogue), then the optional query path: c_Q in

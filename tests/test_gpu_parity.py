@@ -425,6 +425,35 @@ def test_mfma_projection_and_prefill_ragged():
     assert_parity(got, ref, "bf16", "prefill")
 
 
+@pytest.mark.parametrize("H,d_nope,d_rope", [(3, 10, 8), (8, 5, 8), (5, 12, 8), (5, 8, 16)])
+def test_projection_with_odd_head_widths(H, d_nope, d_rope):
+    """Query path with per-head widths whose column groups do not line up with
+    the MFMA epilogue's 4- and 8-column stores: H*d_nope not a multiple of 8
+    takes the generic kernels; (8, 5, 8) and (5, 8, 16) take the MFMA path
+    with odd per-head widths or head counts."""
+    _log(f"projection H={H} d_nope={d_nope} d_rope={d_rope}")
+    dims = Dims(H, 64, d_rope, d_nope, 16)
+    case = make_project_case(41 + H, batch=2, seq_len=70, d_model=128, dims=dims, d_q=64, shuffle=True)
+    T, nb = case.n_tokens, case.num_blocks
+    rows = torch.zeros((nb, 64, dims.row), dtype=torch.bfloat16, device="cuda")
+    cache = mla.Cache(rows, torch.full((2,), 70, dtype=torch.int32, device="cuda"), 70, to_torch(case.block_table))
+    # one guard row past each output, which no call may touch
+    qn = torch.full((T * H * d_nope + 64,), 7.0, dtype=torch.bfloat16, device="cuda")
+    qp = torch.full((T * H * d_rope + 64,), 7.0, dtype=torch.bfloat16, device="cuda")
+    qproj = mla.QProj(to_torch(case.w_dq), to_torch(case.w_uq), to_torch(case.w_qr),
+                      qn[:T * H * d_nope].view(T, H, d_nope), qp[:T * H * d_rope].view(T, H, d_rope))
+    mla.mla_rope_latent_project(dims, to_torch(case.h), to_torch(case.w_dkv), to_torch(case.w_kr),
+                                to_torch(case.positions), to_torch(case.slots), cache, qproj)
+    torch.cuda.synchronize()
+    got_n, got_p = from_torch(qn), from_torch(qp)
+    assert np.all(got_n[T * H * d_nope:] == 7.0) and np.all(got_p[T * H * d_rope:] == 7.0)
+    ref_qn, ref_qp = oracle.query_projection(case.h, case.w_dq, case.w_uq, case.w_qr, H, d_nope, d_rope)
+    assert_parity(got_n[:T * H * d_nope].reshape(T, H, d_nope), ref_qn, "bf16", "q_nope")
+    assert_parity(got_p[:T * H * d_rope].reshape(T, H, d_rope), ref_qp, "bf16", "q_pe")
+    ref_rows = oracle.latent_rows(case.h, case.w_dkv, case.w_kr, case.positions)
+    _check_rows(from_torch(rows)[case.slots // 64, case.slots % 64], ref_rows)
+
+
 def test_workload5_full_size_sampled():
     _log("workload 5: B=4 S=4096 d_model=7168 projection + prefill, oracle on sampled queries")
     case = workload(5)

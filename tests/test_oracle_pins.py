@@ -116,6 +116,16 @@ def test_rope_touches_only_the_rotary_slice_of_cache_rows():
 
 # --------------------------------------------------------- brute force -----
 
+def _w(a):
+    """float64 copy of an input array, widened with torch's own bfloat16 type
+    (uint16 bit patterns) rather than the oracle's widening, so that the pins
+    do not share that conversion with the oracle."""
+    a = np.asarray(a)
+    if a.dtype == np.uint16:
+        return torch.from_numpy(a.view(np.int16).copy()).view(torch.bfloat16).to(torch.float64).numpy()
+    return a.astype(np.float64)
+
+
 def _bf_rope(x, pos, base):
     out = []
     d = len(x)
@@ -150,10 +160,10 @@ def _bf_attend_one(dims, qn, qp_rot, rows, wuk, wuv, h):
 
 def bruteforce_decode(case):
     d = case.dims
-    qn, qp = om.widen(case.q_nope).tolist(), om.widen(case.q_pe).tolist()
-    wuk, wuv = om.widen(case.w_uk).tolist(), om.widen(case.w_uv).tolist()
+    qn, qp = _w(case.q_nope).tolist(), _w(case.q_pe).tolist()
+    wuk, wuv = _w(case.w_uk).tolist(), _w(case.w_uv).tolist()
     out = np.zeros((case.batch, d.n_heads, d.d_v))
-    pool, table = om.widen(case.cache.pool), case.cache.block_table
+    pool, table = _w(case.cache.pool), case.cache.block_table
     for b in range(case.batch):
         L = int(case.cache.context_lens[b])
         rows = [pool[table[b][t // 64], t % 64].tolist() for t in range(L)]
@@ -164,7 +174,7 @@ def bruteforce_decode(case):
 
 
 def bruteforce_prefill(dims, qn, qp, wuk, wuv, rows):
-    qn, qp, wuk, wuv, rows = (om.widen(a).tolist() for a in (qn, qp, wuk, wuv, rows))
+    qn, qp, wuk, wuv, rows = (_w(a).tolist() for a in (qn, qp, wuk, wuv, rows))
     B, S = len(qn), len(qn[0])
     out = np.zeros((B, S, dims.n_heads, dims.d_v))
     for b in range(B):
@@ -206,15 +216,148 @@ def test_prefill_matches_bruteforce():
     assert np.allclose(sub, got[[1, 0, 1], [0, 8, 4]], rtol=1e-12, atol=1e-13)
 
 
+def bruteforce_latent_rows(h, w_dkv, w_kr, positions, base):
+    """[V2] §2.1: c_t[i] = sum_j W_DKV[i, j] h_t[j]; [V2] §2.3: the rotary key
+    is W_KR h_t rotated at the token's own position. Plain loops."""
+    H, Wd, Wr = _w(h).tolist(), _w(w_dkv).tolist(), _w(w_kr).tolist()
+    rows = []
+    for t, ht in enumerate(H):
+        c = [sum(Wd[i][j] * ht[j] for j in range(len(ht))) for i in range(len(Wd))]
+        k = [sum(Wr[i][j] * ht[j] for j in range(len(ht))) for i in range(len(Wr))]
+        rows.append(c + _bf_rope(k, int(positions[t]), base))
+    return np.array(rows)
+
+
+def bruteforce_query_projection(h, w_dq, w_uq, w_qr, n_heads, d_nope, d_rope):
+    """[V2] §4.3: c_Q = W_DQ h; head hh's q_nope is rows hh*d_nope .. of
+    W_UQ times c_Q and its q_pe rows hh*d_rope .. of W_QR times c_Q. Loops."""
+    H, Wd, Wu, Wr = _w(h).tolist(), _w(w_dq).tolist(), _w(w_uq).tolist(), _w(w_qr).tolist()
+    T = len(H)
+    qn = np.zeros((T, n_heads, d_nope))
+    qp = np.zeros((T, n_heads, d_rope))
+    for t, ht in enumerate(H):
+        cq = [sum(Wd[i][j] * ht[j] for j in range(len(ht))) for i in range(len(Wd))]
+        for hh in range(n_heads):
+            for j in range(d_nope):
+                qn[t, hh, j] = sum(Wu[hh * d_nope + j][i] * cq[i] for i in range(len(cq)))
+            for j in range(d_rope):
+                qp[t, hh, j] = sum(Wr[hh * d_rope + j][i] * cq[i] for i in range(len(cq)))
+    return qn, qp
+
+
+# projection cases: positions far from 0 and not in token order, so that a
+# rotation at the wrong position or no rotation shows; d_nope == d_rope and
+# d_q == d_model so that the planted mistakes below keep valid shapes
+PROJ_CASES = [
+    (Dims(3, 8, 4, 4, 5, dtype="f32"), 7, 12, 12),
+    (Dims(2, 16, 8, 8, 4, dtype="bf16"), 5, 16, 16),
+]
+
+
+def _projection_case(dims, n_tok, d_model, d_q, seed=31):
+    case = make_project_case(seed, 1, n_tok, d_model, dims, d_q=d_q)
+    pos = np.random.default_rng(seed).integers(0, 5000, size=n_tok).astype(np.int32)
+    return case, pos
+
+
+@pytest.mark.parametrize("dims,n_tok,d_model,d_q", PROJ_CASES)
+def test_latent_rows_match_bruteforce(dims, n_tok, d_model, d_q):
+    case, pos = _projection_case(dims, n_tok, d_model, d_q)
+    got = oracle.latent_rows(case.h, case.w_dkv, case.w_kr, pos, dims.rope_base)
+    assert np.allclose(got, bruteforce_latent_rows(case.h, case.w_dkv, case.w_kr, pos, dims.rope_base),
+                       rtol=1e-11, atol=1e-12)
+
+
+@pytest.mark.parametrize("dims,n_tok,d_model,d_q", PROJ_CASES)
+def test_query_projection_matches_bruteforce(dims, n_tok, d_model, d_q):
+    case, _ = _projection_case(dims, n_tok, d_model, d_q)
+    qn, qp = oracle.query_projection(case.h, case.w_dq, case.w_uq, case.w_qr, dims.n_heads, dims.d_nope,
+                                     dims.d_rope)
+    bn, bp = bruteforce_query_projection(case.h, case.w_dq, case.w_uq, case.w_qr, dims.n_heads, dims.d_nope,
+                                         dims.d_rope)
+    assert qn.shape == bn.shape and qp.shape == bp.shape
+    assert np.allclose(qn, bn, rtol=1e-11, atol=1e-12) and np.allclose(qp, bp, rtol=1e-11, atol=1e-12)
+
+
+def test_projection_store_rounds_to_bf16():
+    dims, n_tok, d_model, d_q = PROJ_CASES[1]
+    case, pos = _projection_case(dims, n_tok, d_model, d_q)
+    exact = bruteforce_latent_rows(case.h, case.w_dkv, case.w_kr, pos, dims.rope_base)
+    got = oracle.latent_rows(case.h, case.w_dkv, case.w_kr, pos, dims.rope_base, store="bf16")
+    # every stored value is a bf16 number within half a bf16 ulp of the exact row
+    bits = torch.from_numpy(got.astype(np.float32)).to(torch.bfloat16).to(torch.float64).numpy()
+    assert np.array_equal(bits, got)
+    assert np.all(np.abs(got - exact) <= np.abs(exact) * 2.0 ** -8 + 1e-30)
+
+
+def _projection_pins_pass():
+    ok = True
+    for dims, n_tok, d_model, d_q in PROJ_CASES:
+        case, pos = _projection_case(dims, n_tok, d_model, d_q)
+        rows = oracle.latent_rows(case.h, case.w_dkv, case.w_kr, pos, dims.rope_base)
+        ok &= np.allclose(rows, bruteforce_latent_rows(case.h, case.w_dkv, case.w_kr, pos, dims.rope_base),
+                          rtol=1e-9, atol=1e-11)
+        qn, qp = oracle.query_projection(case.h, case.w_dq, case.w_uq, case.w_qr, dims.n_heads, dims.d_nope,
+                                         dims.d_rope)
+        bn, bp = bruteforce_query_projection(case.h, case.w_dq, case.w_uq, case.w_qr, dims.n_heads,
+                                             dims.d_nope, dims.d_rope)
+        ok &= np.allclose(qn, bn, rtol=1e-9, atol=1e-11) and np.allclose(qp, bp, rtol=1e-9, atol=1e-11)
+    return bool(ok)
+
+
+_ORIG_QP = om.query_projection
+_ORIG_ROPE = om.rope
+
+
+def _plant_q_heads_transposed(h, w_dq, w_uq, w_qr, n_heads, d_nope, d_rope, store=None):
+    # per-head split read as [d, n_heads] instead of [n_heads, d]
+    qn, qp = _ORIG_QP(h, w_dq, w_uq, w_qr, n_heads, d_nope, d_rope, store)
+    T = qn.shape[0]
+    return (qn.reshape(T, -1).reshape(T, d_nope, n_heads).transpose(0, 2, 1),
+            qp.reshape(T, -1).reshape(T, d_rope, n_heads).transpose(0, 2, 1))
+
+
+def _plant_uq_qr_swapped(h, w_dq, w_uq, w_qr, n_heads, d_nope, d_rope, store=None):
+    # the cases use d_nope == d_rope, so swapped weights still have the right shapes
+    return _ORIG_QP(h, w_dq, w_qr, w_uq, n_heads, d_nope, d_rope, store)
+
+
+def _plant_cq_skipped(h, w_dq, w_uq, w_qr, n_heads, d_nope, d_rope, store=None):
+    # up-projections applied to h directly (d_q == d_model in the cases)
+    eye = np.eye(np.asarray(w_dq).shape[0])
+    return _ORIG_QP(h, eye, w_uq, w_qr, n_heads, d_nope, d_rope, store)
+
+
+PROJECTION_PLANTS = {
+    "query head axis transposed": ("query_projection", _plant_q_heads_transposed),
+    "W_UQ and W_QR swapped": ("query_projection", _plant_uq_qr_swapped),
+    "c_Q skipped": ("query_projection", _plant_cq_skipped),
+    "key RoPE at position + 1": ("rope", lambda x, pos, base=10000.0: _ORIG_ROPE(x, np.asarray(pos) + 1, base)),
+    "key RoPE skipped": ("rope", lambda x, pos, base=10000.0: np.asarray(x, dtype=np.float64)),
+}
+
+
+def test_projection_pins_pass_on_the_true_oracle():
+    assert _projection_pins_pass()
+
+
+@pytest.mark.parametrize("name", sorted(PROJECTION_PLANTS))
+def test_projection_pins_catch_planted_mistake(name, monkeypatch):
+    attr, fn = PROJECTION_PLANTS[name]
+    monkeypatch.setattr(om, attr, fn)
+    monkeypatch.setattr(oracle, attr, fn)
+    assert not _projection_pins_pass(), name
+
+
 # ------------------------------------------------------- library routine ---
 
 def _sdpa_decode(case):
     """torch's CPU scaled_dot_product_attention on K/V built here with torch."""
     d = case.dims
     H, dn, dv, dc = d.n_heads, d.d_nope, d.d_v, d.d_c
-    wuk = torch.from_numpy(om.widen(case.w_uk)).view(H, dn, dc)
-    wuv = torch.from_numpy(om.widen(case.w_uv)).view(H, dv, dc)
-    pool = torch.from_numpy(om.widen(case.cache.pool))
+    wuk = torch.from_numpy(_w(case.w_uk)).view(H, dn, dc)
+    wuv = torch.from_numpy(_w(case.w_uv)).view(H, dv, dc)
+    pool = torch.from_numpy(_w(case.cache.pool))
     outs = []
     for b in range(case.batch):
         L = int(case.cache.context_lens[b])
@@ -224,10 +367,10 @@ def _sdpa_decode(case):
         k = torch.cat([torch.einsum("hnc,tc->htn", wuk, c), kpe.expand(H, L, d.d_rope)], dim=-1)
         v = torch.einsum("hvc,tc->htv", wuv, c)
         ang = (L - 1) * d.rope_base ** (-torch.arange(0, d.d_rope, 2, dtype=torch.float64) / d.d_rope)
-        qp = torch.from_numpy(om.widen(case.q_pe[b]))
+        qp = torch.from_numpy(_w(case.q_pe[b]))
         rot = torch.view_as_real(torch.view_as_complex(qp.view(H, -1, 2).contiguous())
                                  * torch.polar(torch.ones_like(ang), ang)).view(H, -1)
-        q = torch.cat([torch.from_numpy(om.widen(case.q_nope[b])), rot], dim=-1)[:, None, :]
+        q = torch.cat([torch.from_numpy(_w(case.q_nope[b])), rot], dim=-1)[:, None, :]
         outs.append(torch.nn.functional.scaled_dot_product_attention(q, k, v, scale=d.scale)[:, 0])
     return torch.stack(outs).numpy()
 
@@ -247,8 +390,8 @@ def test_prefill_matches_torch_sdpa_causal():
     qn, qp = rng.standard_normal((2, 40, 4, 16)), rng.standard_normal((2, 40, 4, 8))
     got = oracle.prefill(dims, qn, qp, case.w_uk, case.w_uv, rows)
     H = 4
-    wuk = torch.from_numpy(om.widen(case.w_uk)).view(H, 16, 32)
-    wuv = torch.from_numpy(om.widen(case.w_uv)).view(H, 16, 32)
+    wuk = torch.from_numpy(_w(case.w_uk)).view(H, 16, 32)
+    wuv = torch.from_numpy(_w(case.w_uv)).view(H, 16, 32)
     for b in range(2):
         r = torch.from_numpy(rows[b])
         k = torch.cat([torch.einsum("hnc,tc->htn", wuk, r[:, :32]), r[:, 32:].expand(H, 40, 8)], -1)
@@ -265,14 +408,14 @@ def test_prefill_matches_torch_sdpa_causal():
 
 def _wuv_c(case, h, c):
     d = case.dims
-    return om.widen(case.w_uv)[h * d.d_v:(h + 1) * d.d_v] @ c
+    return _w(case.w_uv)[h * d.d_v:(h + 1) * d.d_v] @ c
 
 
 def test_single_token_context_returns_its_value():
     case = make_decode_case(15, 2, Dims(4, 16, 4, 8, 8, dtype="f32"), [1, 1])
     out = _oracle_decode(case)
     for b in range(2):
-        c0 = om.widen(case.cache.pool[case.cache.block_table[b, 0], 0])[:16]
+        c0 = _w(case.cache.pool[case.cache.block_table[b, 0], 0])[:16]
         for h in range(4):
             assert np.allclose(out[b, h], _wuv_c(case, h, c0), rtol=1e-13, atol=1e-14)
 
@@ -283,7 +426,7 @@ def test_identical_rows_return_their_value():
     pool[:] = pool[0, 0]
     out = _oracle_decode(case)
     for h in range(4):
-        assert np.allclose(out[0, h], _wuv_c(case, h, om.widen(pool[0, 0, :16])), rtol=1e-12, atol=1e-13)
+        assert np.allclose(out[0, h], _wuv_c(case, h, _w(pool[0, 0, :16])), rtol=1e-12, atol=1e-13)
 
 
 def test_zero_query_gives_uniform_average():
@@ -329,7 +472,7 @@ def test_shifting_every_position_leaves_decode_unchanged():
     outs = []
     for delta in (0, 777, 30000):
         rows = oracle.latent_rows(case.h, case.w_dkv, case.w_kr, case.positions + delta)
-        qpe = oracle.rope(om.widen(case.q_pe), delta)        # query moved by the same delta
+        qpe = oracle.rope(_w(case.q_pe), delta)        # query moved by the same delta
         outs.append(oracle.decode(dims, case.q_nope, qpe, case.w_uk, case.w_uv, rows[None], None, lens))
     assert np.allclose(outs[1], outs[0], rtol=1e-9, atol=1e-11)
     assert np.allclose(outs[2], outs[0], rtol=1e-9, atol=1e-11)
