@@ -290,7 +290,8 @@ __global__ __launch_bounds__(256) void k_absorb(int B, int H, int q_len, const b
 // The reference max is set by the first tile and then moves lazily (only when
 // a tile's max exceeds it by more than 8) and only by whole steps k, so the
 // rescale factor of the other waves' accumulators is an exact power of two
-// 2^-k. The owner sends k (8 bits) in
+// 2^-k; a jump of 255 or more resets the reference to the tile's max and
+// sends k = 255 (factor 0 in fp32). The owner sends k (8 bits) in
 // the sign bits of the head's first P fragment (P >= 0, so those bits are
 // otherwise clear); the readers test them, and in the rare case decode k,
 // clear the bits and rescale.
@@ -500,13 +501,19 @@ __global__ __launch_bounds__(SPLIT_THREADS, 1) void k_split(int H, int B, int q_
         sm_mx = fmaxf(__uint_as_float(pr[0]), __uint_as_float(pr[1]));
       }
       // first tile: the reference is the exact max (its p is exactly 1);
-      // later moves are by whole steps k >= 9
+      // later moves are by whole steps k >= 9. A jump of 255 or more resets
+      // the reference to the max and sends k = 255: every earlier term then
+      // weighs less than 2^-246 against the new max (its score was at most
+      // 8 above the old reference), below the smallest fp32 number, so the
+      // factor 2^-255 (0 in fp32) that the sum and the accumulators are
+      // scaled by is their weight rounded to fp32.
       const bool first = m_run == -INFINITY;
       const bool up = !first && sm_mx > m_run + 8.f;
-      const float kf = up ? fminf(ceilf(sm_mx - m_run), 255.f) : 0.f;
-      sm_k = (int)kf;
+      const float kc = up ? ceilf(sm_mx - m_run) : 0.f;
+      const bool reset = !(kc < 255.f);
+      sm_k = reset ? 255 : (int)kc;
       sm_alpha = __builtin_amdgcn_ldexpf(1.f, -sm_k);
-      m_run = first ? sm_mx : m_run + kf;
+      m_run = (first || reset) ? sm_mx : m_run + kc;
       sm_sub = m_run;
       sm_lsum = 0.f;
     } else {

@@ -528,12 +528,17 @@ __global__ __launch_bounds__(THREADS, 1) void k_split8(int H, int B, int q_len, 
         const auto pr = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx), false, false);
         mx = fmaxf(__uint_as_float(pr[0]), __uint_as_float(pr[1]));
       }
+      // a jump of 255 or more resets the reference to the max and sends
+      // k = 255: the earlier terms weigh less than 2^-246 against it (each
+      // was at most 8 above the old reference), below the smallest fp32
+      // number, so the factor 2^-255 (0 in fp32) is their weight rounded
       const bool first = m_run == -INFINITY;
       const bool up = !first && mx > m_run + 8.f;
-      const float kf = up ? fminf(ceilf(mx - m_run), 255.f) : 0.f;
-      const int k_shift = (int)kf;
+      const float kc = up ? ceilf(mx - m_run) : 0.f;
+      const bool reset = !(kc < 255.f);
+      const int k_shift = reset ? 255 : (int)kc;
       alpha = __builtin_amdgcn_ldexpf(1.f, -k_shift);
-      m_run = first ? mx : m_run + kf;
+      m_run = (first || reset) ? mx : m_run + kc;
       // the shift goes to the other waves beside P
       if (g == 0) *(LDS_AS uint8_t*)(size_t)(kb_addr(i) + 4 * hl + w) = (uint8_t)k_shift;
       pw = pb_addr(i);

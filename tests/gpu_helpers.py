@@ -62,3 +62,33 @@ def fails_bar(got, ref, dtype):
     except AssertionError:
         return True
     return False
+
+
+def score_jump_case(case, jump_log2, low_pages=2):
+    """Makes the scores of every sequence's first `low_pages` pages about
+    `jump_log2` log2 units below those of the rest, for every head, so that the
+    running max of a page run jumps by that much inside the run.
+
+    All heads of a sequence get head 0's rotary query v; the low pages' k_pe is
+    set to -lam * R(L-1) v (R the oracle's rotation at the query's position),
+    which adds -lam |v|^2 * scale to every head's score there. The values
+    (c_KV) keep their scale, so the output is set by the high pages, whose
+    scores are ordinary."""
+    import oracle
+    from synth import bf16_bits_to_f32, f32_to_bf16_bits
+    d = case.dims
+    pool = bf16_bits_to_f32(case.cache.pool)
+    q_pe = bf16_bits_to_f32(case.q_pe)
+    table = case.cache.block_table
+    for b, L in enumerate(case.cache.context_lens):
+        L = int(L)
+        v = q_pe[b, 0].astype(np.float64)
+        q_pe[b, :] = q_pe[b, 0]
+        u = oracle.rope(v, L - 1, d.rope_base)
+        lam = jump_log2 / (float(u @ u) * d.scale * np.log2(np.e))
+        n_low = min(low_pages, (L + 63) // 64)
+        for p in range(n_low):
+            pool[table[b, p], :, d.d_c:] = (-lam * u).astype(np.float32)
+    case.cache.pool = f32_to_bf16_bits(pool)
+    case.q_pe = f32_to_bf16_bits(q_pe)
+    return case

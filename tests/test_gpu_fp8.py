@@ -172,6 +172,17 @@ def test_decode_fp8_large_score_growth_takes_the_rescale_branch():
     assert_parity(_run_fp8(case, pages), _oracle_fp8(case, deq), "fp8", "rescale")
 
 
+@pytest.mark.parametrize("jump", [300.0, 600.0])
+def test_decode_fp8_score_jump_beyond_the_shift_field(jump):
+    _log(f"decode fp8 with a score jump of {jump} log2 units inside a run")
+    from gpu_helpers import score_jump_case
+    case = score_jump_case(make_decode_case(505, 3, Dims(128, **V3), [300, 700, 1500], shuffle=True), jump)
+    pages, deq = _fp8_case(case)
+    got = _run_fp8(case, pages)
+    assert np.all(np.isfinite(got))
+    assert_parity(got, _oracle_fp8(case, deq), "fp8", f"jump {jump}")
+
+
 def test_decode_fp8_ignores_non_finite_bytes_past_the_context():
     _log("decode fp8 with NaN codes and scales past the context")
     case = make_decode_case(503, 4, Dims(64, **V3), [1, 33, 100, 1000], shuffle=True, q_len=1)

@@ -238,6 +238,19 @@ def test_decode_large_score_growth_takes_the_rescale_branch():
     assert_parity(run_decode(case), oracle_decode(case), "bf16", "rescale")
 
 
+@pytest.mark.parametrize("jump", [300.0, 600.0])
+def test_decode_score_jump_beyond_the_shift_field(jump):
+    """Scores that jump by more than 255 log2 units inside one page run: the
+    first pages of each sequence score about `jump` below the rest, so the
+    lazy reference is reset to the new max instead of moved by k."""
+    _log(f"decode with a score jump of {jump} log2 units inside a run")
+    from gpu_helpers import score_jump_case
+    case = score_jump_case(make_decode_case(14, 3, Dims(128, **V3), [300, 700, 1500], shuffle=True), jump)
+    got = run_decode(case)
+    assert np.all(np.isfinite(got))
+    assert_parity(got, oracle_decode(case), "bf16", f"jump {jump}")
+
+
 def _poison_tails(case):
     """Fills every cache row past a sequence's context in its last page with
     NaN or infinity bit patterns, as a reused page may hold."""
