@@ -24,8 +24,10 @@
  *
  * Conventions for every entry point
  *   - Pointers marked "device" are device memory owned by the caller; the
- *     library never frees or retains them and allocates no device memory. All
- *     arrays are dense, row-major and 16-byte aligned.
+ *     library never frees or retains them and allocates no device memory
+ *     (mla_decode_noalloc's fixed scratch array is part of the library's
+ *     code object, one per GPU). All arrays are dense, row-major and 16-byte
+ *     aligned.
  *   - Work is enqueued on `stream` (a hipStream_t; NULL = the default stream)
  *     and the call returns without waiting. Results are ready once the stream
  *     is synchronised. Calls on different streams need separate workspaces.
@@ -220,6 +222,25 @@ mla_status mla_prefill(const mla_dims* dims, int32_t batch, int32_t seq_len,
                        const void* q_nope, const void* q_pe, const void* w_uk, const void* w_uv,
                        const mla_cache* cache, void* out,
                        void* workspace, size_t workspace_bytes, void* stream);
+
+/* Decode without allocation and without a caller workspace, for callers that
+ * cannot allocate device memory: code under HIP graph capture, tight serving
+ * loops, harnesses that forbid allocation. Arguments, checks and result are
+ * those of mla_decode_multi (q_len == 1 is mla_decode). The scratch memory it
+ * needs comes from a device array inside the library of
+ * MLA_NOALLOC_SCRATCH_BYTES (64 MiB), one per GPU the library runs on, held
+ * until the process ends; its device address is looked up on the first call
+ * on each device. A call whose mla_decode_multi_workspace_size exceeds the
+ * array returns MLA_ERR_WORKSPACE before anything is enqueued (the DeepSeek-V3
+ * shape with B = 64 sequences of 8192 tokens needs 43.3 MB). The array keeps
+ * whatever the last call left; nothing in it needs to start cleared. Calls
+ * that overlap on one GPU (other streams or threads) share the array and
+ * race: serialise them. */
+#define MLA_NOALLOC_SCRATCH_BYTES (64u << 20)
+mla_status mla_decode_noalloc(const mla_dims* dims, int32_t batch, int32_t q_len,
+                              const void* q_nope, const void* q_pe, const void* w_uk, const void* w_uv,
+                              const mla_cache* cache, void* out, void* stream);
+size_t mla_noalloc_scratch_bytes(void);
 
 /* Workspace each entry point needs for the given sizes (bytes, 0 possible). */
 mla_status mla_project_workspace_size(const mla_dims* dims, int32_t n_tokens, int32_t d_q, size_t* bytes);

@@ -22,7 +22,7 @@ __all__ = [
     "mla_rope_latent_project", "mla_decode", "mla_decode_multi", "mla_prefill",
     "mla_project_workspace_size", "mla_decode_workspace_size", "mla_decode_multi_workspace_size",
     "mla_prefill_workspace_size", "Fp8Cache", "mla_fp8_page_bytes", "mla_quantize_fp8", "mla_decode_fp8",
-    "mla_decode_fp8_workspace_size",
+    "mla_decode_fp8_workspace_size", "mla_decode_noalloc", "mla_noalloc_scratch_bytes",
     "mla_status_string", "mla_decode_path", "mla_prefill_path", "mla_version",
 ]
 
@@ -78,6 +78,10 @@ def library():
         lib.mla_decode_multi.argtypes = [pd, i32, i32, vp, vp, vp, vp, pc, vp, vp, sz, vp]
         lib.mla_prefill.argtypes = [pd, i32, i32, vp, vp, vp, vp, pc, vp, vp, sz, vp]
         lib.mla_decode_fp8.argtypes = [pd, i32, i32, vp, vp, vp, vp, pc, vp, vp, sz, vp]
+        lib.mla_decode_noalloc.argtypes = [pd, i32, i32, vp, vp, vp, vp, pc, vp, vp]
+        lib.mla_decode_noalloc.restype = ctypes.c_int
+        lib.mla_noalloc_scratch_bytes.argtypes = []
+        lib.mla_noalloc_scratch_bytes.restype = sz
         lib.mla_quantize_fp8.argtypes = [pd, i32, vp, vp, i32, vp, vp]
         lib.mla_fp8_page_bytes.argtypes = [pd, i32, ctypes.POINTER(sz)]
         lib.mla_decode_fp8_workspace_size.argtypes = [pd, i32, i32, i32, ctypes.POINTER(sz)]
@@ -366,6 +370,30 @@ def mla_decode_multi(dims, q_nope, q_pe, w_uk, w_uv, cache: Cache, out=None, wor
                                    ws.data_ptr() if ws is not None else None, nbytes, _stream(stream)),
         "mla_decode_multi")
     return out
+
+
+def mla_decode_noalloc(dims, q_nope, q_pe, w_uk, w_uv, cache: Cache, out, stream=None):
+    """mla_decode_multi without a workspace: the library's fixed scratch array
+    is used instead (see include/mla.h). q_nope is [B, q_len, H, d_nope]; out
+    [B, q_len, H, d_v] must be given (this call allocates nothing)."""
+    d = Dims.of(dims)
+    B, Q = q_nope.shape[:2]
+    dt = d.torch_dtype
+    _need(q_nope, "q_nope", (B, Q, d.n_heads, d.d_nope), dt)
+    _need(q_pe, "q_pe", (B, Q, d.n_heads, d.d_rope), dt)
+    _need(w_uk, "w_uk", (d.n_heads * d.d_nope, d.d_c), dt)
+    _need(w_uv, "w_uv", (d.n_heads * d.d_v, d.d_c), dt)
+    _check_cache(cache, d, B)
+    _need(out, "out", (B, Q, d.n_heads, d.d_v), dt)
+    cc = cache.c()
+    _ok(library().mla_decode_noalloc(ctypes.byref(d.c()), B, Q, q_nope.data_ptr(), q_pe.data_ptr(), w_uk.data_ptr(),
+                                     w_uv.data_ptr(), ctypes.byref(cc), out.data_ptr(), _stream(stream)),
+        "mla_decode_noalloc")
+    return out
+
+
+def mla_noalloc_scratch_bytes() -> int:
+    return int(library().mla_noalloc_scratch_bytes())
 
 
 def mla_fp8_page_bytes(dims, block_size: int = 64) -> int:
