@@ -33,6 +33,13 @@ them):
   (intelliparadigm.com/article/weixin_29047545/2249442), §3.1: score count
   of a 2048-token sequence and its multiply-add count at dimension 128.
 
+The output projection W_O (the attention layer's last step, which the pages'
+§2.2 of [V2] names when it says W_UV can be absorbed into it) is written here
+in its plain form, W_O applied to the concatenated per-head outputs, with
+the fused weight W_O,h W_UV,h written out separately (``fold_output_weights``
+and ``folded_decode_output``) only so that the tests can pin the two forms to
+each other.
+
 Readings taken where the pages are silent (each is a choice, stated once):
 
 * RoPE pairs elements (2i, 2i+1) and rotates pair i by pos * base^(-2i/d_rope)
@@ -44,6 +51,9 @@ Readings taken where the pages are silent (each is a choice, stated once):
 * Softmax scale 1/sqrt(d_nope + d_rope) unless a scale is given.
 * Weights use the pages' [out, in] orientation; head h owns rows
   h*d .. h*d + d - 1 of W_UK (d = d_nope) and of W_UV (d = d_v).
+* W_O is [d_model, n_h*d_v]; head h's output goes into columns
+  h*d_v .. h*d_v + d_v - 1, the order in which the heads' outputs are
+  concatenated.
 """
 from __future__ import annotations
 
@@ -282,4 +292,52 @@ def absorbed_decode(dims, q_nope, q_pe, w_uk, w_uv, pool, block_table, context_l
             s = dims.scale * (c @ q_abs + kpe @ qpe[h])
             p = _softmax(s)
             out[b, h] = _head_rows(wuv, h, dv) @ (p @ c)
+    return out
+
+
+# ----------------------------------------------------- output projection ---
+
+def output_projection(attn_out, w_o) -> np.ndarray:
+    """Attention layer output: W_O applied to the concatenation of the
+    per-head outputs. attn_out [..., n_h, d_v], w_o [d_model, n_h*d_v];
+    returns [..., d_model]."""
+    a = widen(attn_out)
+    lead = a.shape[:-2]
+    x = a.reshape(lead + (a.shape[-2] * a.shape[-1],))
+    return x @ widen(w_o).T
+
+
+def decode_output(dims, q_nope, q_pe, w_uk, w_uv, w_o, pool, block_table, context_lens, batch_rows=None):
+    """Decode followed by the output projection: [len(rows), d_model]."""
+    return output_projection(decode(dims, q_nope, q_pe, w_uk, w_uv, pool, block_table, context_lens,
+                                    batch_rows), w_o)
+
+
+def fold_output_weights(w_uv, w_o, n_heads: int, d_v: int) -> np.ndarray:
+    """[V2] §2.2: W_UV absorbed into the output projection. Block h of the
+    result, columns h*d_c .. of [d_model, n_h*d_c], is W_O,h W_UV,h, with
+    W_O,h the columns of W_O that take head h's output. For pinning only."""
+    wuv, wo = widen(w_uv), widen(w_o)
+    return np.concatenate([wo[:, h * d_v:(h + 1) * d_v] @ _head_rows(wuv, h, d_v) for h in range(n_heads)],
+                          axis=1)
+
+
+def folded_decode_output(dims, q_nope, q_pe, w_uk, w_ouv, pool, block_table, context_lens):
+    """The absorbed form of ``decode_output`` ([V2] §2.2 on both sides), for
+    pinning only: scores and the latent output o_c as in ``absorbed_decode``,
+    then out = sum_h W_OUV,h o_c,h with the folded weights [d_model, n_h*d_c];
+    neither keys, values nor per-head outputs are formed."""
+    H, dn, dc = dims.n_heads, dims.d_nope, dims.d_c
+    wuk, wouv = widen(w_uk), widen(w_ouv)
+    qn_all, qp_all = widen(q_nope), widen(q_pe)
+    B = qn_all.shape[0]
+    out = np.zeros((B, wouv.shape[0]))
+    for b in range(B):
+        rows = gather_rows(pool, block_table, context_lens, b)
+        c, kpe = rows[:, :dc], rows[:, dc:]
+        qpe = rope(qp_all[b], rows.shape[0] - 1, dims.rope_base)
+        for h in range(H):
+            q_abs = _head_rows(wuk, h, dn).T @ qn_all[b, h]
+            p = _softmax(dims.scale * (c @ q_abs + kpe @ qpe[h]))
+            out[b] += wouv[:, h * dc:(h + 1) * dc] @ (p @ c)
     return out

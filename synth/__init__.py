@@ -253,6 +253,12 @@ def make_project_case(seed: int, batch: int, seq_len: int, d_model: int, dims: D
                        w_uk, w_uv, q_nope, q_pe, positions, slots, table, nb, seed)
 
 
+def draw_output_weights(seed: int, d_model: int, n_heads: int, d_v: int, dtype: str = "bf16") -> np.ndarray:
+    """The output projection W_O [d_model, n_heads*d_v], std 1/sqrt(fan_in),
+    drawn from its own seeded stream (so no other draw of a workload moves)."""
+    return _Draw(seed, dtype).normal((d_model, n_heads * d_v), 1.0 / math.sqrt(n_heads * d_v))
+
+
 # The five measured shapes. Each entry builds its inputs from seed 1000 + k.
 V3 = dict(d_c=512, d_rope=64, d_nope=128, d_v=128)
 

@@ -540,6 +540,98 @@ def test_round_to_bf16_is_nearest_even():
     assert r[5] == pytest.approx(3.0e38, rel=2 ** -8)
 
 
+# ------------------------------------------------------ output projection --
+
+def bruteforce_output_projection(attn, w_o):
+    """out[n][j] = sum over heads h and value dims v of W_O[j][h*d_v + v] *
+    attn[n][h][v], by loops."""
+    A, W = _w(attn).tolist(), _w(w_o).tolist()
+    out = np.zeros((len(A), len(W)))
+    for n, an in enumerate(A):
+        dv = len(an[0])
+        for j, wj in enumerate(W):
+            out[n, j] = sum(wj[h * dv + v] * an[h][v] for h in range(len(an)) for v in range(dv))
+    return out
+
+
+def _wo_case(seed, H, dv, d_model, dtype="f32"):
+    from synth import draw_output_weights
+    dims = Dims(H, 16, 4, 8, dv, dtype=dtype)
+    case = make_decode_case(seed, 3, dims, [1, 70, 130], shuffle=True, w_std=0.6)
+    return case, draw_output_weights(seed + 1, d_model, H, dv, dtype)
+
+
+def _output_pins_pass():
+    ok = True
+    for seed, H, dv, d_model, dtype in ((40, 3, 5, 7, "f32"), (41, 2, 4, 8, "bf16"), (42, 4, 6, 24, "f32")):
+        case, w_o = _wo_case(seed, H, dv, d_model, dtype)
+        c = case.cache
+        attn = _oracle_decode(case)
+        plain = oracle.output_projection(attn, w_o)
+        ok &= np.allclose(plain, bruteforce_output_projection(attn, w_o), rtol=1e-11, atol=1e-12)
+        ok &= np.allclose(oracle.decode_output(case.dims, case.q_nope, case.q_pe, case.w_uk, case.w_uv, w_o, c.pool,
+                                               c.block_table, c.context_lens), plain, rtol=1e-12, atol=1e-13)
+        w_ouv = oracle.fold_output_weights(case.w_uv, w_o, H, dv)
+        folded = oracle.folded_decode_output(case.dims, case.q_nope, case.q_pe, case.w_uk, w_ouv, c.pool,
+                                             c.block_table, c.context_lens)
+        ok &= np.linalg.norm(folded - plain) <= 1e-12 * np.linalg.norm(plain)
+    return bool(ok)
+
+
+def test_output_projection_matches_bruteforce_and_the_fold():
+    """[V2] §2.2: W_UV absorbed into W_O gives the same layer output as W_O
+    applied to the per-head outputs (an exact rewrite, checked in fp64)."""
+    assert _output_pins_pass()
+
+
+def test_output_projection_of_one_head_with_identity_weights_is_its_output():
+    case, _ = _wo_case(43, 1, 8, 8)
+    attn = _oracle_decode(case)
+    assert np.array_equal(oracle.output_projection(attn, np.eye(8)), attn[:, 0])
+
+
+def test_fold_of_identity_output_weights_is_w_uv():
+    """With W_O the identity (d_model = n_h d_v) the folded weight of head h is
+    W_UV,h laid out as column block h."""
+    H, dv, dc = 3, 4, 16
+    case, _ = _wo_case(44, H, dv, H * dv)
+    f = oracle.fold_output_weights(case.w_uv, np.eye(H * dv), H, dv)
+    wuv = _w(case.w_uv)
+    for h in range(H):
+        assert np.array_equal(f[h * dv:(h + 1) * dv, h * dc:(h + 1) * dc], wuv[h * dv:(h + 1) * dv])
+        for g in range(H):
+            if g != h:
+                assert not np.any(f[g * dv:(g + 1) * dv, h * dc:(h + 1) * dc])
+
+
+_ORIG_OP = om.output_projection
+
+
+def _plant_heads_interleaved(attn, w_o):
+    # concatenation in [d_v, n_h] order instead of [n_h, d_v]
+    a = om.widen(attn)
+    return _ORIG_OP(np.swapaxes(a, -1, -2).reshape(a.shape), w_o)
+
+
+def _plant_head_blocks_reversed(attn, w_o):
+    return _ORIG_OP(om.widen(attn)[..., ::-1, :], w_o)
+
+
+OUTPUT_PLANTS = {
+    "heads interleaved in the concatenation": _plant_heads_interleaved,
+    "head blocks of W_O reversed": _plant_head_blocks_reversed,
+    "one head dropped": lambda attn, w_o: _ORIG_OP(np.concatenate([om.widen(attn)[..., :-1, :],
+                                                                   0 * om.widen(attn)[..., -1:, :]], axis=-2), w_o),
+}
+
+
+@pytest.mark.parametrize("name", sorted(OUTPUT_PLANTS))
+def test_output_pins_catch_planted_mistake(name, monkeypatch):
+    monkeypatch.setattr(om, "output_projection", OUTPUT_PLANTS[name])
+    monkeypatch.setattr(oracle, "output_projection", OUTPUT_PLANTS[name])
+    assert not _output_pins_pass(), name
+
+
 # ------------------------------------------------------ planted mistakes ----
 
 def _pins_pass():
