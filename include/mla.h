@@ -223,6 +223,46 @@ mla_status mla_prefill(const mla_dims* dims, int32_t batch, int32_t seq_len,
                        const mla_cache* cache, void* out,
                        void* workspace, size_t workspace_bytes, void* stream);
 
+/* Output side of the attention layer. W_O is device [d_model, n_heads * d_v]
+ * ([out, in], like every weight here); head h's output feeds columns
+ * h*d_v .. h*d_v + d_v - 1, the order in which the heads' outputs are
+ * concatenated. d_model in [1, 65536].
+ *
+ * mla_output_project: out = W_O applied to each row's concatenated per-head
+ * outputs, out[r] = W_O attn_out[r] (fp32 accumulate).
+ *   attn_out device [n_rows, n_heads, d_v] (e.g. mla_decode's output)
+ *   out      device [n_rows, d_model]
+ *   workspace at least mla_output_workspace_size(dims, n_rows, d_model, 0)
+ * n_rows == 0 is a no-op. */
+mla_status mla_output_project(const mla_dims* dims, int32_t n_rows, int32_t d_model, const void* attn_out,
+                              const void* w_o, void* out, void* workspace, size_t workspace_bytes, void* stream);
+
+/* W_UV absorbed into W_O ("DeepSeek-V2 paper digest" §2.2: on the output side
+ * W_UV can be absorbed into the output projection W_O, the weights being fused
+ * before inference). Writes W_OUV, device [d_model, n_heads * d_c], whose
+ * column block h (columns h*d_c .. h*d_c + d_c - 1) is W_O,h W_UV,h, with W_O,h
+ * the d_v columns of W_O that take head h's output (fp32 accumulate, rounded
+ * to the dtype). A one-time weight preparation for mla_decode_folded. */
+mla_status mla_fold_output_weights(const mla_dims* dims, int32_t d_model, const void* w_uv, const void* w_o,
+                                   void* w_ouv, void* stream);
+
+/* Decode with the folded output weights: the scores and the latent output
+ * o_c of each head as in mla_decode_multi (absorbed form), then
+ * out[r] = sum_h W_OUV,h o_c[r, h], the attention layer's output, without
+ * forming the per-head outputs. Equal to mla_decode_multi followed by
+ * mla_output_project up to rounding (the fused weights are rounded to the
+ * dtype once).
+ *   w_ouv device [d_model, n_heads * d_c] (mla_fold_output_weights)
+ *   out   device [batch, q_len, d_model]
+ *   workspace at least mla_decode_folded_workspace_size bytes
+ * Needs the MFMA decode path (bf16, the DeepSeek-V3 latent shape, 64-token
+ * pages, paged cache); other shapes return MLA_ERR_UNSUPPORTED. Other bounds
+ * as for mla_decode_multi. batch == 0 is a no-op. */
+mla_status mla_decode_folded(const mla_dims* dims, int32_t batch, int32_t q_len, const void* q_nope,
+                             const void* q_pe, const void* w_uk, const void* w_ouv, int32_t d_model,
+                             const mla_cache* cache, void* out, void* workspace, size_t workspace_bytes,
+                             void* stream);
+
 /* Decode without allocation and without a caller workspace, for callers that
  * cannot allocate device memory: code under HIP graph capture, tight serving
  * loops, harnesses that forbid allocation. Arguments, checks and result are
@@ -251,6 +291,11 @@ mla_status mla_decode_fp8_workspace_size(const mla_dims* dims, int32_t batch, in
                                          int32_t max_context, size_t* bytes);
 mla_status mla_prefill_workspace_size(const mla_dims* dims, int32_t batch, int32_t seq_len,
                                       int32_t max_context, size_t* bytes);
+/* folded = 0: mla_output_project; folded != 0: a product with W_OUV */
+mla_status mla_output_workspace_size(const mla_dims* dims, int32_t n_rows, int32_t d_model, int32_t folded,
+                                     size_t* bytes);
+mla_status mla_decode_folded_workspace_size(const mla_dims* dims, int32_t batch, int32_t q_len,
+                                            int32_t max_context, int32_t d_model, size_t* bytes);
 
 /* Static description of a status code (never NULL). */
 const char* mla_status_string(mla_status status);

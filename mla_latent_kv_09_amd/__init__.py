@@ -23,6 +23,8 @@ __all__ = [
     "mla_project_workspace_size", "mla_decode_workspace_size", "mla_decode_multi_workspace_size",
     "mla_prefill_workspace_size", "Fp8Cache", "mla_fp8_page_bytes", "mla_quantize_fp8", "mla_decode_fp8",
     "mla_decode_fp8_workspace_size", "mla_decode_noalloc", "mla_noalloc_scratch_bytes",
+    "mla_output_project", "mla_output_workspace_size", "mla_fold_output_weights", "mla_decode_folded",
+    "mla_decode_folded_workspace_size",
     "mla_status_string", "mla_decode_path", "mla_prefill_path", "mla_version",
 ]
 
@@ -78,6 +80,14 @@ def library():
         lib.mla_decode_multi.argtypes = [pd, i32, i32, vp, vp, vp, vp, pc, vp, vp, sz, vp]
         lib.mla_prefill.argtypes = [pd, i32, i32, vp, vp, vp, vp, pc, vp, vp, sz, vp]
         lib.mla_decode_fp8.argtypes = [pd, i32, i32, vp, vp, vp, vp, pc, vp, vp, sz, vp]
+        lib.mla_output_project.argtypes = [pd, i32, i32, vp, vp, vp, vp, sz, vp]
+        lib.mla_fold_output_weights.argtypes = [pd, i32, vp, vp, vp, vp]
+        lib.mla_decode_folded.argtypes = [pd, i32, i32, vp, vp, vp, vp, i32, pc, vp, vp, sz, vp]
+        lib.mla_output_workspace_size.argtypes = [pd, i32, i32, i32, ctypes.POINTER(sz)]
+        lib.mla_decode_folded_workspace_size.argtypes = [pd, i32, i32, i32, i32, ctypes.POINTER(sz)]
+        for f in ("mla_output_project", "mla_fold_output_weights", "mla_decode_folded", "mla_output_workspace_size",
+                  "mla_decode_folded_workspace_size"):
+            getattr(lib, f).restype = ctypes.c_int
         lib.mla_decode_noalloc.argtypes = [pd, i32, i32, vp, vp, vp, vp, pc, vp, vp]
         lib.mla_decode_noalloc.restype = ctypes.c_int
         lib.mla_noalloc_scratch_bytes.argtypes = []
@@ -369,6 +379,79 @@ def mla_decode_multi(dims, q_nope, q_pe, w_uk, w_uv, cache: Cache, out=None, wor
                                    w_uv.data_ptr(), ctypes.byref(cc), out.data_ptr(),
                                    ws.data_ptr() if ws is not None else None, nbytes, _stream(stream)),
         "mla_decode_multi")
+    return out
+
+
+def mla_output_workspace_size(dims, n_rows: int, d_model: int, folded: bool = False) -> int:
+    n = ctypes.c_size_t(0)
+    _ok(library().mla_output_workspace_size(ctypes.byref(Dims.of(dims).c()), n_rows, d_model, int(folded),
+                                            ctypes.byref(n)), "mla_output_workspace_size")
+    return n.value
+
+
+def mla_output_project(dims, attn_out, w_o, out=None, workspace=None, stream=None):
+    """W_O applied to the concatenated per-head outputs: attn_out [n, H, d_v],
+    w_o [d_model, H*d_v]; returns out [n, d_model]."""
+    d = Dims.of(dims)
+    n = attn_out.shape[0]
+    d_model = w_o.shape[0]
+    dt = d.torch_dtype
+    _need(attn_out, "attn_out", (n, d.n_heads, d.d_v), dt)
+    _need(w_o, "w_o", (d_model, d.n_heads * d.d_v), dt)
+    if out is None:
+        out = torch.empty((n, d_model), dtype=dt, device=attn_out.device)
+    _need(out, "out", (n, d_model), dt)
+    ws, nbytes = _workspace(mla_output_workspace_size(d, n, d_model), attn_out.device, workspace)
+    _ok(library().mla_output_project(ctypes.byref(d.c()), n, d_model, attn_out.data_ptr(), w_o.data_ptr(),
+                                     out.data_ptr(), ws.data_ptr() if ws is not None else None, nbytes,
+                                     _stream(stream)), "mla_output_project")
+    return out
+
+
+def mla_fold_output_weights(dims, w_uv, w_o, w_ouv=None, stream=None):
+    """W_OUV [d_model, H*d_c] with column block h = W_O,h W_UV,h."""
+    d = Dims.of(dims)
+    d_model = w_o.shape[0]
+    dt = d.torch_dtype
+    _need(w_uv, "w_uv", (d.n_heads * d.d_v, d.d_c), dt)
+    _need(w_o, "w_o", (d_model, d.n_heads * d.d_v), dt)
+    if w_ouv is None:
+        w_ouv = torch.empty((d_model, d.n_heads * d.d_c), dtype=dt, device=w_o.device)
+    _need(w_ouv, "w_ouv", (d_model, d.n_heads * d.d_c), dt)
+    _ok(library().mla_fold_output_weights(ctypes.byref(d.c()), d_model, w_uv.data_ptr(), w_o.data_ptr(),
+                                          w_ouv.data_ptr(), _stream(stream)), "mla_fold_output_weights")
+    return w_ouv
+
+
+def mla_decode_folded_workspace_size(dims, batch: int, q_len: int, max_context: int, d_model: int) -> int:
+    n = ctypes.c_size_t(0)
+    _ok(library().mla_decode_folded_workspace_size(ctypes.byref(Dims.of(dims).c()), batch, q_len, max_context,
+                                                   d_model, ctypes.byref(n)), "mla_decode_folded_workspace_size")
+    return n.value
+
+
+def mla_decode_folded(dims, q_nope, q_pe, w_uk, w_ouv, cache: Cache, out=None, workspace=None, stream=None):
+    """Decode whose output is the layer output through the folded weights:
+    q_nope [B, q_len, H, d_nope]; returns out [B, q_len, d_model]."""
+    d = Dims.of(dims)
+    B, Q = q_nope.shape[:2]
+    d_model = w_ouv.shape[0]
+    dt = d.torch_dtype
+    _need(q_nope, "q_nope", (B, Q, d.n_heads, d.d_nope), dt)
+    _need(q_pe, "q_pe", (B, Q, d.n_heads, d.d_rope), dt)
+    _need(w_uk, "w_uk", (d.n_heads * d.d_nope, d.d_c), dt)
+    _need(w_ouv, "w_ouv", (d_model, d.n_heads * d.d_c), dt)
+    _check_cache(cache, d, B)
+    if out is None:
+        out = torch.empty((B, Q, d_model), dtype=dt, device=q_nope.device)
+    _need(out, "out", (B, Q, d_model), dt)
+    ws, nbytes = _workspace(mla_decode_folded_workspace_size(d, B, Q, cache.max_context, d_model), q_nope.device,
+                            workspace)
+    cc = cache.c()
+    _ok(library().mla_decode_folded(ctypes.byref(d.c()), B, Q, q_nope.data_ptr(), q_pe.data_ptr(), w_uk.data_ptr(),
+                                    w_ouv.data_ptr(), d_model, ctypes.byref(cc), out.data_ptr(),
+                                    ws.data_ptr() if ws is not None else None, nbytes, _stream(stream)),
+        "mla_decode_folded")
     return out
 
 

@@ -752,6 +752,9 @@ __global__ __launch_bounds__(SPLIT_THREADS, 1) void k_split(int H, int B, int q_
 //      split loads of a thread issued together; bf16 into LDS
 //   3. out^T[v, b] = sum_c W_UV[h*128 + v, c] o_c[b, c] on MFMA; each lane ends
 //      with 4 consecutive outputs of one sequence (one 8-byte store)
+// With UV false, step 3 is left out and o_c itself is written, as out
+// [B, H, 512] bf16, for an output projection with W_UV folded into W_O.
+template <bool UV>
 __global__ __launch_bounds__(256) void k_combine_uv(int H, int B, int q_len, int splits, int pps,
                                                     const int32_t* __restrict__ ctx_lens,
                                                     const bf16* __restrict__ part_o,
@@ -779,12 +782,15 @@ __global__ __launch_bounds__(256) void k_combine_uv(int H, int B, int q_len, int
   typedef __attribute__((ext_vector_type(2))) float f32x2_t;
   f32x2_t ml_q = {-INFINITY, 0.f};
   if (q < splits && b < B) ml_q = *(const f32x2_t*)(ml + 2 * q);  // used only if q < ns
-  const bf16* wv = w_uv + (size_t)h * DV * DC;
   u32x4 wf[DC / 32][2];
+  if constexpr (UV) {
+    const bf16* wv = w_uv + (size_t)h * DV * DC;
 #pragma unroll
-  for (int ks = 0; ks < DC / 32; ++ks)
+    for (int ks = 0; ks < DC / 32; ++ks)
 #pragma unroll
-    for (int mt = 0; mt < 2; ++mt) wf[ks][mt] = *(const u32x4*)(wv + (size_t)(32 * w + 16 * mt + i16) * DC + 32 * ks + 8 * G);
+      for (int mt = 0; mt < 2; ++mt)
+        wf[ks][mt] = *(const u32x4*)(wv + (size_t)(32 * w + 16 * mt + i16) * DC + 32 * ks + 8 * G);
+  }
   {
     const int ns = b < B && len > 0 ? ((len + PAGE - 1) / PAGE + pps - 1) / pps : 0;
     float M = q < ns ? ml_q[0] : -INFINITY;
@@ -843,6 +849,16 @@ __global__ __launch_bounds__(256) void k_combine_uv(int H, int B, int q_len, int
     }
   }
   __syncthreads();
+  if constexpr (!UV) {
+    // o_c rows of the 16 sequences: 16 threads per row, 64 bytes each
+    const int r = tid >> 4, q = tid & 15, b = b0 + r;
+    if (b < B) {
+      bf16* dst = out + ((size_t)b * H + h) * DC + 32 * q;
+#pragma unroll
+      for (int u = 0; u < 4; ++u) *(u32x4*)(dst + 8 * u) = *(const u32x4*)&oc[r * LDO + 32 * q + 8 * u];
+    }
+    return;
+  }
   // wave w: outputs v = 32w .. 32w+31 (two 16-row tiles), all 16 sequences
   f32x4 acc[2] = {};
 #pragma unroll
@@ -895,8 +911,12 @@ hipError_t decode_combine(const mla_dims& d, int rows, int q_len, int splits, in
   const int nbt = (rows + 15) / 16;
   const int hpad = (H + 7) / 8 * 8;
   ProfScope ps(prof_name, s);
-  hipLaunchKernelGGL(k_combine_uv, dim3(hpad * nbt), dim3(256), 0, s, H, rows, q_len, splits, pps, ctx_lens,
-                     (const bf16*)part_o, part_ml, (const bf16*)w_uv, (bf16*)out);
+  if (w_uv)
+    hipLaunchKernelGGL(k_combine_uv<true>, dim3(hpad * nbt), dim3(256), 0, s, H, rows, q_len, splits, pps, ctx_lens,
+                       (const bf16*)part_o, part_ml, (const bf16*)w_uv, (bf16*)out);
+  else
+    hipLaunchKernelGGL(k_combine_uv<false>, dim3(hpad * nbt), dim3(256), 0, s, H, rows, q_len, splits, pps,
+                       ctx_lens, (const bf16*)part_o, part_ml, nullptr, (bf16*)out);
   return hipGetLastError();
 }
 
@@ -910,6 +930,7 @@ size_t decode_fast_workspace(const mla_dims& d, int batch, int q_len, int max_co
   return ws_layout(d.n_heads, batch * q_len, p.splits).total;
 }
 
+// w_uv == nullptr: out receives the latent output o_c [rows, H, 512] instead
 hipError_t decode_fast(const mla_dims& d, float scale, int n_seq, int q_len, int max_context, const void* q_nope,
                        const void* q_pe, const void* w_uk, const void* w_uv, const CacheView& c, void* out,
                        void* ws, size_t ws_bytes, hipStream_t s) {

@@ -1,0 +1,214 @@
+// Output side of the attention layer: the output projection W_O
+// ([d_model, n_heads * d_v]; head h's output feeds columns h*d_v .. +d_v) and
+// its fold with W_UV ("DeepSeek-V2 paper digest" §2.2: the value up-projection
+// W_UV can be absorbed into W_O, fused once before inference, so the latent
+// output o_c of each head goes straight into the layer output).
+//
+//   k_fold_wo      W_OUV[:, h*d_c + c] = sum_v W_O[:, h*d_v + v] W_UV[h*d_v + v, c]
+//                  (one-time weight preparation; fp32 FMA, any dims)
+//   k_rowgemm      partial[s][m][n] = sum over the s-th slice of k of
+//                  X[m][k] W[n][k] for few rows m (decode: one row per query):
+//                  16x16x32 bf16 MFMA with both operands loaded straight from
+//                  memory; the weight streams from HBM once, split over k so
+//                  that enough workgroups stream it at once
+//   k_rowgemm_sum  out[m][n] = sum_s partial[s][m][n], rounded to bf16
+#include <math.h>
+
+#include "common.h"
+#include "launch.h"
+
+namespace mla {
+namespace {
+
+// block: 64 output rows j x 64 latent columns c of head h = blockIdx.z; v in
+// steps of 32 through LDS, 4 x 4 outputs per thread
+template <typename T>
+__global__ __launch_bounds__(256) void k_fold_wo(int d_model, int H, int dv, int dc, const T* __restrict__ w_uv,
+                                                 const T* __restrict__ w_o, T* __restrict__ w_ouv) {
+  __shared__ float As[32][65];  // W_O[j0 + r, h*dv + v0 + kk] at [kk][r]
+  __shared__ float Bs[32][65];  // W_UV[h*dv + v0 + kk, c0 + r] at [kk][r]
+  const int h = blockIdx.z, j0 = blockIdx.y * 64, c0 = blockIdx.x * 64;
+  const int tx = threadIdx.x % 16, ty = threadIdx.x / 16;
+  const size_t ld_o = (size_t)H * dv;
+  float acc[4][4] = {};
+  for (int v0 = 0; v0 < dv; v0 += 32) {
+    for (int i = threadIdx.x; i < 64 * 32; i += 256) {
+      const int r = i / 32, kk = i % 32, j = j0 + r, v = v0 + kk;
+      As[kk][r] = (j < d_model && v < dv) ? ld<T>(w_o + (size_t)j * ld_o + (size_t)h * dv + v) : 0.f;
+    }
+    for (int i = threadIdx.x; i < 64 * 32; i += 256) {
+      const int kk = i / 64, r = i % 64, v = v0 + kk, c = c0 + r;
+      Bs[kk][r] = (v < dv && c < dc) ? ld<T>(w_uv + ((size_t)h * dv + v) * dc + c) : 0.f;
+    }
+    __syncthreads();
+#pragma unroll 8
+    for (int kk = 0; kk < 32; ++kk) {
+      float av[4], bv[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        av[i] = As[kk][ty * 4 + i];
+        bv[i] = Bs[kk][tx * 4 + i];
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[i][j] = fmaf(av[i], bv[j], acc[i][j]);
+    }
+    __syncthreads();
+  }
+  const size_t ld_ouv = (size_t)H * dc;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int j = j0 + ty * 4 + i;
+    if (j >= d_model) continue;
+#pragma unroll
+    for (int jj = 0; jj < 4; ++jj) {
+      const int c = c0 + tx * 4 + jj;
+      if (c < dc) st<T>(w_ouv + (size_t)j * ld_ouv + (size_t)h * dc + c, acc[i][jj]);
+    }
+  }
+}
+
+constexpr int RG_N = 64;      // weight rows per workgroup (16 per wave)
+constexpr int RG_M = 64;      // activation rows per workgroup
+constexpr int RG_STEP = 128;  // k per loop iteration (4 MFMA steps of 32)
+
+// grid (ceil(N / 64), splits, ceil(M / 64)); 4 waves. Wave w owns weight rows
+// n0 + 16w .. +15 and all 64 activation rows of the tile: C^T[n, m] as four
+// 16 x 16 tiles, A = W rows (lane: row n0 + l%16, k + 8(l/16) .. +7), B = X rows
+// (lane: row m0 + 16t + l%16, the same k). Rows past M or N are clamped to the
+// last row (read, never stored).
+__global__ __launch_bounds__(256) void k_rowgemm(int M, int N, int K, int kc, const bf16* __restrict__ x,
+                                                 const bf16* __restrict__ wt, float* __restrict__ part) {
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, i16 = lane & 15, G = lane >> 4;
+  const int n0 = blockIdx.x * RG_N + 16 * w, sp = blockIdx.y, m0 = blockIdx.z * RG_M;
+  const int k_begin = sp * kc, k_end = min(K, k_begin + kc);
+  const bf16* wrow = wt + (size_t)min(n0 + i16, N - 1) * K + 8 * G;
+  const bf16* xrow[4];
+#pragma unroll
+  for (int t = 0; t < 4; ++t) xrow[t] = x + (size_t)min(m0 + 16 * t + i16, M - 1) * K + 8 * G;
+  const int mt = min(4, (M - m0 + 15) / 16);  // activation tiles with any row
+  f32x4 acc[4] = {};
+  for (int k = k_begin; k < k_end; k += RG_STEP) {
+    u32x4 a[4], b[4][4];
+    // the weight (the HBM stream) first, then the activations (cached)
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+      a[u] = k + 32 * u < k_end ? *(const u32x4*)(wrow + k + 32 * u) : (u32x4){0, 0, 0, 0};
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+#pragma unroll
+      for (int t = 0; t < 4; ++t)
+        b[u][t] = (t < mt && k + 32 * u < k_end) ? *(const u32x4*)(xrow[t] + k + 32 * u) : (u32x4){0, 0, 0, 0};
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+#pragma unroll
+      for (int t = 0; t < 4; ++t)
+        if (t < mt)
+          acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a[u]),
+                                                           __builtin_bit_cast(bf16x8_t, b[u][t]), acc[t], 0, 0, 0);
+  }
+  // lane holds C^T[n0 + 4G + r][m0 + 16t + l%16]: 4 consecutive n of one m
+  const int n = n0 + 4 * G;
+#pragma unroll
+  for (int t = 0; t < 4; ++t) {
+    const int m = m0 + 16 * t + i16;
+    if (t < mt && m < M && n < N) *(f32x4*)(part + ((size_t)sp * M + m) * N + n) = acc[t];
+  }
+}
+
+// out[m, n .. n+3] = sum_s part[s][m][n .. n+3] (N % 4 == 0)
+__global__ __launch_bounds__(256) void k_rowgemm_sum(int M, int N, int splits, const float* __restrict__ part,
+                                                     bf16* __restrict__ out) {
+  const size_t i = ((size_t)blockIdx.x * 256 + threadIdx.x) * 4, total = (size_t)M * N;
+  if (i >= total) return;
+  f32x4 s = *(const f32x4*)(part + i);
+  for (int sp = 1; sp < splits; ++sp) {
+    const f32x4 v = *(const f32x4*)(part + (size_t)sp * total + i);
+    s[0] += v[0];
+    s[1] += v[1];
+    s[2] += v[2];
+    s[3] += v[3];
+  }
+  typedef __attribute__((ext_vector_type(4))) __bf16 bf16x4_t;
+  *(bf16x4_t*)(out + i) = (bf16x4_t){(__bf16)s[0], (__bf16)s[1], (__bf16)s[2], (__bf16)s[3]};
+}
+
+struct RowPlan {
+  int splits, kc;
+};
+
+// enough workgroups to stream the weight from every CU (about 2048), with k
+// slices of at least 512 so the partial sums stay small against the weight
+RowPlan row_plan(int M, int N, int K) {
+  const int tiles = ((N + RG_N - 1) / RG_N) * ((M + RG_M - 1) / RG_M);
+  int splits = (2048 + tiles - 1) / tiles;
+  const int max_splits = (K + 511) / 512;
+  splits = splits < 1 ? 1 : (splits > max_splits ? max_splits : splits);
+  int kc = (K + splits - 1) / splits;
+  kc = (kc + RG_STEP - 1) / RG_STEP * RG_STEP;
+  RowPlan p;
+  p.kc = kc;
+  p.splits = (K + kc - 1) / kc;
+  return p;
+}
+
+bool row_path(const mla_dims& d, int M, int N, int K) {
+  return d.dtype == MLA_BF16 && M <= 256 && K % 32 == 0 && N % 4 == 0;
+}
+
+}  // namespace
+
+size_t rows_times_weight_workspace(const mla_dims& d, int M, int N, int K) {
+  if (!row_path(d, M, N, K)) return 0;
+  const RowPlan p = row_plan(M, N, K);
+  return (size_t)p.splits * M * N * sizeof(float);
+}
+
+hipError_t rows_times_weight(const mla_dims& d, int M, int N, int K, const void* x, const void* w, void* out,
+                             void* ws, size_t ws_bytes, const char* prof_name, hipStream_t s) {
+  ProfScope ps(prof_name, s);
+  if (row_path(d, M, N, K)) {
+    const RowPlan p = row_plan(M, N, K);
+    if (ws_bytes < (size_t)p.splits * M * N * sizeof(float)) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(k_rowgemm, dim3((N + RG_N - 1) / RG_N, p.splits, (M + RG_M - 1) / RG_M), dim3(256), 0, s, M, N,
+                       K, p.kc, (const bf16*)x, (const bf16*)w, (float*)ws);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    const size_t quads = (size_t)M * N / 4;
+    hipLaunchKernelGGL(k_rowgemm_sum, dim3((unsigned)((quads + 255) / 256)), dim3(256), 0, s, M, N, p.splits,
+                       (const float*)ws, (bf16*)out);
+    return hipGetLastError();
+  }
+  if (d.dtype == MLA_BF16 && gemm_fast_supported(M, N, K)) {
+    GemmArgs g{};
+    g.M = M;
+    g.N = N;
+    g.K = K;
+    g.a = (const bf16*)x;
+    g.lda = K;
+    g.b0 = g.b1 = (const bf16*)w;
+    g.n_split = N;
+    g.ldb = K;
+    g.c0 = g.c1 = (bf16*)out;
+    g.ldc0 = g.ldc1 = N;
+    g.c_split = N;
+    return gemm_fast(g, 0, s);
+  }
+  return gemm_nt_generic(d.dtype, d.dtype, d.dtype, M, N, K, x, K, w, w, N, K, out, N, s);
+}
+
+hipError_t fold_output_weights(const mla_dims& d, int d_model, const void* w_uv, const void* w_o, void* w_ouv,
+                               hipStream_t s) {
+  ProfScope ps("mla_fold_output_weights", s);
+  const dim3 grid((d.d_c + 63) / 64, (d_model + 63) / 64, d.n_heads);
+  if (d.dtype == MLA_BF16)
+    hipLaunchKernelGGL(k_fold_wo<bf16>, grid, dim3(256), 0, s, d_model, d.n_heads, d.d_v, d.d_c, (const bf16*)w_uv,
+                       (const bf16*)w_o, (bf16*)w_ouv);
+  else
+    hipLaunchKernelGGL(k_fold_wo<float>, grid, dim3(256), 0, s, d_model, d.n_heads, d.d_v, d.d_c,
+                       (const float*)w_uv, (const float*)w_o, (float*)w_ouv);
+  return hipGetLastError();
+}
+
+}  // namespace mla

@@ -62,7 +62,8 @@ hipError_t decode_fast(const mla_dims& d, float scale, int n_seq, int q_len, int
 // Pieces of the decode path that the FP8-cache decode shares (rows = query
 // rows, n_seq * q_len). decode_absorb writes q~ [rows, H, 576] bf16;
 // decode_combine merges per-split partials [H][rows][splits][512] bf16 and
-// (m, l) [H][rows][splits][2] and applies W_UV.
+// (m, l) [H][rows][splits][2] and applies W_UV (w_uv == nullptr: writes the
+// merged latent output o_c [rows, H, 512] bf16 instead; so does decode_fast).
 void decode_plan(int rows, int max_context, int q_len, int* pages_per_split, int* splits);
 hipError_t decode_absorb(const mla_dims& d, float scale, int rows, int q_len, const void* q_nope, const void* q_pe,
                          const void* w_uk, const int32_t* ctx_lens, void* qt, const char* prof_name, hipStream_t s);
@@ -116,6 +117,17 @@ bool gemm_fast_supported(int M, int N, int K);
 // 2: c0[b][h][t / 64][d][t % 64] (values transposed in 64-token blocks);
 // 3: c0[b][h][t][d] (head-major)
 hipError_t gemm_fast(const GemmArgs& g, int epi, hipStream_t s);
+
+// ---- output side: W_O, and W_UV folded into W_O ---------------------------
+// out[m, n] = sum_k X[m, k] W[n, k] for X [M, K] and W [N, K] (K-contiguous,
+// the dims' dtype): the MFMA row GEMM (bf16, K % 32 == 0, N % 4 == 0) for few
+// rows, the tiled MFMA GEMM for many, the generic kernel otherwise.
+size_t rows_times_weight_workspace(const mla_dims& d, int M, int N, int K);
+hipError_t rows_times_weight(const mla_dims& d, int M, int N, int K, const void* x, const void* w, void* out,
+                             void* ws, size_t ws_bytes, const char* prof_name, hipStream_t s);
+// W_OUV[:, h*d_c .. h*d_c + d_c) = W_O[:, h*d_v .. h*d_v + d_v) W_UV,h
+hipError_t fold_output_weights(const mla_dims& d, int d_model, const void* w_uv, const void* w_o, void* w_ouv,
+                               hipStream_t s);
 
 // ---- MFMA prefill attention (bf16, DeepSeek-V3 latent shape) --------------
 bool prefill_fast_supported(const mla_dims& d, const CacheView& c);

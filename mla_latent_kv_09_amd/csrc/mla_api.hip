@@ -305,6 +305,108 @@ mla_status mla_decode_fp8(const mla_dims* d, int32_t batch, int32_t q_len, const
                                     out, ws, ws_bytes, s));
 }
 
+// ---- output side: W_O, and W_UV folded into W_O ---------------------------
+
+static bool d_model_ok(int32_t d_model) { return d_model >= 1 && d_model <= 65536; }
+
+mla_status mla_output_workspace_size(const mla_dims* d, int32_t n_rows, int32_t d_model, int32_t folded,
+                                     size_t* bytes) {
+  mla_status st = check_dims(d);
+  if (st != MLA_OK) return st;
+  if (!bytes) return MLA_ERR_NULL_ARG;
+  if (n_rows < 0 || !d_model_ok(d_model)) return MLA_ERR_BAD_SHAPE;
+  const int K = d->n_heads * (folded ? d->d_c : d->d_v);
+  *bytes = n_rows > 0 ? mla::rows_times_weight_workspace(*d, n_rows, d_model, K) : 0;
+  return MLA_OK;
+}
+
+mla_status mla_output_project(const mla_dims* d, int32_t n_rows, int32_t d_model, const void* attn_out,
+                              const void* w_o, void* out, void* ws, size_t ws_bytes, void* stream) {
+  mla_status st = check_dims(d);
+  if (st != MLA_OK) return st;
+  if (n_rows < 0 || !d_model_ok(d_model)) return MLA_ERR_BAD_SHAPE;
+  if (n_rows == 0) return MLA_OK;
+  if (!attn_out || !w_o || !out) return MLA_ERR_NULL_ARG;
+  if (!aligned(attn_out, 16) || !aligned(w_o, 16) || !aligned(out, 16)) return MLA_ERR_ALIGNMENT;
+  const int K = d->n_heads * d->d_v;
+  const size_t need = mla::rows_times_weight_workspace(*d, n_rows, d_model, K);
+  if ((st = check_ws(ws, ws_bytes, need)) != MLA_OK) return st;
+  if (trace_on()) fprintf(stderr, "[mla] output_project rows=%d d_model=%d K=%d ws=%zu\n", n_rows, d_model, K, need);
+  return hip_status(mla::rows_times_weight(*d, n_rows, d_model, K, attn_out, w_o, out, ws, ws_bytes,
+                                           "mla_output_project", (hipStream_t)stream));
+}
+
+mla_status mla_fold_output_weights(const mla_dims* d, int32_t d_model, const void* w_uv, const void* w_o,
+                                   void* w_ouv, void* stream) {
+  mla_status st = check_dims(d);
+  if (st != MLA_OK) return st;
+  if (!d_model_ok(d_model)) return MLA_ERR_BAD_SHAPE;
+  if (!w_uv || !w_o || !w_ouv) return MLA_ERR_NULL_ARG;
+  if (!aligned(w_uv, 16) || !aligned(w_o, 16) || !aligned(w_ouv, 16)) return MLA_ERR_ALIGNMENT;
+  if (trace_on()) fprintf(stderr, "[mla] fold_output_weights d_model=%d heads=%d\n", d_model, d->n_heads);
+  return hip_status(mla::fold_output_weights(*d, d_model, w_uv, w_o, w_ouv, (hipStream_t)stream));
+}
+
+// workspace of the folded decode: the decode's own, then o_c [rows, H, d_c]
+// bf16, then the output GEMM's partial sums
+static size_t folded_ws(const mla_dims* d, int32_t batch, int32_t q_len, int32_t max_context, int32_t d_model,
+                        size_t* oc_off, size_t* gemm_off) {
+  const size_t a = (mla::decode_fast_workspace(*d, batch, q_len, max_context) + 255) & ~(size_t)255;
+  const int64_t rows = (int64_t)batch * q_len;
+  const size_t b = ((size_t)rows * d->n_heads * d->d_c * 2 + 255) & ~(size_t)255;
+  *oc_off = a;
+  *gemm_off = a + b;
+  return a + b + mla::rows_times_weight_workspace(*d, (int)rows, d_model, d->n_heads * d->d_c);
+}
+
+mla_status mla_decode_folded_workspace_size(const mla_dims* d, int32_t batch, int32_t q_len, int32_t max_context,
+                                            int32_t d_model, size_t* bytes) {
+  mla_status st = check_dims(d);
+  if (st != MLA_OK) return st;
+  if (!bytes) return MLA_ERR_NULL_ARG;
+  if (batch < 0 || max_context < 0 || q_len < 1 || q_len > MAX_Q_LEN || !d_model_ok(d_model))
+    return MLA_ERR_BAD_SHAPE;
+  if ((int64_t)batch * q_len > MAX_QUERY_ROWS) return MLA_ERR_BAD_SHAPE;
+  size_t o1, o2;
+  *bytes = (fast_dims(d) && batch > 0 && max_context > 0 && mla::decode_fast_context_ok(max_context))
+               ? folded_ws(d, batch, q_len, max_context, d_model, &o1, &o2)
+               : 0;
+  return MLA_OK;
+}
+
+mla_status mla_decode_folded(const mla_dims* d, int32_t batch, int32_t q_len, const void* q_nope, const void* q_pe,
+                             const void* w_uk, const void* w_ouv, int32_t d_model, const mla_cache* cache, void* out,
+                             void* ws, size_t ws_bytes, void* stream) {
+  mla_status st = check_dims(d);
+  if (st != MLA_OK) return st;
+  if (batch < 0 || q_len < 1 || q_len > MAX_Q_LEN || !d_model_ok(d_model)) return MLA_ERR_BAD_SHAPE;
+  if ((int64_t)batch * q_len > MAX_QUERY_ROWS) return MLA_ERR_BAD_SHAPE;
+  if (batch == 0) return MLA_OK;
+  if (!q_nope || !q_pe || !w_uk || !w_ouv || !out) return MLA_ERR_NULL_ARG;
+  if (!aligned(q_nope, 16) || !aligned(q_pe, 16) || !aligned(w_uk, 16) || !aligned(w_ouv, 16) ||
+      !aligned(out, 16))
+    return MLA_ERR_ALIGNMENT;
+  CacheView v{};
+  if ((st = check_cache(cache, &v)) != MLA_OK) return st;
+  if (q_len > cache->max_context) return MLA_ERR_BAD_SHAPE;
+  if (!(mla::decode_fast_supported(*d, v) && mla::decode_fast_context_ok(cache->max_context)))
+    return MLA_ERR_UNSUPPORTED;
+  size_t oc_off, gemm_off;
+  const size_t need = folded_ws(d, batch, q_len, cache->max_context, d_model, &oc_off, &gemm_off);
+  if ((st = check_ws(ws, ws_bytes, need)) != MLA_OK) return st;
+  hipStream_t s = (hipStream_t)stream;
+  if (trace_on())
+    fprintf(stderr, "[mla] decode_folded batch=%d q_len=%d heads=%d d_model=%d ws=%zu\n", batch, q_len, d->n_heads,
+            d_model, need);
+  char* w = (char*)ws;
+  hipError_t e = mla::decode_fast(*d, scale_of(d), batch, q_len, cache->max_context, q_nope, q_pe, w_uk, nullptr, v,
+                                  w + oc_off, ws, oc_off, s);
+  if (e != hipSuccess) return MLA_ERR_HIP;
+  const int rows = batch * q_len;
+  return hip_status(mla::rows_times_weight(*d, rows, d_model, d->n_heads * d->d_c, w + oc_off, w_ouv, out,
+                                           w + gemm_off, need - gemm_off, "mla_output_project_folded", s));
+}
+
 mla_status mla_prefill(const mla_dims* d, int32_t batch, int32_t seq_len, const void* q_nope, const void* q_pe,
                        const void* w_uk, const void* w_uv, const mla_cache* cache, void* out, void* ws,
                        size_t ws_bytes, void* stream) {
