@@ -56,7 +56,11 @@ WORKLOAD_NAMES = {
        "per sequence)",
     7: "mla_decode_fp8 B=64 H=128 L=8192 d_c=512 d_rope=64, FP8 (E4M3, per-token scale) cache of workload 3, "
        "64-token pages",
+    8: "mla_decode_folded (W_UV folded into W_O, d_model=7168) on workload 3's inputs, against mla_decode + "
+       "mla_output_project",
 }
+D_MODEL = 7168                 # the DeepSeek-V3 hidden size (the prefill workload's d_model)
+SWEEP_CONTEXTS = (1024, 2048, 4096, 8192, 16384, 32768)
 FP8_TOKEN_BYTES = 641          # one cached token in the FP8 cache: 512 codes + 64 bf16 + 1 scale byte
 
 
@@ -73,6 +77,9 @@ def parse():
     ap.add_argument("--workload", type=int, default=3, choices=sorted(WORKLOAD_NAMES))
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="budget of the CPU oracle sample")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle leg")
+    ap.add_argument("--sweep", action="store_true",
+                    help="decode over contexts 1K..32K (B=64, H=128, the DeepSeek-V3 shape): one JSON line per "
+                         "context length")
     ap.add_argument("--copy-bytes", type=int, default=0,
                     help="instead of a workload, run 5 device-to-device copies of this many bytes "
                          "(the known-size kernel that calibrates the HBM byte counters)")
@@ -285,6 +292,150 @@ def cold_pass(step, lib, kernel_name, n):
             "step_us_min": round(float(np.min(steps_us)), 2), "split_us_median": round(float(np.median(kern_us)), 2)}
 
 
+def _timed(step, steps, warmup, lib, names):
+    """warmup untimed steps, then steps timed between two events (barrier and
+    synchronise on both sides), then a 10-step pass with events around every
+    library launch; returns (ms per step, {kernel: us per launch})."""
+    import torch
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ev0.record(stream)
+    for _ in range(steps):
+        step()
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    ms = ev0.elapsed_time(ev1) / steps
+    lib.mla_profile_only(None)
+    lib.mla_profile_begin()
+    for _ in range(10):
+        step()
+    torch.cuda.synchronize()
+    k = profile_end(lib)
+    return ms, {n: round(v[0] / v[1] * 1e3, 2) for n, v in k.items()}
+
+
+def output_bench(args):
+    """Workload 8: decode of workload 3's inputs to the attention layer's
+    output [B, d_model] in the two orders of the output side: W_UV folded into
+    W_O ("DeepSeek-V2 paper digest" 2.2; mla_decode_folded with the folded
+    weights prepared once, untimed) and the per-head W_UV then W_O
+    (mla_decode + mla_output_project). The line's value is the folded path."""
+    import torch
+    import mla_latent_kv_09_amd as mla
+    from synth import draw_output_weights, to_torch, workload
+
+    dev = "cuda:0"
+    case = workload(3)
+    c = case.cache
+    d = mla.Dims.of(case.dims)
+    B, H = case.batch, d.n_heads
+    cache = mla.Cache(to_torch(c.pool, dev), to_torch(c.context_lens, dev), int(c.context_lens.max()),
+                      to_torch(c.block_table, dev))
+    qn, qp = to_torch(case.q_nope, dev), to_torch(case.q_pe, dev)
+    w_uk, w_uv = to_torch(case.w_uk, dev), to_torch(case.w_uv, dev)
+    w_o = to_torch(draw_output_weights(1008, D_MODEL, H, d.d_v), dev)
+    w_ouv = mla.mla_fold_output_weights(d, w_uv, w_o)
+    ws_f = torch.empty(mla.mla_decode_folded_workspace_size(d, B, 1, cache.max_context, D_MODEL), dtype=torch.uint8,
+                       device=dev)
+    ws_d = torch.empty(mla.mla_decode_workspace_size(d, B, cache.max_context), dtype=torch.uint8, device=dev)
+    ws_o = torch.empty(max(mla.mla_output_workspace_size(d, B, D_MODEL), 1), dtype=torch.uint8, device=dev)
+    per_head = torch.empty((B, H, d.d_v), dtype=torch.bfloat16, device=dev)
+    y_f = torch.empty((B, 1, D_MODEL), dtype=torch.bfloat16, device=dev)
+    y_u = torch.empty((B, D_MODEL), dtype=torch.bfloat16, device=dev)
+    qn1, qp1 = qn.unsqueeze(1), qp.unsqueeze(1)
+    lib = mla.library()
+
+    def folded():
+        mla.mla_decode_folded(d, qn1, qp1, w_uk, w_ouv, cache, out=y_f, workspace=ws_f)
+
+    def unfolded():
+        mla.mla_decode(d, qn, qp, w_uk, w_uv, cache, out=per_head, workspace=ws_d)
+        mla.mla_output_project(d, per_head, w_o, out=y_u, workspace=ws_o)
+
+    ms_f, k_f = _timed(folded, args.steps, args.warmup, lib, None)
+    ms_u, k_u = _timed(unfolded, args.steps, args.warmup, lib, None)
+    sum_l = int(c.context_lens.astype(np.int64).sum())
+    gemm_f_bytes = D_MODEL * H * d.d_c * 2 + B * H * d.d_c * 2 + B * D_MODEL * 2
+    gemm_u_bytes = D_MODEL * H * d.d_v * 2 + B * H * d.d_v * 2 + B * D_MODEL * 2
+    dom = max(k_f, key=k_f.get)
+    dom_bytes = {"mla_output_project_folded": gemm_f_bytes, "mla_decode_split": sum_l * CACHE_ROW_BYTES}.get(dom)
+    roof = {"bound": "hbm", "achieved": None, "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": None, "traffic": None,
+            "kernel": dom, "kernel_us": k_f[dom]}
+    if dom_bytes:
+        roof["achieved"] = round(dom_bytes / (k_f[dom] * 1e-6) / 1e9, 1)
+        roof["frac"] = round(roof["achieved"] / HBM_PEAK_GBS, 4)
+        roof["algorithmic_bytes"] = dom_bytes
+    line = {
+        "metric": "MLA decode tokens/s to the layer output (W_UV folded into W_O), 1xMI355X",
+        "value": round(B / (ms_f * 1e-3), 1), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms_f, 5), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic (workload 3's seeded inputs; W_O std 1/sqrt(16384), seed 1008)",
+        "config": {"workload": WORKLOAD_NAMES[8], "batch": B, "heads": H, "d_model": D_MODEL,
+                   "cached_tokens": sum_l, "parallelism": "none (1 GPU)"},
+        "roofline": roof,
+        "folded": {"ms_per_step": round(ms_f, 5), "kernels_us": k_f,
+                   "output_gemm_bytes": gemm_f_bytes},
+        "unfolded": {"ms_per_step": round(ms_u, 5), "tokens_per_s": round(B / (ms_u * 1e-3), 1), "kernels_us": k_u,
+                     "output_gemm_bytes": gemm_u_bytes + D_MODEL * 0},
+        "fold_speedup": round(ms_u / ms_f, 3),
+    }
+    print(json.dumps(line), flush=True)
+
+
+def sweep_bench(args):
+    """Decode over contexts 1K .. 32K for B = 64 sequences of the DeepSeek-V3
+    shape (H = 128): one JSON line per context length with tokens/s and the
+    split kernel's fraction of the HBM roofline. The cache pool is drawn on the
+    GPU from a seeded torch generator (N(0,1), rounded to bf16 once) so the 2.4 GB
+    pool of the 32K point needs no host copy; queries and weights come from the
+    synthetic recipe. The bytes an MHA cache of the same heads would hold per
+    token (H (d_nope + d_rope + d_v) bf16 values) are given for comparison."""
+    import torch
+    import mla_latent_kv_09_amd as mla
+    from synth import Dims, make_decode_case, to_torch
+
+    dev = "cuda:0"
+    B, H = 64, 128
+    dims = Dims(H, 512, 64, 128, 128, softmax_scale=1.0 / math.sqrt(192.0))
+    small = make_decode_case(1009, B, dims, 64)   # queries and weights of the recipe; the cache is drawn below
+    d = mla.Dims.of(dims)
+    qn, qp = to_torch(small.q_nope, dev), to_torch(small.q_pe, dev)
+    w_uk, w_uv = to_torch(small.w_uk, dev), to_torch(small.w_uv, dev)
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(1009)
+    L_max = max(SWEEP_CONTEXTS)
+    pool = torch.randn((B * L_max // 64, 64, d.row), generator=gen, device=dev, dtype=torch.float32)
+    pool = pool.to(torch.bfloat16)
+    lib = mla.library()
+    mha_bytes = H * (d.d_nope + d.d_rope + d.d_v) * 2
+    for L in SWEEP_CONTEXTS:
+        n_pages = L // 64
+        table = torch.arange(B * n_pages, dtype=torch.int32, device=dev).view(B, n_pages)
+        cache = mla.Cache(pool, torch.full((B,), L, dtype=torch.int32, device=dev), L, table)
+        ws = torch.empty(mla.mla_decode_workspace_size(d, B, L), dtype=torch.uint8, device=dev)
+        out = torch.empty((B, H, d.d_v), dtype=torch.bfloat16, device=dev)
+
+        def step():
+            mla.mla_decode(d, qn, qp, w_uk, w_uv, cache, out=out, workspace=ws)
+
+        ms, k = _timed(step, args.steps, args.warmup, lib, None)
+        cache_bytes = B * L * CACHE_ROW_BYTES
+        split_us = k["mla_decode_split"]
+        print(json.dumps({
+            "metric": "MLA decode tokens/s, context sweep, 1xMI355X", "context": L, "batch": B, "heads": H,
+            "value": round(B / (ms * 1e-3), 1), "unit": "tokens/s", "steps": args.steps, "warmup": args.warmup,
+            "ms_per_step": round(ms, 5), "kernels_us": k,
+            "split_frac_hbm": round(cache_bytes / (split_us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+            "step_frac_hbm": round((cache_bytes + 2 * H * 128 * 512 * 2) / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+            "cache_bytes_per_token": CACHE_ROW_BYTES, "mha_cache_bytes_per_token": mha_bytes,
+            "data": "synthetic (cache N(0,1) from torch.Generator seed 1009 on the GPU; queries, weights seed 1009)",
+        }), flush=True)
+
+
 def prefill_bench(args):
     """Workload 5: one step = latent + query projection of B*S tokens (cache
     write) followed by causal prefill attention over them."""
@@ -372,6 +523,12 @@ def main():
         return
     if args.workload == 5:
         prefill_bench(args)
+        return
+    if args.sweep:
+        sweep_bench(args)
+        return
+    if args.workload == 8:
+        output_bench(args)
         return
 
     import torch

@@ -9,8 +9,8 @@
 //   k_rowgemm      partial[s][m][n] = sum over the s-th slice of k of
 //                  X[m][k] W[n][k] for few rows m (decode: one row per query):
 //                  16x16x32 bf16 MFMA with both operands loaded straight from
-//                  memory; the weight streams from HBM once, split over k so
-//                  that enough workgroups stream it at once
+//                  memory into registers; the weight streams from HBM once,
+//                  split over k so that enough workgroups stream it at once
 //   k_rowgemm_sum  out[m][n] = sum_s partial[s][m][n], rounded to bf16
 #include <math.h>
 
@@ -69,51 +69,90 @@ __global__ __launch_bounds__(256) void k_fold_wo(int d_model, int H, int dv, int
   }
 }
 
-constexpr int RG_N = 64;      // weight rows per workgroup (16 per wave)
-constexpr int RG_M = 64;      // activation rows per workgroup
-constexpr int RG_STEP = 128;  // k per loop iteration (4 MFMA steps of 32)
+constexpr int RG_N = 64;   // weight rows per workgroup
+constexpr int RG_M = 64;   // activation rows per workgroup
+constexpr int RG_K = 32;   // k per MFMA step
 
-// grid (ceil(N / 64), splits, ceil(M / 64)); 4 waves. Wave w owns weight rows
-// n0 + 16w .. +15 and all 64 activation rows of the tile: C^T[n, m] as four
-// 16 x 16 tiles, A = W rows (lane: row n0 + l%16, k + 8(l/16) .. +7), B = X rows
-// (lane: row m0 + 16t + l%16, the same k). Rows past M or N are clamped to the
-// last row (read, never stored).
+// grid (ceil(N / 64), splits, ceil(M / 64)); 4 waves. The workgroup computes
+// C^T[n, m] for 64 weight rows n and 64 activation rows m over its k slice;
+// wave w takes the slice's MFMA steps w, w + 4, ... with all 64 x 64 outputs
+// (4 x 4 tiles of 16 x 16: A = W rows, lane row n0 + 16i + l%16, k + 8(l/16)
+// .. +7; B = X rows, lane row m0 + 16t + l%16, the same k), so each weight
+// and activation fragment loaded feeds four MFMAs and the activations cost no
+// more bytes than the weight. The next step's fragments are requested before
+// the current step's MFMAs. The four waves' sums are added in LDS at the end.
+// Rows past M or N are clamped to the last row (read, never stored).
 __global__ __launch_bounds__(256) void k_rowgemm(int M, int N, int K, int kc, const bf16* __restrict__ x,
                                                  const bf16* __restrict__ wt, float* __restrict__ part) {
+  __shared__ __attribute__((aligned(16))) float red[RG_M * RG_N];  // [m][n], 16 KB
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, i16 = lane & 15, G = lane >> 4;
-  const int n0 = blockIdx.x * RG_N + 16 * w, sp = blockIdx.y, m0 = blockIdx.z * RG_M;
+  const int n0 = blockIdx.x * RG_N, sp = blockIdx.y, m0 = blockIdx.z * RG_M;
   const int k_begin = sp * kc, k_end = min(K, k_begin + kc);
-  const bf16* wrow = wt + (size_t)min(n0 + i16, N - 1) * K + 8 * G;
+  const int mt = min(4, (M - m0 + 15) / 16);  // activation tiles with any row
+  const bf16* wrow[4];
   const bf16* xrow[4];
 #pragma unroll
-  for (int t = 0; t < 4; ++t) xrow[t] = x + (size_t)min(m0 + 16 * t + i16, M - 1) * K + 8 * G;
-  const int mt = min(4, (M - m0 + 15) / 16);  // activation tiles with any row
-  f32x4 acc[4] = {};
-  for (int k = k_begin; k < k_end; k += RG_STEP) {
-    u32x4 a[4], b[4][4];
-    // the weight (the HBM stream) first, then the activations (cached)
+  for (int i = 0; i < 4; ++i) {
+    wrow[i] = wt + (size_t)min(n0 + 16 * i + i16, N - 1) * K + 8 * G;
+    xrow[i] = x + (size_t)min(m0 + 16 * i + i16, M - 1) * K + 8 * G;
+  }
+  f32x4 acc[4][4] = {};  // [weight tile i][activation tile t]
+  // weight fragments two steps ahead (the HBM stream), activations one (cached)
+  u32x4 a0[4], a1[4], a2[4], b0[4], b1[4];
+  auto load_w = [&](u32x4 (&a)[4], int k) {
 #pragma unroll
-    for (int u = 0; u < 4; ++u)
-      a[u] = k + 32 * u < k_end ? *(const u32x4*)(wrow + k + 32 * u) : (u32x4){0, 0, 0, 0};
+    for (int i = 0; i < 4; ++i) a[i] = k < k_end ? *(const u32x4*)(wrow[i] + k) : (u32x4){0, 0, 0, 0};
+  };
+  auto load_x = [&](u32x4 (&b)[4], int k) {
 #pragma unroll
-    for (int u = 0; u < 4; ++u)
+    for (int t = 0; t < 4; ++t) b[t] = (t < mt && k < k_end) ? *(const u32x4*)(xrow[t] + k) : (u32x4){0, 0, 0, 0};
+  };
+  constexpr int STRIDE = 4 * RG_K;  // this wave's steps
+  int k = k_begin + RG_K * w;
+  load_w(a0, k);
+  load_x(b0, k);
+  load_w(a1, k + STRIDE);
+  for (; k < k_end; k += STRIDE) {
+    load_w(a2, k + 2 * STRIDE);
+    load_x(b1, k + STRIDE);
 #pragma unroll
-      for (int t = 0; t < 4; ++t)
-        b[u][t] = (t < mt && k + 32 * u < k_end) ? *(const u32x4*)(xrow[t] + k + 32 * u) : (u32x4){0, 0, 0, 0};
-#pragma unroll
-    for (int u = 0; u < 4; ++u)
+    for (int i = 0; i < 4; ++i)
 #pragma unroll
       for (int t = 0; t < 4; ++t)
         if (t < mt)
-          acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a[u]),
-                                                           __builtin_bit_cast(bf16x8_t, b[u][t]), acc[t], 0, 0, 0);
-  }
-  // lane holds C^T[n0 + 4G + r][m0 + 16t + l%16]: 4 consecutive n of one m
-  const int n = n0 + 4 * G;
+          acc[i][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a0[i]),
+                                                              __builtin_bit_cast(bf16x8_t, b0[t]), acc[i][t], 0, 0, 0);
 #pragma unroll
-  for (int t = 0; t < 4; ++t) {
-    const int m = m0 + 16 * t + i16;
-    if (t < mt && m < M && n < N) *(f32x4*)(part + ((size_t)sp * M + m) * N + n) = acc[t];
+    for (int i = 0; i < 4; ++i) {
+      a0[i] = a1[i];
+      a1[i] = a2[i];
+      b0[i] = b1[i];
+    }
+  }
+  // lane holds C^T[n0 + 16i + 4G + r][m0 + 16t + l%16]: 4 consecutive n of one m
+  for (int ww = 0; ww < 4; ++ww) {
+    if (w == ww) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+          float* r = red + (16 * t + i16) * RG_N + 16 * i + 4 * G;
+          if (ww == 0) {
+            *(f32x4*)r = acc[i][t];
+          } else {
+            const f32x4 o = *(const f32x4*)r;
+            *(f32x4*)r = (f32x4){o[0] + acc[i][t][0], o[1] + acc[i][t][1], o[2] + acc[i][t][2], o[3] + acc[i][t][3]};
+          }
+        }
+    }
+    __syncthreads();
+  }
+  // 64 rows m of 64 n: 16 threads per row, 4 n each
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    const int mm = 16 * u + (threadIdx.x >> 4), nn = 4 * (threadIdx.x & 15);
+    const int m = m0 + mm, n = n0 + nn;
+    if (m < M && n < N) *(f32x4*)(part + ((size_t)sp * M + m) * N + n) = *(const f32x4*)(red + mm * RG_N + nn);
   }
 }
 
@@ -138,15 +177,15 @@ struct RowPlan {
   int splits, kc;
 };
 
-// enough workgroups to stream the weight from every CU (about 2048), with k
-// slices of at least 512 so the partial sums stay small against the weight
+// enough workgroups to stream the weight from every CU (about 1024), with k
+// slices of at least 1024 so the partial sums stay small against the weight
 RowPlan row_plan(int M, int N, int K) {
   const int tiles = ((N + RG_N - 1) / RG_N) * ((M + RG_M - 1) / RG_M);
-  int splits = (2048 + tiles - 1) / tiles;
-  const int max_splits = (K + 511) / 512;
+  int splits = (1024 + tiles - 1) / tiles;
+  const int max_splits = (K + 1023) / 1024;
   splits = splits < 1 ? 1 : (splits > max_splits ? max_splits : splits);
   int kc = (K + splits - 1) / splits;
-  kc = (kc + RG_STEP - 1) / RG_STEP * RG_STEP;
+  kc = (kc + 4 * RG_K - 1) / (4 * RG_K) * (4 * RG_K);
   RowPlan p;
   p.kc = kc;
   p.splits = (K + kc - 1) / kc;
