@@ -194,6 +194,22 @@ mla_status mla_fp8_page_bytes(const mla_dims* dims, int32_t block_size, size_t* 
 mla_status mla_quantize_fp8(const mla_dims* dims, int32_t n_rows, const void* rows, const int32_t* slots,
                             int32_t block_size, void* pool, void* stream);
 
+/* Latent projection straight into an FP8 cache: the rows of
+ * mla_rope_latent_project ("DeepSeek-V2 paper digest" §2.1, §2.3), quantised
+ * as mla_quantize_fp8 does ("DeepSeek core techniques" §6.3: the cache is
+ * quantised to FP8 as it is written), so the caller needs no bf16 cache. The
+ * rows are formed in bf16 (fp32 accumulate, RoPE, rounding) in the workspace,
+ * then quantised into pool (FP8 pages of block_size tokens) at slots; the pool
+ * holds the same bytes as mla_rope_latent_project into a bf16 cache followed by
+ * mla_quantize_fp8 of those rows. dims->dtype must be MLA_BF16; qproj as for
+ * mla_rope_latent_project. workspace: mla_project_fp8_workspace_size bytes.
+ * n_tokens == 0 is a no-op. */
+mla_status mla_rope_latent_project_fp8(const mla_dims* dims, int32_t n_tokens, int32_t d_model, const void* h,
+                                       const void* w_dkv, const void* w_kr, const int32_t* positions,
+                                       const int32_t* slots, void* pool, int32_t block_size,
+                                       const mla_qproj* qproj, void* workspace, size_t workspace_bytes,
+                                       void* stream);
+
 /* mla_decode_multi over an FP8 cache: cache->rows is the FP8 page pool, the
  * block table and lengths as for mla_decode. The scores use the FP8 matrix
  * core with the query q~ quantised like a cache row (one scale per head, its
@@ -287,6 +303,7 @@ mla_status mla_project_workspace_size(const mla_dims* dims, int32_t n_tokens, in
 mla_status mla_decode_workspace_size(const mla_dims* dims, int32_t batch, int32_t max_context, size_t* bytes);
 mla_status mla_decode_multi_workspace_size(const mla_dims* dims, int32_t batch, int32_t q_len,
                                            int32_t max_context, size_t* bytes);
+mla_status mla_project_fp8_workspace_size(const mla_dims* dims, int32_t n_tokens, int32_t d_q, size_t* bytes);
 mla_status mla_decode_fp8_workspace_size(const mla_dims* dims, int32_t batch, int32_t q_len,
                                          int32_t max_context, size_t* bytes);
 mla_status mla_prefill_workspace_size(const mla_dims* dims, int32_t batch, int32_t seq_len,

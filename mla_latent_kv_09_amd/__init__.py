@@ -23,6 +23,7 @@ __all__ = [
     "mla_project_workspace_size", "mla_decode_workspace_size", "mla_decode_multi_workspace_size",
     "mla_prefill_workspace_size", "Fp8Cache", "mla_fp8_page_bytes", "mla_quantize_fp8", "mla_decode_fp8",
     "mla_decode_fp8_workspace_size", "mla_decode_noalloc", "mla_noalloc_scratch_bytes",
+    "mla_rope_latent_project_fp8", "mla_project_fp8_workspace_size",
     "mla_output_project", "mla_output_workspace_size", "mla_fold_output_weights", "mla_decode_folded",
     "mla_decode_folded_workspace_size",
     "mla_status_string", "mla_decode_path", "mla_prefill_path", "mla_version",
@@ -80,6 +81,10 @@ def library():
         lib.mla_decode_multi.argtypes = [pd, i32, i32, vp, vp, vp, vp, pc, vp, vp, sz, vp]
         lib.mla_prefill.argtypes = [pd, i32, i32, vp, vp, vp, vp, pc, vp, vp, sz, vp]
         lib.mla_decode_fp8.argtypes = [pd, i32, i32, vp, vp, vp, vp, pc, vp, vp, sz, vp]
+        lib.mla_rope_latent_project_fp8.argtypes = [pd, i32, i32, vp, vp, vp, vp, vp, vp, i32, pq, vp, sz, vp]
+        lib.mla_rope_latent_project_fp8.restype = ctypes.c_int
+        lib.mla_project_fp8_workspace_size.argtypes = [pd, i32, i32, ctypes.POINTER(sz)]
+        lib.mla_project_fp8_workspace_size.restype = ctypes.c_int
         lib.mla_output_project.argtypes = [pd, i32, i32, vp, vp, vp, vp, sz, vp]
         lib.mla_fold_output_weights.argtypes = [pd, i32, vp, vp, vp, vp]
         lib.mla_decode_folded.argtypes = [pd, i32, i32, vp, vp, vp, vp, i32, pc, vp, vp, sz, vp]
@@ -336,6 +341,48 @@ def mla_rope_latent_project(dims, h, w_dkv, w_kr, positions, slots, cache: Cache
                                           ctypes.byref(qp) if qp is not None else None,
                                           ws.data_ptr() if ws is not None else None, nbytes, _stream(stream)),
         "mla_rope_latent_project")
+
+
+def mla_project_fp8_workspace_size(dims, n_tokens: int, d_q: int = 0) -> int:
+    n = ctypes.c_size_t(0)
+    _ok(library().mla_project_fp8_workspace_size(ctypes.byref(Dims.of(dims).c()), n_tokens, d_q, ctypes.byref(n)),
+        "mla_project_fp8_workspace_size")
+    return n.value
+
+
+def mla_rope_latent_project_fp8(dims, h, w_dkv, w_kr, positions, slots, pages, block_size: int = 64,
+                                qproj: Optional[QProj] = None, workspace=None, stream=None):
+    """The latent rows of each token of h, RoPE'd and quantised straight into
+    the FP8 pages [num_blocks, page_bytes] at slots (see include/mla.h)."""
+    d = Dims.of(dims)
+    T, d_model = h.shape
+    dt = d.torch_dtype
+    _need(h, "h", (T, d_model), dt)
+    _need(w_dkv, "w_dkv", (d.d_c, d_model), dt)
+    _need(w_kr, "w_kr", (d.d_rope, d_model), dt)
+    _need(positions, "positions", (T,), torch.int32)
+    _need(slots, "slots", (T,), torch.int32)
+    if pages.dtype != torch.uint8 or pages.dim() != 2 or not pages.is_contiguous() or \
+            pages.shape[1] != mla_fp8_page_bytes(d, block_size):
+        raise ValueError("pages must be contiguous uint8 [num_blocks, mla_fp8_page_bytes]")
+    qp = None
+    d_q = 0
+    if qproj is not None:
+        d_q = qproj.d_q
+        _need(qproj.w_dq, "w_dq", (d_q, d_model), dt)
+        _need(qproj.w_uq, "w_uq", (d.n_heads * d.d_nope, d_q), dt)
+        _need(qproj.w_qr, "w_qr", (d.n_heads * d.d_rope, d_q), dt)
+        _need(qproj.q_nope, "q_nope", (T, d.n_heads, d.d_nope), dt)
+        _need(qproj.q_pe, "q_pe", (T, d.n_heads, d.d_rope), dt)
+        qp = _QProj(d_q, qproj.w_dq.data_ptr(), qproj.w_uq.data_ptr(), qproj.w_qr.data_ptr(),
+                    qproj.q_nope.data_ptr(), qproj.q_pe.data_ptr())
+    ws, nbytes = _workspace(mla_project_fp8_workspace_size(d, T, d_q), h.device, workspace)
+    _ok(library().mla_rope_latent_project_fp8(ctypes.byref(d.c()), T, d_model, h.data_ptr(), w_dkv.data_ptr(),
+                                              w_kr.data_ptr(), positions.data_ptr(), slots.data_ptr(),
+                                              pages.data_ptr(), block_size,
+                                              ctypes.byref(qp) if qp is not None else None,
+                                              ws.data_ptr() if ws is not None else None, nbytes, _stream(stream)),
+        "mla_rope_latent_project_fp8")
 
 
 def mla_decode(dims, q_nope, q_pe, w_uk, w_uv, cache: Cache, out=None, workspace=None, stream=None):

@@ -441,12 +441,15 @@ __global__ __launch_bounds__(SPLIT_THREADS, 1) void k_split(int H, int B, int q_
   // query of this lane's head: Qt[b, h_own, 16s + 8g .. +7], s < 36 (lanes of
   // heads >= H read head H-1; nothing of theirs is stored)
   bf16x8_t qf[QK_STEPS];
+  __builtin_amdgcn_sched_barrier(0);  // the page numbers are requested before the query
   {
     const bf16* q = qt + ((size_t)b * H + min(h_own, H - 1)) * ROW + 8 * g;
 #pragma unroll
     for (int s = 0; s < QK_STEPS; ++s) qf[s] = as_bf16x8(*(const u32x4*)(q + 16 * s));
   }
-  wait_vmcnt<0>();  // query and page loads done: from here on only tile loads use vmcnt
+  // page numbers in (loads complete in order), the query may still fly: the
+  // first tiles' copies go out now and travel together with the query
+  wait_vmcnt<QK_STEPS>();
   load_tile(0);
   if (n_tiles > 1) load_tile(1);
 
@@ -484,7 +487,7 @@ __global__ __launch_bounds__(SPLIT_THREADS, 1) void k_split(int H, int B, int q_
   // ---- online softmax of the owned heads, in 8 slices (slice k of 8) ----
   // slices 0-1: tile max, new reference and its shift k; slices
   // 2-7: exponentials, row sum, bf16 P fragments
-  float sm_mx, sm_sub, sm_alpha, sm_lsum;
+  float sm_mx, sm_sub, sm_alpha, sm_ls[3];
   int sm_k;
   bf16x8_t pk[2];
   auto softmax_slice = [&](const f32x16& sc, int k) {
@@ -515,18 +518,22 @@ __global__ __launch_bounds__(SPLIT_THREADS, 1) void k_split(int H, int B, int q_
       sm_alpha = __builtin_amdgcn_ldexpf(1.f, -sm_k);
       m_run = (first || reset) ? sm_mx : m_run + kc;
       sm_sub = m_run;
-      sm_lsum = 0.f;
     } else {
-      // slices 2..7 take elements 0-2, 3-5, 6-8, 9-11, 12-14, 15
+      // slices 2..7 take elements 0-2, 3-5, 6-8, 9-11, 12-14, 15; the row
+      // sum is kept as three running sums of the slices' own short sums, so
+      // no long chain of dependent adds is left for the end of the step
       const int e0 = 3 * (k - 2), e1 = min(e0 + 3, 16);
+      float ps = 0.f;
 #pragma unroll
       for (int e = e0; e < e1; ++e) {
         const float pe = __builtin_amdgcn_exp2f(sc[e] - sm_sub);
-        sm_lsum += pe;
+        ps = e == e0 ? pe : ps + pe;
         pk[e >> 3][e & 7] = (__bf16)pe;
       }
+      const int a = (k - 2) % 3;
+      sm_ls[a] = k < 5 ? ps : sm_ls[a] + ps;
       if (k == 7) {
-        l_run = l_run * sm_alpha + sm_lsum;
+        l_run = l_run * sm_alpha + ((sm_ls[0] + sm_ls[1]) + sm_ls[2]);
       }
     }
   };
@@ -690,9 +697,14 @@ __global__ __launch_bounds__(SPLIT_THREADS, 1) void k_split(int H, int B, int q_
 
   using T = std::true_type;
   using F = std::false_type;
-  // iteration 0: scores and softmax of tile 0
+  // iteration 0: scores and softmax of tile 0. Tile 0 landed means the query
+  // (requested before it) has too; the empty asm tells the compiler so, so
+  // that it places no wait for the query inside the step, where the step's
+  // own copies would make that wait drain them (it may wait here for tile 1)
   wait_vmcnt<TILE_LOADS>();
   if (n_tiles == 1) wait_vmcnt<0>();
+#pragma unroll
+  for (int s = 0; s < QK_STEPS; ++s) asm volatile("" : "+v"(qf[s]));
   lds_barrier();
   // the copies of tile i + 2 go out during step i (spread over its score MFMAs)
   step(T{}, F{}, 0, n_tiles > 2 ? 2 : -1);

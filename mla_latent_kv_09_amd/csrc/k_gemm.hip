@@ -294,7 +294,7 @@ __global__ __launch_bounds__(G_THREADS, 1) void k_gemm(GemmArgs g) {
     bf16* crow;
     int pos = 0;
     if (EPI == 1) {
-      crow = g.c0 + (size_t)g.slots[m] * g.ldc0;
+      crow = g.c0 + (size_t)(g.slots ? g.slots[m] : m) * g.ldc0;
       pos = g.positions[m];
     }
     const int seq_b = seq_of[j >> 1], seq_t = m - seq_b * g.a_seq;

@@ -65,7 +65,7 @@ __global__ __launch_bounds__(256) void k_gemm_nt(int M, int N, int K, const TA* 
         if (n < N) st<TC>(c + n, acc[i][j]);
       }
     } else {
-      TC* row = (TC*)ep.c + (size_t)ep.slots[m] * (ep.d_c + ep.d_rope);
+      TC* row = (TC*)ep.c + (size_t)(ep.slots ? ep.slots[m] : m) * (ep.d_c + ep.d_rope);
       const int pos = ep.positions[m];
       for (int j = 0; j < 4; j += 2) {
         const int n = n0 + tx * 4 + j;   // even; d_c is a multiple of 8

@@ -38,7 +38,8 @@ struct CacheView {
 hipError_t gemm_nt_generic(int a_dtype, int b_dtype, int c_dtype, int M, int N, int K,
                            const void* a, int lda, const void* b0, const void* b1, int n_split,
                            int ldb, void* c, int ldc, hipStream_t s);
-// Latent rows: [c || RoPE(k)] = [W_DKV; W_KR] h, written to row slots[i] of rows.
+// Latent rows: [c || RoPE(k)] = [W_DKV; W_KR] h, written to row slots[i] of rows
+// (row i when slots is null; likewise for project_fast).
 hipError_t project_latent_generic(const mla_dims& d, int n_tokens, int d_model, const void* h,
                                   const void* w_dkv, const void* w_kr, const int32_t* positions,
                                   const int32_t* slots, void* rows, hipStream_t s);

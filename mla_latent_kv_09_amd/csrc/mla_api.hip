@@ -89,6 +89,11 @@ bool prefill_fast_dims(const mla_dims* d) {
 
 extern "C" {
 
+static mla_status mla_rope_latent_project_rows(const mla_dims* d, int32_t n_tokens, int32_t d_model, const void* h,
+                                               const void* w_dkv, const void* w_kr, const int32_t* positions,
+                                               const int32_t* slots, const mla_cache* cache, const mla_qproj* qp,
+                                               void* ws, size_t ws_bytes, void* stream);
+
 const char* mla_status_string(mla_status s) {
   switch (s) {
     case MLA_OK: return "ok";
@@ -163,13 +168,23 @@ mla_status mla_rope_latent_project(const mla_dims* d, int32_t n_tokens, int32_t 
                                    const void* w_dkv, const void* w_kr, const int32_t* positions,
                                    const int32_t* slots, const mla_cache* cache, const mla_qproj* qp,
                                    void* ws, size_t ws_bytes, void* stream) {
+  if (n_tokens > 0 && !slots) return MLA_ERR_NULL_ARG;
+  return mla_rope_latent_project_rows(d, n_tokens, d_model, h, w_dkv, w_kr, positions, slots, cache, qp, ws,
+                                      ws_bytes, stream);
+}
+
+// As mla_rope_latent_project; slots == NULL writes token i to row i.
+static mla_status mla_rope_latent_project_rows(const mla_dims* d, int32_t n_tokens, int32_t d_model, const void* h,
+                                               const void* w_dkv, const void* w_kr, const int32_t* positions,
+                                               const int32_t* slots, const mla_cache* cache, const mla_qproj* qp,
+                                               void* ws, size_t ws_bytes, void* stream) {
   mla_status st = check_dims(d);
   if (st != MLA_OK) return st;
   if (n_tokens < 0 || d_model < 1 || d_model > 16384) return MLA_ERR_BAD_SHAPE;
   if (n_tokens == 0) return MLA_OK;
-  if (!h || !w_dkv || !w_kr || !positions || !slots || !cache || !cache->rows) return MLA_ERR_NULL_ARG;
+  if (!h || !w_dkv || !w_kr || !positions || !cache || !cache->rows) return MLA_ERR_NULL_ARG;
   if (!aligned(h, 16) || !aligned(w_dkv, 16) || !aligned(w_kr, 16) || !aligned(cache->rows, 16) ||
-      !aligned(positions, 4) || !aligned(slots, 4))
+      !aligned(positions, 4) || (slots && !aligned(slots, 4)))
     return MLA_ERR_ALIGNMENT;
   size_t need = 0;
   if (qp) {
@@ -202,6 +217,52 @@ mla_status mla_rope_latent_project(const mla_dims* d, int32_t n_tokens, int32_t 
   if (e != hipSuccess) return MLA_ERR_HIP;
   return hip_status(mla::gemm_nt_generic(MLA_F32, dt, dt, n_tokens, hr, qp->d_q, ws, qp->d_q, qp->w_qr,
                                          qp->w_qr, hr, qp->d_q, qp->q_pe, hr, s));
+}
+
+// FP8 projection: the latent rows go to a bf16 staging area at the front of
+// the workspace (row i for token i), then the quantiser writes them into the
+// FP8 pages at their slots; the query path's c_Q follows the staging area.
+static size_t fp8_stage_bytes(const mla_dims* d, int32_t n_tokens) {
+  return ((size_t)n_tokens * (d->d_c + d->d_rope) * 2 + 255) & ~(size_t)255;
+}
+
+mla_status mla_project_fp8_workspace_size(const mla_dims* d, int32_t n_tokens, int32_t d_q, size_t* bytes) {
+  mla_status st = check_dims(d);
+  if (st != MLA_OK) return st;
+  if (!bytes) return MLA_ERR_NULL_ARG;
+  if (n_tokens < 0 || d_q < 0) return MLA_ERR_BAD_SHAPE;
+  *bytes = fp8_stage_bytes(d, n_tokens) + (size_t)n_tokens * d_q * sizeof(float);
+  return MLA_OK;
+}
+
+mla_status mla_rope_latent_project_fp8(const mla_dims* d, int32_t n_tokens, int32_t d_model, const void* h,
+                                       const void* w_dkv, const void* w_kr, const int32_t* positions,
+                                       const int32_t* slots, void* pool, int32_t block_size, const mla_qproj* qp,
+                                       void* ws, size_t ws_bytes, void* stream) {
+  mla_status st = check_dims(d);
+  if (st != MLA_OK) return st;
+  if (d->dtype != MLA_BF16) return MLA_ERR_BAD_DTYPE;
+  if (n_tokens < 0 || d_model < 1 || d_model > 16384 || block_size < 1 || block_size > 4096) return MLA_ERR_BAD_SHAPE;
+  if (n_tokens == 0) return MLA_OK;
+  if (!pool || !slots) return MLA_ERR_NULL_ARG;
+  if (!aligned(pool, 16)) return MLA_ERR_ALIGNMENT;
+  size_t need = 0;
+  if ((st = mla_project_fp8_workspace_size(d, n_tokens, qp ? qp->d_q : 0, &need)) != MLA_OK) return st;
+  if ((st = check_ws(ws, ws_bytes, need)) != MLA_OK) return st;
+  // the bf16 rows into the staging area (a contiguous "cache" of n_tokens rows)
+  const size_t stage = fp8_stage_bytes(d, n_tokens);
+  mla_cache staging{};
+  staging.rows = ws;
+  staging.num_blocks = 1;
+  staging.block_size = n_tokens;
+  staging.context_lens = slots;  // not read by the projection
+  staging.max_context = n_tokens;
+  if ((st = mla_rope_latent_project_rows(d, n_tokens, d_model, h, w_dkv, w_kr, positions, nullptr, &staging, qp,
+                                         (char*)ws + stage, ws_bytes - stage, stream)) != MLA_OK)
+    return st;
+  hipStream_t s = (hipStream_t)stream;
+  if (trace_on()) fprintf(stderr, "[mla] project_fp8 n_tokens=%d block_size=%d\n", n_tokens, block_size);
+  return hip_status(mla::quant_fp8(*d, n_tokens, ws, slots, block_size, pool, s));
 }
 
 mla_status mla_decode_multi(const mla_dims* d, int32_t batch, int32_t q_len, const void* q_nope, const void* q_pe,

@@ -226,3 +226,70 @@ def test_workload3_fp8_full_size_sampled():
     deq = np.zeros((nb, P, R))
     deq[used] = fp8.dequantize_pool(want, P, 512, 64)
     assert_parity(got[sample], _oracle_fp8(case, deq, seqs=sample), "fp8", "workload 3, fp8 cache")
+
+
+def _decode_fp8_bytes(pages, bs, d_c, d_rope):
+    """Rows [n_pages * bs, d_c + d_rope] held by FP8 pages, decoded here with
+    torch's float8_e4m3fn type and the scale bytes (2^(E - 127)); independent of
+    the oracle's decoder."""
+    t = torch.from_numpy(np.ascontiguousarray(pages))
+    nb = t.shape[0]
+    rb = d_c + 2 * d_rope
+    body = t[:, :bs * rb].reshape(nb * bs, rb)
+    codes = body[:, :d_c].contiguous().view(torch.float8_e4m3fn).to(torch.float64)
+    kpe = body[:, d_c:].contiguous().view(torch.bfloat16).to(torch.float64)
+    E = t[:, bs * rb:bs * rb + bs].reshape(nb * bs).to(torch.float64)
+    return torch.cat([codes * torch.exp2(E - 127.0)[:, None], kpe], dim=1).numpy()
+
+
+@pytest.mark.parametrize("d_model,d_q", [(512, 0), (256, 128)])
+def test_project_fp8_writes_the_quantised_rows(d_model, d_q):
+    """mla_rope_latent_project_fp8 gives the pages of the bf16 projection
+    followed by mla_quantize_fp8, byte for byte; the rows it holds are the
+    oracle's latent rows within E4M3 rounding (c_KV, relative 2^-4 of each
+    token's scale) and the bf16 bar (k_pe); decode over it matches the oracle's
+    decode over its own quantised rows."""
+    from synth import make_project_case
+    _log(f"projection into an FP8 cache d_model={d_model} d_q={d_q}")
+    dims = Dims(128, **V3)
+    case = make_project_case(61 + d_q, batch=2, seq_len=150, d_model=d_model, dims=dims, d_q=d_q, shuffle=True)
+    T, nb = case.n_tokens, case.num_blocks
+    pb = mla.mla_fp8_page_bytes(dims, 64)
+    h, wd, wr = to_torch(case.h), to_torch(case.w_dkv), to_torch(case.w_kr)
+    pos, slots = to_torch(case.positions), to_torch(case.slots)
+    qp = None
+    if d_q:
+        qn = torch.empty((T, 128, 128), dtype=torch.bfloat16, device="cuda")
+        qpe = torch.empty((T, 128, 64), dtype=torch.bfloat16, device="cuda")
+        qp = mla.QProj(to_torch(case.w_dq), to_torch(case.w_uq), to_torch(case.w_qr), qn, qpe)
+    fused = torch.zeros((nb, pb), dtype=torch.uint8, device="cuda")
+    mla.mla_rope_latent_project_fp8(dims, h, wd, wr, pos, slots, fused, 64, qp)
+    rows = torch.zeros((nb, 64, dims.row), dtype=torch.bfloat16, device="cuda")
+    lens = torch.full((2,), 150, dtype=torch.int32, device="cuda")
+    mla.mla_rope_latent_project(dims, h, wd, wr, pos, slots, mla.Cache(rows, lens, 150, to_torch(case.block_table)))
+    two_step = torch.zeros((nb, pb), dtype=torch.uint8, device="cuda")
+    mla.mla_quantize_fp8(dims, rows.view(nb * 64, dims.row)[slots.long()].contiguous(), two_step, slots, 64)
+    torch.cuda.synchronize()
+    got = fused.cpu().numpy()
+    assert np.array_equal(got, two_step.cpu().numpy())
+    sl = case.slots
+    deq = _decode_fp8_bytes(got, 64, 512, 64)[sl]
+    ref = oracle.latent_rows(case.h, case.w_dkv, case.w_kr, case.positions)
+    scale = 2.0 ** (np.ceil(np.log2(np.abs(ref[:, :512]).max(axis=1) / 448.0)))[:, None]
+    # E4M3 rounding (half an ulp: 2^-4 relative, 2^-10 of the scale below the
+    # normal range) of a bf16 row that is itself within 2^-7 of the exact value
+    assert np.all(np.abs(deq[:, :512] - ref[:, :512]) <= (2.0 ** -4 + 2.0 ** -7) * np.abs(ref[:, :512]) + 2.0 ** -9 * scale)
+    assert np.all(np.abs(deq[:, 512:] - ref[:, 512:]) <= 2 ** -7 * np.abs(ref[:, 512:]) + 2e-3)
+    # decode over the fused pool against the oracle's decode over its own pages
+    rng = np.random.default_rng(5)
+    q_nope = f32_to_bf16_bits(rng.standard_normal((2, 128, 128)).astype(np.float32))
+    q_pe = f32_to_bf16_bits(rng.standard_normal((2, 128, 64)).astype(np.float32))
+    dcase = make_decode_case(62, 2, dims, [150, 150])
+    dcase.q_nope, dcase.q_pe = q_nope, q_pe
+    dcase.cache.block_table = case.block_table
+    dcase.cache.context_lens = np.array([150, 150], dtype=np.int32)
+    own = np.zeros((nb, 64, dims.row))
+    own.reshape(nb * 64, dims.row)[sl] = oracle.round_to(ref, "bf16")
+    own_pages = fp8.quantize_pool(own, 512)
+    want = _oracle_fp8(dcase, fp8.dequantize_pool(own_pages, 64, 512, 64))
+    assert_parity(_run_fp8(dcase, got), want, "fp8", "decode over the projected FP8 cache")
