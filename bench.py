@@ -266,16 +266,19 @@ FLUSH_BYTES = 512 << 20   # twice the 256 MB last-level cache (MALL)
 
 def cold_pass(step, lib, kernel_name, n):
     """Cold-cache timing, after the timed region: n steps, each preceded by an
-    untimed write of a 512 MiB scratch buffer (so no input is left in the
-    MALL or L2), each bracketed by its own events. Returns the median and
-    minimum step time and the median time of kernel_name (HIP events around
-    that kernel's launch), in microseconds."""
+    untimed read of a 512 MiB scratch buffer (a sum over it, so no input is
+    left in the MALL or L2 and no dirty line is left for the step to write
+    back), each bracketed by its own events. Returns the median and minimum
+    step time and the median time of kernel_name (HIP events around that
+    kernel's launch), in microseconds."""
     import torch
-    flush = torch.empty(FLUSH_BYTES, dtype=torch.uint8, device="cuda:0")
+    flush = torch.zeros(FLUSH_BYTES // 8, dtype=torch.int64, device="cuda:0")
+    acc = torch.zeros((), dtype=torch.int64, device="cuda:0")
+    torch.cuda.synchronize()
     stream = torch.cuda.current_stream()
     steps_us, kern_us = [], []
     for i in range(n):
-        flush.fill_(i & 0xFF)
+        torch.sum(flush, dim=0, out=acc)
         ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         lib.mla_profile_only(kernel_name.encode())
         lib.mla_profile_begin()

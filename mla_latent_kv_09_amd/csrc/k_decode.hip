@@ -155,97 +155,93 @@ struct RopeFreq {
   double theta[DR / 2];
 };
 
-// grid (H, DC / 64); 4 waves. Block (h, c0) forms Qt[:, h, c0 .. c0+63] for
-// every sequence as the transposed product Qt^T[c, b] = sum_j W_UK[h*128+j, c]
-// q_nope[b, h, j]: the 128 x 64 slice of W_UK,h is staged in LDS and read
-// transposed (as the A operand); each lane then holds 4 consecutive columns of
-// one sequence. Results go through LDS so that every row segment (64 columns,
-// 128 bytes) is written whole. The blocks of head h also write its rotated,
-// scaled q_pe slice, each for every 8th sequence; those loads are issued
-// first.
+// grid (H, DC / 128); 4 waves; one block round on the chip for H = 128. Block
+// (h, c0) forms Qt[:, h, c0 .. c0+127] for every query row as the transposed
+// product Qt^T[c, b] = sum_j W_UK[h*128+j, c] q_nope[b, h, j]. The 128 x 128
+// slice of W_UK,h (32 KB) and the first 64 query rows are requested before
+// anything else, so each block has all of its HBM reads in flight at once.
+// The slice is staged in LDS and read transposed (the A operand); wave w takes
+// query rows 16w .. 16w+15 of each 64-row chunk (the B operand, straight from
+// memory: 8 consecutive j of one row per lane) against all 8 column tiles, so
+// every query element is loaded once per block. Results go through LDS so
+// that each row segment (128 columns, 256 bytes) is written whole. The blocks
+// of head h also write its rotated, scaled q_pe slice, each for every 4th row.
 __global__ __launch_bounds__(256) void k_absorb(int B, int H, int q_len, const bf16* __restrict__ q_nope,
                                                 const bf16* __restrict__ q_pe, const bf16* __restrict__ w_uk,
                                                 const int32_t* __restrict__ ctx_lens, float qscale, RopeFreq rope,
                                                 bf16* __restrict__ qt) {
-  constexpr int LD = 72;  // padded row (144 B) keeps the transposed reads conflict-free
-  constexpr int BT_CHUNK = 4;  // sequence tiles whose query loads are in flight together
-  constexpr int LDO = 72;      // staged output row: 64 columns + pad
+  constexpr int CW = 128;       // columns of one block
+  constexpr int LD = CW + 8;    // padded row (272 B): two-way LDS conflicts at most on the transposed reads
+  constexpr int NCB = DC / CW;  // column blocks per head
   __shared__ __attribute__((aligned(16))) bf16 wt[DN * LD];
-  __shared__ __attribute__((aligned(16))) bf16 ot[16 * BT_CHUNK * LDO];
-  const int h = blockIdx.x, c0 = blockIdx.y * 64;
+  __shared__ __attribute__((aligned(16))) bf16 ot[64 * LD];
+  const int h = blockIdx.x, c0 = blockIdx.y * CW;
   const int w = threadIdx.x >> 6, lane = threadIdx.x & 63, i16 = lane & 15, G = lane >> 4;
-  // RoPE part of this thread: pair i = tid % 32 of sequences b = 8k + y with
-  // k = tid / 32, tid / 32 + 8, ... (first one's inputs requested now)
+  // W_UK slice: 128 rows of 256 bytes, 16 lanes per row, 8 loads per lane
+  u32x4 wr[DN * CW / 8 / 256];
+#pragma unroll
+  for (int u = 0; u < DN * CW / 8 / 256; ++u) {
+    const int i = threadIdx.x + 256 * u, j = i >> 4, ch = i & 15;
+    wr[u] = *(const u32x4*)(w_uk + (size_t)(h * DN + j) * DC + c0 + ch * 8);
+  }
+  auto load_q = [&](int b0, u32x4 (&qv)[DN / 32]) {
+    const int b = b0 + 16 * w + i16;
+#pragma unroll
+    for (int ks = 0; ks < DN / 32; ++ks)
+      qv[ks] = b < B ? *(const u32x4*)(q_nope + ((size_t)b * H + h) * DN + 32 * ks + 8 * G) : (u32x4){0, 0, 0, 0};
+  };
+  u32x4 qv[DN / 32];
+  load_q(0, qv);
+  // RoPE part of this thread: pair i = tid % 32 of rows b = NCB k + blockIdx.y
+  // with k = tid / 32, tid / 32 + 8, ... (first one's inputs requested now)
   const int rp_i = threadIdx.x & (DR / 2 - 1);
-  const int rp_b0 = (threadIdx.x / (DR / 2)) * (DC / 64) + blockIdx.y;
-  constexpr int RP_STEP = (256 / (DR / 2)) * (DC / 64);
+  const int rp_b0 = (threadIdx.x / (DR / 2)) * NCB + blockIdx.y;
+  constexpr int RP_STEP = (256 / (DR / 2)) * NCB;
   int rp_len = 0;
   uint32_t rp_x = 0;
   if (rp_b0 < B) {
     rp_len = visible_rows(ctx_lens, rp_b0, q_len);
     rp_x = *(const uint32_t*)(q_pe + ((size_t)rp_b0 * H + h) * DR + 2 * rp_i);
   }
-  // every independent load first: the W_UK slice and the first chunk of queries
-  u32x4 wr[DN * 8 / 256];
 #pragma unroll
-  for (int u = 0; u < DN * 8 / 256; ++u) {
-    const int i = threadIdx.x + 256 * u, j = i >> 3, ch = i & 7;
-    wr[u] = *(const u32x4*)(w_uk + (size_t)(h * DN + j) * DC + c0 + ch * 8);
-  }
-  auto load_q = [&](int bt0, u32x4 (&qv)[BT_CHUNK][DN / 32]) {
-#pragma unroll
-    for (int t = 0; t < BT_CHUNK; ++t)
-#pragma unroll
-      for (int ks = 0; ks < DN / 32; ++ks) {
-        const int b = (bt0 + t) * 16 + i16;
-        qv[t][ks] = b < B ? *(const u32x4*)(q_nope + ((size_t)b * H + h) * DN + 32 * ks + 8 * G) : (u32x4){0, 0, 0, 0};
-      }
-  };
-  u32x4 qv[BT_CHUNK][DN / 32];
-  load_q(0, qv);
-#pragma unroll
-  for (int u = 0; u < DN * 8 / 256; ++u) {
-    const int i = threadIdx.x + 256 * u, j = i >> 3, ch = i & 7;
+  for (int u = 0; u < DN * CW / 8 / 256; ++u) {
+    const int i = threadIdx.x + 256 * u, j = i >> 4, ch = i & 15;
     *(u32x4*)&wt[j * LD + ch * 8] = wr[u];
   }
   __syncthreads();
   const LDS_AS char* wbase = (const LDS_AS char*)wt;
-  // A fragments of column tile w (columns c0 + 16w .. +15), all 4 K-steps
-  bf16x8_t af[DN / 32];
+  for (int b0 = 0; b0 < B; b0 += 64) {
+    u32x4 cur[DN / 32];
 #pragma unroll
-  for (int ks = 0; ks < DN / 32; ++ks) {
-    const int k0 = 32 * ks + 8 * G, col = 16 * w + 4 * (i16 & 3);
-    af[ks] = cat_tr(tr_read(wbase + ((k0 + (i16 >> 2)) * LD + col) * 2),
-                    tr_read(wbase + ((k0 + 4 + (i16 >> 2)) * LD + col) * 2));
-  }
-  for (int bt0 = 0; bt0 * 16 < B; bt0 += BT_CHUNK) {
-    u32x4 cur[BT_CHUNK][DN / 32];
+    for (int ks = 0; ks < DN / 32; ++ks) cur[ks] = qv[ks];
+    if (b0 + 64 < B) load_q(b0 + 64, qv);
+    f32x4 acc[CW / 16];
 #pragma unroll
-    for (int t = 0; t < BT_CHUNK; ++t)
+    for (int ct = 0; ct < CW / 16; ++ct) {
+      acc[ct] = (f32x4){0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int ks = 0; ks < DN / 32; ++ks) cur[t][ks] = qv[t][ks];
-    if ((bt0 + BT_CHUNK) * 16 < B) load_q(bt0 + BT_CHUNK, qv);
-    if (bt0 > 0) __syncthreads();  // the previous chunk's rows are out of ot
-#pragma unroll
-    for (int t = 0; t < BT_CHUNK; ++t) {
-      f32x4 acc = {};
-#pragma unroll
-      for (int ks = 0; ks < DN / 32; ++ks)
-        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[ks], as_bf16x8(cur[t][ks]), acc, 0, 0, 0);
-      typedef __attribute__((ext_vector_type(4))) __bf16 bf16x4_t;
-      const bf16x4_t v = {(__bf16)(acc[0] * qscale), (__bf16)(acc[1] * qscale), (__bf16)(acc[2] * qscale),
-                          (__bf16)(acc[3] * qscale)};
-      *(bf16x4_t*)&ot[(16 * t + i16) * LDO + 16 * w + 4 * G] = v;
+      for (int ks = 0; ks < DN / 32; ++ks) {
+        const int k0 = 32 * ks + 8 * G, col = 16 * ct + 4 * (i16 & 3);
+        const bf16x8_t af = cat_tr(tr_read(wbase + ((k0 + (i16 >> 2)) * LD + col) * 2),
+                                   tr_read(wbase + ((k0 + 4 + (i16 >> 2)) * LD + col) * 2));
+        acc[ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af, as_bf16x8(cur[ks]), acc[ct], 0, 0, 0);
+      }
     }
+    // lane: columns 16 ct + 4 G .. +3 of row 16 w + i16; each wave stages and
+    // stores only its own 16 rows
+    typedef __attribute__((ext_vector_type(4))) __bf16 bf16x4_t;
+#pragma unroll
+    for (int ct = 0; ct < CW / 16; ++ct)
+      *(bf16x4_t*)&ot[(16 * w + i16) * LD + 16 * ct + 4 * G] =
+          (bf16x4_t){(__bf16)(acc[ct][0] * qscale), (__bf16)(acc[ct][1] * qscale), (__bf16)(acc[ct][2] * qscale),
+                     (__bf16)(acc[ct][3] * qscale)};
     __syncthreads();
-    // 16 * BT_CHUNK rows of 128 bytes: 8 lanes per row, 16 bytes each
 #pragma unroll
-    for (int rr = 0; rr < (16 * BT_CHUNK + 31) / 32; ++rr) {
-      const int r = 32 * rr + (threadIdx.x >> 3), ch = threadIdx.x & 7;
-      const int b = bt0 * 16 + r;
-      if (r < 16 * BT_CHUNK && b < B)
-        *(u32x4*)(qt + ((size_t)b * H + h) * ROW + c0 + 8 * ch) = *(const u32x4*)&ot[r * LDO + 8 * ch];
+    for (int k = 0; k < 4; ++k) {
+      const int r = 16 * w + 4 * k + (lane >> 4), ch = lane & 15, b = b0 + r;
+      if (b < B) *(u32x4*)(qt + ((size_t)b * H + h) * ROW + c0 + 8 * ch) = *(const u32x4*)&ot[r * LD + 8 * ch];
     }
+    __syncthreads();  // this chunk's rows are out of ot before the next one lands
   }
   // the rotated, scaled q_pe slice: reduce the angle to [-pi, pi] in double,
   // then single-precision sin/cos
@@ -756,16 +752,21 @@ __global__ __launch_bounds__(SPLIT_THREADS, 1) void k_split(int H, int B, int q_
 }
 
 // -------------------------------------------------------- k_combine_uv ----
-// One block per (head, tile of 16 sequences). Blocks of the same head share
+// One block per (head, tile of 16 query rows). Blocks of the same head share
 // blockIdx % 8, i.e. the same XCD and L2, so W_UV,h is fetched from HBM once.
-//   1. per sequence: M = max_s m_s, weights e_s = 2^(m_s - M), 1 / sum_s e_s l_s
-//      (16 lanes per sequence, each over every 16th split)
-//   2. o_c = sum_s e_s O_s / sum_s e_s l_s, 16 threads per sequence, all the
-//      split loads of a thread issued together; bf16 into LDS
-//   3. out^T[v, b] = sum_c W_UV[h*128 + v, c] o_c[b, c] on MFMA; each lane ends
-//      with 4 consecutive outputs of one sequence (one 8-byte store)
-// With UV false, step 3 is left out and o_c itself is written, as out
-// [B, H, 512] bf16, for an output projection with W_UV folded into W_O.
+// Thread (r, q) = (tid / 16, tid % 16) owns row b0 + r and the latent columns
+// 8q + 128u .. +7 (u < 4). It reads (m, l) and its columns of the row's
+// partials itself, 4 splits at a time, and merges them online:
+//   M = max_s m_s, o_c = sum_s 2^(m_s - M) O_s / sum_s 2^(m_s - M) l_s
+// (one group of at most 4 splits in the common case, so no rescale at all).
+// The first group's partials and (m, l) are requested before anything else;
+// this wave's W_UV,h fragments (128 registers) only once the merge is done,
+// which keeps the kernel at two waves per SIMD (holding both would take one
+// block round more). Then out^T[v, b] = sum_c W_UV[h*128 + v, c] o_c[b, c]
+// on MFMA from o_c staged in LDS as bf16; each lane ends with 4 consecutive
+// outputs of one row (one 8-byte store).
+// With UV false, the W_UV product is left out and o_c itself is written, as
+// out [B, H, 512] bf16, for an output projection with W_UV folded into W_O.
 template <bool UV>
 __global__ __launch_bounds__(256) void k_combine_uv(int H, int B, int q_len, int splits, int pps,
                                                     const int32_t* __restrict__ ctx_lens,
@@ -773,9 +774,8 @@ __global__ __launch_bounds__(256) void k_combine_uv(int H, int B, int q_len, int
                                                     const float* __restrict__ part_ml,
                                                     const bf16* __restrict__ w_uv, bf16* __restrict__ out) {
   constexpr int LDO = DC + 8;
+  constexpr int SG = 4;  // splits per load group
   __shared__ __attribute__((aligned(16))) bf16 oc[16 * LDO];
-  __shared__ float wgt[16][MAX_SPLITS];
-  __shared__ float inv_l[16];
   const int nbt = (B + 15) / 16;
   const int bid = blockIdx.x, xcd = bid & 7, k = bid >> 3;
   const int bt = k % nbt, h = (k / nbt) * 8 + xcd;
@@ -783,17 +783,61 @@ __global__ __launch_bounds__(256) void k_combine_uv(int H, int B, int q_len, int
   const int b0 = bt * 16;
   const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
   const int i16 = lane & 15, G = lane >> 4;
-  // 1. lane group rr = lane / 16 of wave w owns sequence r = 4w + rr; lane q of
-  // the group takes splits q, q + 16, ...; 16-lane reductions. The context
-  // length and the (m, l) of split q are requested first (they gate the
-  // weights), then the W_UV,h fragments of this wave (rows 32w .. 32w+31, all
-  // 512 columns), which are needed only at the end.
-  const int rr = lane >> 4, q = lane & 15, r = 4 * w + rr, b = b0 + r;
-  const float* ml = part_ml + ((size_t)h * B + (b < B ? b : 0)) * splits * 2;
+  const int r = tid >> 4, q = tid & 15, b = b0 + r;
   const int len = b < B ? visible_rows(ctx_lens, b, q_len) : 0;
+  // splits that hold rows of this query row; the others were never written
+  const int ns = len > 0 ? ((len + PAGE - 1) / PAGE + pps - 1) / pps : 0;
+  const bf16* po = part_o + ((size_t)h * B + (b < B ? b : 0)) * splits * DC + 8 * q;
+  const float* ml = part_ml + ((size_t)h * B + (b < B ? b : 0)) * splits * 2;
   typedef __attribute__((ext_vector_type(2))) float f32x2_t;
-  f32x2_t ml_q = {-INFINITY, 0.f};
-  if (q < splits && b < B) ml_q = *(const f32x2_t*)(ml + 2 * q);  // used only if q < ns
+  u32x4 pv[SG][4];
+  f32x2_t mlv[SG];
+  auto issue = [&](int s0) {
+#pragma unroll
+    for (int d = 0; d < SG; ++d) {
+      const int sp = s0 + d;
+      if (sp < ns) {
+        mlv[d] = *(const f32x2_t*)(ml + 2 * sp);
+#pragma unroll
+        for (int u = 0; u < 4; ++u) pv[d][u] = *(const u32x4*)(po + (size_t)sp * DC + 128 * u);
+      }
+    }
+  };
+  issue(0);
+  float acc[4][8] = {};
+  float M = -INFINITY, l = 0.f;
+  for (int s0 = 0; s0 < ns; s0 += SG) {
+    float Mg = M;
+#pragma unroll
+    for (int d = 0; d < SG; ++d)
+      if (s0 + d < ns) Mg = fmaxf(Mg, mlv[d][0]);
+    if (Mg > M) {  // a later group raised the max: rescale what is summed so far
+      const float a = __builtin_amdgcn_exp2f(M - Mg);
+      l *= a;
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+#pragma unroll
+        for (int x = 0; x < 8; ++x) acc[u][x] *= a;
+      M = Mg;
+    }
+#pragma unroll
+    for (int d = 0; d < SG; ++d) {
+      if (s0 + d < ns) {
+        const float e = __builtin_amdgcn_exp2f(mlv[d][0] - M);
+        l += e * mlv[d][1];
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+#pragma unroll
+          for (int x = 0; x < 4; ++x) {
+            acc[u][2 * x] += e * __uint_as_float(pv[d][u][x] << 16);
+            acc[u][2 * x + 1] += e * __uint_as_float(pv[d][u][x] & 0xFFFF0000u);
+          }
+      }
+    }
+    if (s0 + SG < ns) issue(s0 + SG);
+  }
+  // W_UV,h fragments of this wave (rows 32w .. 32w+31, all 512 columns);
+  // their loads fly while o_c is staged
   u32x4 wf[DC / 32][2];
   if constexpr (UV) {
     const bf16* wv = w_uv + (size_t)h * DV * DC;
@@ -803,67 +847,17 @@ __global__ __launch_bounds__(256) void k_combine_uv(int H, int B, int q_len, int
       for (int mt = 0; mt < 2; ++mt)
         wf[ks][mt] = *(const u32x4*)(wv + (size_t)(32 * w + 16 * mt + i16) * DC + 32 * ks + 8 * G);
   }
-  {
-    const int ns = b < B && len > 0 ? ((len + PAGE - 1) / PAGE + pps - 1) / pps : 0;
-    float M = q < ns ? ml_q[0] : -INFINITY;
-    for (int sp = q + 16; sp < ns; sp += 16) M = fmaxf(M, ml[2 * sp]);
+  const float il = ns > 0 ? 1.f / l : 0.f;
 #pragma unroll
-    for (int o = 8; o > 0; o >>= 1) M = fmaxf(M, __shfl_xor(M, o, 64));
-    float l = 0.f;
-    for (int sp = q; sp < splits; sp += 16) {
-      const float m_sp = sp == q ? ml_q[0] : ml[2 * sp];
-      const float l_sp = sp == q ? ml_q[1] : ml[2 * sp + 1];
-      const float e = sp < ns ? __builtin_amdgcn_exp2f(m_sp - M) : 0.f;
-      wgt[r][sp] = e;
-      if (sp < ns) l += e * l_sp;
-    }
+  for (int u = 0; u < 4; ++u) {
+    bf16x8_t v;
 #pragma unroll
-    for (int o = 8; o > 0; o >>= 1) l += __shfl_xor(l, o, 64);
-    if (q == 0) inv_l[r] = ns > 0 ? 1.f / l : 0.f;
-  }
-  __syncthreads();
-  {
-    // 16 threads per sequence; thread q takes columns 8q + 128u .. +7 (u < 4)
-    const int r = tid >> 4, q = tid & 15, b = b0 + r;
-    float acc[4][8] = {};
-    if (b < B) {
-      const bf16* po = part_o + ((size_t)h * B + b) * splits * DC + 8 * q;
-      // two splits' loads in flight per step; splits past the context were
-      // never written, so their (arbitrary) values are selected away, not scaled
-      for (int s = 0; s < splits; s += 2) {
-        u32x4 v[2][4];
-#pragma unroll
-        for (int d = 0; d < 2; ++d)
-#pragma unroll
-          for (int u = 0; u < 4; ++u)
-            v[d][u] = s + d < splits ? *(const u32x4*)(po + (size_t)(s + d) * DC + 128 * u) : (u32x4){0, 0, 0, 0};
-#pragma unroll
-        for (int d = 0; d < 2; ++d) {
-          const float e = s + d < splits ? wgt[r][s + d] : 0.f;
-#pragma unroll
-          for (int u = 0; u < 4; ++u)
-#pragma unroll
-            for (int x = 0; x < 4; ++x) {
-              const float lo = __uint_as_float(v[d][u][x] << 16), hi = __uint_as_float(v[d][u][x] & 0xFFFF0000u);
-              acc[u][2 * x] += e != 0.f ? e * lo : 0.f;
-              acc[u][2 * x + 1] += e != 0.f ? e * hi : 0.f;
-            }
-        }
-      }
-    }
-    const float il = inv_l[r];
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      bf16x8_t v;
-#pragma unroll
-      for (int x = 0; x < 8; ++x) v[x] = (__bf16)(acc[u][x] * il);
-      *(bf16x8_t*)&oc[r * LDO + 8 * q + 128 * u] = v;
-    }
+    for (int x = 0; x < 8; ++x) v[x] = (__bf16)(acc[u][x] * il);
+    *(bf16x8_t*)&oc[r * LDO + 8 * q + 128 * u] = v;
   }
   __syncthreads();
   if constexpr (!UV) {
-    // o_c rows of the 16 sequences: 16 threads per row, 64 bytes each
-    const int r = tid >> 4, q = tid & 15, b = b0 + r;
+    // o_c rows of the 16 query rows: 16 threads per row, 64 bytes each
     if (b < B) {
       bf16* dst = out + ((size_t)b * H + h) * DC + 32 * q;
 #pragma unroll
@@ -871,21 +865,21 @@ __global__ __launch_bounds__(256) void k_combine_uv(int H, int B, int q_len, int
     }
     return;
   }
-  // wave w: outputs v = 32w .. 32w+31 (two 16-row tiles), all 16 sequences
-  f32x4 acc[2] = {};
+  // wave w: outputs v = 32w .. 32w+31 (two 16-row tiles), all 16 query rows
+  f32x4 oacc[2] = {};
 #pragma unroll
   for (int ks = 0; ks < DC / 32; ++ks) {
     const bf16x8_t bo = as_bf16x8(*(const u32x4*)&oc[i16 * LDO + 32 * ks + 8 * G]);
 #pragma unroll
     for (int mt = 0; mt < 2; ++mt)
-      acc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(wf[ks][mt]), bo, acc[mt], 0, 0, 0);
+      oacc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(wf[ks][mt]), bo, oacc[mt], 0, 0, 0);
   }
   const int bo_seq = b0 + i16;
   if (bo_seq < B) {
 #pragma unroll
     for (int mt = 0; mt < 2; ++mt) {
       typedef __attribute__((ext_vector_type(4))) __bf16 bf16x4_t;
-      const bf16x4_t v = {(__bf16)acc[mt][0], (__bf16)acc[mt][1], (__bf16)acc[mt][2], (__bf16)acc[mt][3]};
+      const bf16x4_t v = {(__bf16)oacc[mt][0], (__bf16)oacc[mt][1], (__bf16)oacc[mt][2], (__bf16)oacc[mt][3]};
       *(bf16x4_t*)(out + ((size_t)bo_seq * H + h) * DV + 32 * w + 16 * mt + 4 * G) = v;
     }
   }
@@ -910,7 +904,7 @@ hipError_t decode_absorb(const mla_dims& d, float scale, int rows, int q_len, co
   ProfScope ps(prof_name, s);
   RopeFreq rope;
   for (int i = 0; i < DR / 2; ++i) rope.theta[i] = pow((double)d.rope_base, -2.0 * i / (double)DR);
-  hipLaunchKernelGGL(k_absorb, dim3(d.n_heads, DC / 64), dim3(256), 0, s, rows, d.n_heads, q_len,
+  hipLaunchKernelGGL(k_absorb, dim3(d.n_heads, DC / 128), dim3(256), 0, s, rows, d.n_heads, q_len,
                      (const bf16*)q_nope, (const bf16*)q_pe, (const bf16*)w_uk, ctx_lens, scale * LOG2E, rope,
                      (bf16*)qt);
   return hipGetLastError();
