@@ -115,6 +115,7 @@ SMALL = [
     ("H128 q1 ragged", 128, 1, [1, 129, 1000], True),
     ("H128 q1 identity pages", 128, 1, [64, 2047], False),
     ("H32 q1 long", 32, 1, [5000, 3], True),
+    ("H128 q1 eight rows", 128, 1, [1, 64, 65, 700, 2000, 4097, 130, 3000], True),
     ("H1", 1, 1, [129, 1, 640], True),
     ("H100", 100, 1, [129, 1, 640], True),
     ("H128 q2 pairs", 128, 2, [2, 64, 65, 127, 128, 129, 1500, 2047], True),

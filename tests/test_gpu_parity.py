@@ -58,6 +58,8 @@ SMALL = [
     ("H128 ragged tails", 128, [1, 129, 1000], True),
     ("H128 identity pages", 128, [64, 2047], False),
     ("H32 long", 32, [5000, 3], True),
+    # 8 rows of ragged length, up to 17 splits each (some past the context)
+    ("H128 eight rows", 128, [1, 64, 65, 700, 2000, 4097, 130, 3000], True),
 ]
 
 
