@@ -38,5 +38,15 @@ def test_decode_traffic_summaries_are_found_under_the_names_the_bench_builds(spl
     assert bench.os.path.exists(bench.os.path.join(bench.PROFILES, f"{name}_hbm_traffic.md")), name
 
 
+def test_traffic_summaries_of_the_smaller_and_ragged_decodes_are_found():
+    # workload 2 (B=16, H=16, L=4096) and workload 4 (B=32, H=128, contexts
+    # drawn on [1024, 32768] with seed 1504: the longest is 31044)
+    from synth import make_ragged_lens
+    lens = make_ragged_lens(1504, 32, 1024, 32768)
+    for b, h, L in ((16, 16, 4096), (32, 128, int(max(lens)))):
+        name = bench.split_traffic_name("mla_decode_split", b, 1, h, L, False)
+        assert bench.os.path.exists(bench.os.path.join(bench.PROFILES, f"{name}_hbm_traffic.md")), name
+
+
 def test_prefill_traffic_summary_is_found_under_the_name_the_bench_builds():
     assert bench.os.path.exists(bench.os.path.join(bench.PROFILES, "mla_prefill_attn_B4_S4096_H128_hbm_traffic.md"))
