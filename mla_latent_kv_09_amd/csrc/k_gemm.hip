@@ -3,9 +3,10 @@
 // Both operands are K-contiguous ([rows, K] row-major), the orientation of the
 // pages' [out, in] weights applied to [tokens, in] activations.
 //
-// Block tile: 256 rows of A x 128 rows of B, K in steps of 64 through a ring of
-// three LDS stages filled by direct 16-byte HBM -> LDS copies. Four waves, each
-// owning 128 A-rows x 64 B-rows as 4 x 2 tiles of 32 x 32. Each wave computes
+// Block tile: 256 rows of A x 128 (or 256) rows of B, K in steps of 64
+// through a ring of LDS stages filled by direct 16-byte HBM -> LDS copies.
+// Four (or eight) waves, each owning 128 A-rows x 64 B-rows as 4 x 2 tiles of
+// 32 x 32 (or 4 x 4 with 256-wide tiles and four waves). Each wave computes
 // the transposed tile C^T[n, m] (B rows as the MFMA M side), so a lane ends with
 // 4 consecutive output columns n of one row m: RoPE pairs (2i, 2i+1) sit in one
 // lane and stores are 8 bytes wide.
@@ -28,22 +29,29 @@ namespace mla {
 namespace {
 
 constexpr int BM = 256, BK = 64;
-constexpr int G_THREADS = 256;
 constexpr int A_STAGE = BM * BK * 2;  // 32 KB
 constexpr int HEAD_W = 128;  // head width of the per-head epilogues
-constexpr int A_LOADS = BM * BK * 2 / 16 / G_THREADS;  // 8 per lane
 
-// Block tile 256 x BN with BN = 64 NI: each wave owns 128 A-rows x 32 NI
-// B-rows (4 x NI MFMA tiles of 32 x 32). NI = 2: 256 x 128, three 48 KB
-// stages; NI = 4: 256 x 256, two 64 KB stages (half the copies per MFMA).
-template <int NI>
+// Block tile 256 x BN with BN = 64 NI, WAVES waves: two along the A rows (128
+// each) and WAVES / 2 along the B rows, so each wave owns 128 A-rows x
+// 64 NI / (WAVES / 2) B-rows (4 x NW MFMA tiles of 32 x 32). NI = 2: 256 x
+// 128, three 48 KB stages; NI = 4: 256 x 256, two 64 KB stages (half the
+// copies per MFMA). With 8 waves (NI = 4 only) two waves share each SIMD, so
+// one wave's copies, LDS reads and epilogue stores issue while the other's
+// MFMAs run; each then holds 128 accumulators instead of 256.
+template <int NI, int WAVES>
 struct Tile {
+  static constexpr int THREADS = 64 * WAVES;
+  static constexpr int WN = WAVES / 2;
+  static constexpr int NW = 2 * NI / WN;  // 32-wide B tiles per wave
   static constexpr int BN = 64 * NI;
   static constexpr int B_STAGE = BN * BK * 2;
   static constexpr int STAGE = A_STAGE + B_STAGE;
   static constexpr int N_STAGES = NI == 2 ? 3 : 2;
-  static constexpr int B_LOADS = B_STAGE / 16 / G_THREADS;  // 4 or 8 per lane
+  static constexpr int A_LOADS = A_STAGE / 16 / THREADS;  // 8 or 4 per lane
+  static constexpr int B_LOADS = B_STAGE / 16 / THREADS;  // 4 or 8 (or 4) per lane
   static constexpr int LOADS = A_LOADS + B_LOADS;
+  static_assert(NW >= 1 && 2 * WN == WAVES, "wave layout");
 };
 
 template <int N>
@@ -80,11 +88,11 @@ __device__ __forceinline__ const bf16* b_row_ptr(const GemmArgs& g, int n) {
   return n < g.n_split ? g.b0 + (size_t)n * g.ldb : g.b1 + (size_t)(n - g.n_split) * g.ldb;
 }
 
-template <int EPI, int NI>
-__global__ __launch_bounds__(G_THREADS, 1) void k_gemm(GemmArgs g) {
-  using TL = Tile<NI>;
+template <int EPI, int NI, int WAVES>
+__global__ __launch_bounds__(64 * WAVES, 1) void k_gemm(GemmArgs g) {
+  using TL = Tile<NI, WAVES>;
   constexpr int BN = TL::BN, STAGE = TL::STAGE, N_STAGES = TL::N_STAGES, B_LOADS = TL::B_LOADS;
-  constexpr int LOADS = TL::LOADS;
+  constexpr int LOADS = TL::LOADS, A_LOADS = TL::A_LOADS, NW = TL::NW, G_THREADS = TL::THREADS;
   // the K-step stages, reused at the end to stage the output tile (rows of
   // 256 columns plus 16 bytes of padding)
   constexpr int CT_PITCH = 256 + 8;  // bf16 elements per staged row
@@ -105,7 +113,7 @@ __global__ __launch_bounds__(G_THREADS, 1) void k_gemm(GemmArgs g) {
   }
   const int m0 = mt * BM, n0 = nt * BN;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
-  const int wm = w & 1, wn = w >> 1;  // wave covers A rows m0 + 128wm .., B rows n0 + 32 NI wn ..
+  const int wm = w & 1, wn = w >> 1;  // wave covers A rows m0 + 128wm .., B rows n0 + 32 NW wn ..
   const int k_steps = g.K / BK;
 
   // per-lane source rows and LDS positions of the copies (fixed over K)
@@ -140,10 +148,10 @@ __global__ __launch_bounds__(G_THREADS, 1) void k_gemm(GemmArgs g) {
   // operand read offsets inside a stage: MFMA A side = B rows (n), B side = A rows (m)
   //   step s (16 of K) reads chunk 2s + g of its row
   const int hl = lane & 31, gq = lane >> 5;
-  int an_off[NI][4], bm_off[4][4];  // [tile][k-step within BK]
+  int an_off[NW][4], bm_off[4][4];  // [tile][k-step within BK]
 #pragma unroll
-  for (int i = 0; i < NI; ++i) {
-    const int r = 32 * NI * wn + 32 * i + hl;
+  for (int i = 0; i < NW; ++i) {
+    const int r = 32 * NW * wn + 32 * i + hl;
 #pragma unroll
     for (int s = 0; s < 4; ++s) an_off[i][s] = A_STAGE + r * 128 + (((2 * s + gq) ^ g_swz(r)) << 4);
   }
@@ -154,9 +162,9 @@ __global__ __launch_bounds__(G_THREADS, 1) void k_gemm(GemmArgs g) {
     for (int s = 0; s < 4; ++s) bm_off[j][s] = r * 128 + (((2 * s + gq) ^ g_swz(r)) << 4);
   }
 
-  f32x16 acc[NI][4];  // [n tile][m tile]
+  f32x16 acc[NW][4];  // [n tile][m tile]
 #pragma unroll
-  for (int i = 0; i < NI; ++i)
+  for (int i = 0; i < NW; ++i)
 #pragma unroll
     for (int j = 0; j < 4; ++j) acc[i][j] = (f32x16){};
 
@@ -165,7 +173,7 @@ __global__ __launch_bounds__(G_THREADS, 1) void k_gemm(GemmArgs g) {
   // ks + N_STAGES - 1 a quarter at a time before each 16-wide sub-step, so the
   // texture unit drains them behind the MFMAs. Operand fragments are read one
   // sub-step ahead into a second register set.
-  bf16x8_t fa[2][NI], fb[2][4];
+  bf16x8_t fa[2][NW], fb[2][4];
   for (int ks = 0; ks < k_steps; ++ks) {
     if (N_STAGES == 3 && ks + 1 < k_steps) g_wait_vmcnt<(N_STAGES == 3 ? LOADS : 0)>();
     else g_wait_vmcnt<0>();
@@ -174,7 +182,7 @@ __global__ __launch_bounds__(G_THREADS, 1) void k_gemm(GemmArgs g) {
     const LDS_AS char* st = (const LDS_AS char*)(lds + (ks % N_STAGES) * STAGE);
     auto read_frags = [&](int sub, int set) __attribute__((always_inline)) {
 #pragma unroll
-      for (int i = 0; i < NI; ++i) fa[set][i] = g_as_bf16x8(*(const LDS_AS u32x4*)(st + an_off[i][sub]));
+      for (int i = 0; i < NW; ++i) fa[set][i] = g_as_bf16x8(*(const LDS_AS u32x4*)(st + an_off[i][sub]));
 #pragma unroll
       for (int j = 0; j < 4; ++j) fb[set][j] = g_as_bf16x8(*(const LDS_AS u32x4*)(st + bm_off[j][sub]));
     };
@@ -186,7 +194,7 @@ __global__ __launch_bounds__(G_THREADS, 1) void k_gemm(GemmArgs g) {
 #pragma unroll
         for (int q = s * LOADS / 4; q < (s + 1) * LOADS / 4; ++q) load_one(next, q);
 #pragma unroll
-      for (int i = 0; i < NI; ++i)
+      for (int i = 0; i < NW; ++i)
 #pragma unroll
         for (int j = 0; j < 4; ++j)
           acc[i][j] = EPI == 2 ? __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[s & 1][j], fa[s & 1][i], acc[i][j], 0, 0, 0)
@@ -207,7 +215,7 @@ __global__ __launch_bounds__(G_THREADS, 1) void k_gemm(GemmArgs g) {
       typedef __attribute__((ext_vector_type(4))) __bf16 bf16x4_t;
       typedef __attribute__((ext_vector_type(2))) uint32_t u32x2_t;
 #pragma unroll
-      for (int i = 0; i < NI; ++i)
+      for (int i = 0; i < NW; ++i)
 #pragma unroll
         for (int j = 0; j < 4; ++j)
 #pragma unroll
@@ -215,8 +223,8 @@ __global__ __launch_bounds__(G_THREADS, 1) void k_gemm(GemmArgs g) {
             const bf16x4_t o = {(__bf16)acc[i][j][4 * q], (__bf16)acc[i][j][4 * q + 1], (__bf16)acc[i][j][4 * q + 2],
                                 (__bf16)acc[i][j][4 * q + 3]};
             // EPI 2 holds C^T[n][m .. m+3]: staged as rows n; others C[m][n .. n+3]: rows m
-            const int row = EPI == 2 ? 32 * NI * wn + 32 * i + hl : 128 * wm + 32 * j + hl;
-            const int col = EPI == 2 ? 128 * wm + 32 * j + 8 * q + 4 * gq : 32 * NI * wn + 32 * i + 8 * q + 4 * gq;
+            const int row = EPI == 2 ? 32 * NW * wn + 32 * i + hl : 128 * wm + 32 * j + hl;
+            const int col = EPI == 2 ? 128 * wm + 32 * j + 8 * q + 4 * gq : 32 * NW * wn + 32 * i + 8 * q + 4 * gq;
             *(LDS_AS u32x2_t*)(ct + row * CT_PITCH + col) = __builtin_bit_cast(u32x2_t, o);
           }
       g_lds_barrier();
@@ -260,11 +268,11 @@ __global__ __launch_bounds__(G_THREADS, 1) void k_gemm(GemmArgs g) {
   }
   const int n_heads = g.N / HEAD_W;
   if constexpr (EPI == 2) {
-    // lane holds C[m .. m+3][n] for n = n0 + 32 NI wn + 32i + hl,
+    // lane holds C[m .. m+3][n] for n = n0 + 32 NW wn + 32i + hl,
     // m = m0 + 128wm + 32j + 8q + 4gq (q = r / 4)
 #pragma unroll
-    for (int i = 0; i < NI; ++i) {
-      const int n = n0 + 32 * NI * wn + 32 * i + hl;
+    for (int i = 0; i < NW; ++i) {
+      const int n = n0 + 32 * NW * wn + 32 * i + hl;
       if (n >= g.N) continue;
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
@@ -286,7 +294,7 @@ __global__ __launch_bounds__(G_THREADS, 1) void k_gemm(GemmArgs g) {
     return;
   }
   // epilogue: lane holds C[m][n .. n+3] for m = m0 + 128wm + 32j + hl,
-  // n = n0 + 32 NI wn + 32i + 8q + 4gq (q = r / 4)
+  // n = n0 + 32 NW wn + 32i + 8q + 4gq (q = r / 4)
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
     const int m = m0 + 128 * wm + 32 * j + hl;
@@ -299,10 +307,10 @@ __global__ __launch_bounds__(G_THREADS, 1) void k_gemm(GemmArgs g) {
     }
     const int seq_b = seq_of[j >> 1], seq_t = m - seq_b * g.a_seq;
 #pragma unroll
-    for (int i = 0; i < NI; ++i)
+    for (int i = 0; i < NW; ++i)
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
-        const int n = n0 + 32 * NI * wn + 32 * i + 8 * q + 4 * gq;
+        const int n = n0 + 32 * NW * wn + 32 * i + 8 * q + 4 * gq;
         if (n >= g.N) continue;
         float v[4] = {acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]};
         typedef __attribute__((ext_vector_type(4))) __bf16 bf16x4_t;
@@ -345,16 +353,19 @@ hipError_t gemm_fast(const GemmArgs& g, int epi, hipStream_t s) {
   // times over (and no partial tile); 128-wide otherwise
   const bool wide = epi != 1 && g.N % 256 == 0 && m_tiles * (g.N / 256) >= 1024;
   const int grid = m_tiles * (wide ? g.N / 256 : (g.N + 127) / 128);
-  auto go = [&](auto kern) { hipLaunchKernelGGL(kern, dim3(grid), dim3(G_THREADS), 0, s, g); };
+  auto go = [&](auto kern, int waves) { hipLaunchKernelGGL(kern, dim3(grid), dim3(64 * waves), 0, s, g); };
+  // The K/V up-projections (K = 512: eight K steps, then a 128 KB output
+  // tile) run 8 waves, two per SIMD, which measured 7 % faster there; the
+  // long-K query up-projection stays at 4 waves, where 8 measured 3 % slower.
   if (wide) {
-    if (epi == 2) go(k_gemm<2, 4>);
-    else if (epi == 3) go(k_gemm<3, 4>);
-    else go(k_gemm<0, 4>);
+    if (epi == 2) go(k_gemm<2, 4, 8>, 8);
+    else if (epi == 3) go(k_gemm<3, 4, 8>, 8);
+    else go(k_gemm<0, 4, 4>, 4);
   } else {
-    if (epi == 1) go(k_gemm<1, 2>);
-    else if (epi == 2) go(k_gemm<2, 2>);
-    else if (epi == 3) go(k_gemm<3, 2>);
-    else go(k_gemm<0, 2>);
+    if (epi == 1) go(k_gemm<1, 2, 4>, 4);
+    else if (epi == 2) go(k_gemm<2, 2, 4>, 4);
+    else if (epi == 3) go(k_gemm<3, 2, 4>, 4);
+    else go(k_gemm<0, 2, 4>, 4);
   }
   return hipGetLastError();
 }

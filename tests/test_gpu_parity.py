@@ -13,7 +13,7 @@ import mla_latent_kv_09_amd as mla
 import oracle
 from synth import Dims, from_torch, make_decode_case, make_project_case, to_torch, workload
 
-from gpu_helpers import assert_parity, device_cache, fails_bar, run_decode
+from gpu_helpers import assert_parity, assert_projection_parity, device_cache, fails_bar, run_decode
 
 pytestmark = pytest.mark.gpu
 
@@ -157,8 +157,8 @@ def test_project_with_query_path_then_prefill_small():
     # rows are stored in bf16: allow one bf16 rounding step of the fp64 value
     assert np.all(np.abs(got_rows - ref_rows) <= 2 ** -7 * np.abs(ref_rows) + 1e-3)
     ref_qn, ref_qp = oracle.query_projection(case.h, case.w_dq, case.w_uq, case.w_qr, 16, 128, 64)
-    assert_parity(from_torch(qn), ref_qn, "bf16", "q_nope")
-    assert_parity(from_torch(qp), ref_qp, "bf16", "q_pe")
+    assert_projection_parity(from_torch(qn), ref_qn, "q_nope")
+    assert_projection_parity(from_torch(qp), ref_qp, "q_pe")
     ref = oracle.prefill(dims, ref_qn.reshape(2, 100, 16, 128), ref_qp.reshape(2, 100, 16, 64), case.w_uk,
                          case.w_uv, oracle.round_to(ref_rows, "bf16").reshape(2, 100, -1))
     assert_parity(from_torch(out), ref, "bf16", "prefill")
@@ -430,13 +430,37 @@ def test_mfma_projection_and_prefill_ragged():
     ref_rows = oracle.latent_rows(case.h, case.w_dkv, case.w_kr, case.positions)
     _check_rows(got_rows, ref_rows)
     ref_qn, ref_qp = oracle.query_projection(case.h, case.w_dq, case.w_uq, case.w_qr, 128, 128, 64)
-    assert_parity(qn, ref_qn, "bf16", "q_nope")
-    assert_parity(qp, ref_qp, "bf16", "q_pe")
+    assert_projection_parity(qn, ref_qn, "q_nope")
+    assert_projection_parity(qp, ref_qp, "q_pe")
     queries = [(0, 0), (0, 1), (0, 63), (0, 64), (0, 127), (0, 128), (1, 200), (1, 255), (1, 256), (1, 299)]
     ref = oracle.prefill(dims, oracle.round_to(ref_qn, "bf16").reshape(2, 300, 128, 128),
                          oracle.round_to(ref_qp, "bf16").reshape(2, 300, 128, 64), case.w_uk, case.w_uv,
                          oracle.round_to(ref_rows, "bf16").reshape(2, 300, -1), queries=queries)
     got = out.reshape(2, 300, 128, 128)[[b for b, _ in queries], [s for _, s in queries]]
+    assert_parity(got, ref, "bf16", "prefill")
+
+
+def test_wide_gemm_tiles_projection_and_prefill():
+    """4200 tokens at H = 128: the query up-projection (N = 24576, 17 x 96
+    tiles of 256 x 256) and the K/V up-projections of prefill (N = 16384, 17 x
+    64 tiles) take the 256 x 256 GEMM tiles, with a ragged last row tile.
+    q_nope and q_pe are compared element by element; the prefill output on
+    sampled queries whose keys span every row tile."""
+    _log("wide GEMM tiles: projection + prefill, B=1 S=4200 H=128")
+    dims = Dims(128, **V3)
+    S = 4200
+    case = make_project_case(32, batch=1, seq_len=S, d_model=512, dims=dims, d_q=256, shuffle=True)
+    got_rows, qn, qp, out = _project_and_prefill(case, dims, 256)
+    ref_rows = oracle.latent_rows(case.h, case.w_dkv, case.w_kr, case.positions)
+    _check_rows(got_rows, ref_rows)
+    ref_qn, ref_qp = oracle.query_projection(case.h, case.w_dq, case.w_uq, case.w_qr, 128, 128, 64)
+    assert_projection_parity(qn, ref_qn, "q_nope")
+    assert_projection_parity(qp, ref_qp, "q_pe")
+    picks = [0, 255, 256, 2047, 4096, S - 1]
+    ref = oracle.prefill(dims, oracle.round_to(ref_qn, "bf16").reshape(1, S, 128, 128),
+                         oracle.round_to(ref_qp, "bf16").reshape(1, S, 128, 64), case.w_uk, case.w_uv,
+                         oracle.round_to(ref_rows, "bf16").reshape(1, S, -1), queries=[(0, s) for s in picks])
+    got = out.reshape(1, S, 128, 128)[0, picks]
     assert_parity(got, ref, "bf16", "prefill")
 
 
@@ -463,8 +487,8 @@ def test_projection_with_odd_head_widths(H, d_nope, d_rope):
     got_n, got_p = from_torch(qn), from_torch(qp)
     assert np.all(got_n[T * H * d_nope:] == 7.0) and np.all(got_p[T * H * d_rope:] == 7.0)
     ref_qn, ref_qp = oracle.query_projection(case.h, case.w_dq, case.w_uq, case.w_qr, H, d_nope, d_rope)
-    assert_parity(got_n[:T * H * d_nope].reshape(T, H, d_nope), ref_qn, "bf16", "q_nope")
-    assert_parity(got_p[:T * H * d_rope].reshape(T, H, d_rope), ref_qp, "bf16", "q_pe")
+    assert_projection_parity(got_n[:T * H * d_nope].reshape(T, H, d_nope), ref_qn, "q_nope")
+    assert_projection_parity(got_p[:T * H * d_rope].reshape(T, H, d_rope), ref_qp, "q_pe")
     ref_rows = oracle.latent_rows(case.h, case.w_dkv, case.w_kr, case.positions)
     _check_rows(from_torch(rows)[case.slots // 64, case.slots % 64], ref_rows)
 
@@ -482,8 +506,8 @@ def test_workload5_full_size_sampled():
     picks = [0, 1, 777, 2048, S - 1]
     ids = [sample_b * S + s for s in picks]
     ref_qn, ref_qp = oracle.query_projection(case.h[ids], case.w_dq, case.w_uq, case.w_qr, 128, 128, 64)
-    assert_parity(qn[ids], ref_qn, "bf16", "q_nope")
-    assert_parity(qp[ids], ref_qp, "bf16", "q_pe")
+    assert_projection_parity(qn[ids], ref_qn, "q_nope")
+    assert_projection_parity(qp[ids], ref_qp, "q_pe")
     qn_full = np.zeros((1, S, 128, 128))
     qp_full = np.zeros((1, S, 128, 64))
     qn_full[0, picks] = oracle.round_to(ref_qn, "bf16")
