@@ -69,68 +69,107 @@ __global__ __launch_bounds__(256) void k_fold_wo(int d_model, int H, int dv, int
   }
 }
 
-constexpr int RG_N = 64;   // weight rows per workgroup
-constexpr int RG_M = 64;   // activation rows per workgroup
-constexpr int RG_K = 32;   // k per MFMA step
+constexpr int RG_N = 64;     // weight rows per workgroup
+constexpr int RG_M = 64;     // activation rows per workgroup
+constexpr int RG_K = 32;     // k per MFMA step
+constexpr int RG_SK = 128;   // k per LDS stage: 4 MFMA steps, one per wave
+constexpr int RG_STAGES = 5;
+constexpr int RG_TILE_BYTES = 64 * RG_SK * 2;            // 16 KB: 64 rows x 256 bytes
+constexpr int RG_STAGE_BYTES = 2 * RG_TILE_BYTES;        // weight tile, then activation tile
+constexpr int RG_DMA = RG_TILE_BYTES / 16 / 256;         // 4 copies per lane per tile
+static_assert(RG_STAGES * RG_STAGE_BYTES <= 160 * 1024, "LDS budget of one workgroup");
+
+template <int N>
+__device__ __forceinline__ void rg_wait_vmcnt() {
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x0F70);
+}
+__device__ __forceinline__ void rg_lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+// one 16-byte HBM -> LDS copy per lane, to lds_addr + 16 * lane (lds_addr
+// wave-uniform, through M0); base uniform, voff the lane's byte offset. Issued
+// from asm so that the compiler does not drain all loads before each LDS read;
+// the kernel orders the copies with explicit vmcnt waits before the barrier
+// that publishes a stage. Nothing else in the kernel uses M0.
+__device__ __forceinline__ void rg_dma16(const void* base, uint32_t voff, uint32_t lds_addr) {
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(base), "s"(lds_addr)
+               : "memory", "m0");
+}
 
 // grid (ceil(N / 64), splits, ceil(M / 64)); 4 waves. The workgroup computes
-// C^T[n, m] for 64 weight rows n and 64 activation rows m over its k slice;
-// wave w takes the slice's MFMA steps w, w + 4, ... with all 64 x 64 outputs
-// (4 x 4 tiles of 16 x 16: A = W rows, lane row n0 + 16i + l%16, k + 8(l/16)
-// .. +7; B = X rows, lane row m0 + 16t + l%16, the same k), so each weight
-// and activation fragment loaded feeds four MFMAs and the activations cost no
-// more bytes than the weight. The next step's fragments are requested before
-// the current step's MFMAs. The four waves' sums are added in LDS at the end.
-// Rows past M or N are clamped to the last row (read, never stored).
-__global__ __launch_bounds__(256) void k_rowgemm(int M, int N, int K, int kc, const bf16* __restrict__ x,
-                                                 const bf16* __restrict__ wt, float* __restrict__ part) {
-  __shared__ __attribute__((aligned(16))) float red[RG_M * RG_N];  // [m][n], 16 KB
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, i16 = lane & 15, G = lane >> 4;
+// C^T[n, m] for 64 weight rows n and 64 activation rows m over its k slice.
+// Both operands stream to LDS in stages of 64 rows x 128 k (each copy
+// instruction moves four whole 256-byte row segments) through a ring of five
+// stages, four in flight, so 64 KB of the weight stream per CU is outstanding
+// without holding any of it in registers (and with no register loads in the
+// loop, whose waits the compiler would place behind the copies). Tile
+// position p (16-byte units) holds chunk (p % 16) ^ (row % 16) of row p / 16,
+// so the 16 rows that one fragment read touches sit in 16 distinct bank
+// groups. Wave w takes MFMA step w of every stage with all 64 x 64 outputs
+// (4 x 4 tiles of 16 x 16: A = weight rows, lane row 16i + l%16, k + 8(l/16)
+// .. +7; B = activation rows 16t + l%16, the same k), so each fragment feeds
+// four MFMAs; the four waves' sums are added in LDS at the end. Rows past M
+// or N are clamped to the last row (read, never stored). K % 128 == 0 and
+// kc % 128 == 0.
+__global__ __launch_bounds__(256, 1) void k_rowgemm(int M, int N, int K, int kc, const bf16* __restrict__ x,
+                                                    const bf16* __restrict__ wt, float* __restrict__ part) {
+  __shared__ __attribute__((aligned(1024))) char lds[RG_STAGES * RG_STAGE_BYTES];  // 160 KB
+  const int lane = threadIdx.x & 63, w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int i16 = lane & 15, G = lane >> 4;
   const int n0 = blockIdx.x * RG_N, sp = blockIdx.y, m0 = blockIdx.z * RG_M;
   const int k_begin = sp * kc, k_end = min(K, k_begin + kc);
-  const int mt = min(4, (M - m0 + 15) / 16);  // activation tiles with any row
-  const bf16* wrow[4];
-  const bf16* xrow[4];
+  const int n_st = (k_end - k_begin) / RG_SK;
+  // copy j of wave w fills tile positions (4w + j) * 64 + lane
+  const bf16* wbase = wt + (size_t)n0 * K + k_begin;
+  const bf16* xbase = x + (size_t)m0 * K + k_begin;
+  uint32_t w_off[RG_DMA], x_off[RG_DMA];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    wrow[i] = wt + (size_t)min(n0 + 16 * i + i16, N - 1) * K + 8 * G;
-    xrow[i] = x + (size_t)min(m0 + 16 * i + i16, M - 1) * K + 8 * G;
+  for (int j = 0; j < RG_DMA; ++j) {
+    const int pos = (4 * w + j) * 64 + lane, r = pos >> 4, c = (pos & 15) ^ (r & 15);
+    w_off[j] = (uint32_t)(min(n0 + r, N - 1) - n0) * (uint32_t)K * 2u + 16u * c;
+    x_off[j] = (uint32_t)(min(m0 + r, M - 1) - m0) * (uint32_t)K * 2u + 16u * c;
   }
+  const uint32_t lds_base = (uint32_t)(size_t)(LDS_AS char*)lds;
+  auto issue_stage = [&](int st) {
+    const uint32_t dst = __builtin_amdgcn_readfirstlane(lds_base + (st % RG_STAGES) * RG_STAGE_BYTES +
+                                                        w * RG_DMA * 1024);
+    const char* ws = (const char*)(wbase + st * RG_SK);
+    const char* xs = (const char*)(xbase + st * RG_SK);
+#pragma unroll
+    for (int j = 0; j < RG_DMA; ++j) rg_dma16(ws, w_off[j], dst + j * 1024);
+#pragma unroll
+    for (int j = 0; j < RG_DMA; ++j) rg_dma16(xs, x_off[j], dst + RG_TILE_BYTES + j * 1024);
+  };
+  // fragment reads: row 16i + i16 of a tile, chunk (4w + G) ^ i16
+  const uint32_t f_off = (uint32_t)(i16 * 256 + (((4 * w + G) ^ i16) << 4));
+
   f32x4 acc[4][4] = {};  // [weight tile i][activation tile t]
-  // weight fragments two steps ahead (the HBM stream), activations one (cached)
-  u32x4 a0[4], a1[4], a2[4], b0[4], b1[4];
-  auto load_w = [&](u32x4 (&a)[4], int k) {
+  for (int st = 0; st < RG_STAGES - 1 && st < n_st; ++st) issue_stage(st);
+  for (int st = 0; st < n_st; ++st) {
+    // stage st's copies (8 per lane) are done once at most those of the
+    // stages after it that were issued are still out
+    const int after = min(RG_STAGES - 2, n_st - 1 - st);
+    if (after >= 3) rg_wait_vmcnt<3 * 2 * RG_DMA>();
+    else if (after == 2) rg_wait_vmcnt<2 * 2 * RG_DMA>();
+    else if (after == 1) rg_wait_vmcnt<2 * RG_DMA>();
+    else rg_wait_vmcnt<0>();
+    rg_lds_barrier();  // stage st visible to all; stage st - 1 (the slot of st + 4) read by all
+    if (st + RG_STAGES - 1 < n_st) issue_stage(st + RG_STAGES - 1);
+    const LDS_AS char* sb = (const LDS_AS char*)lds + (st % RG_STAGES) * RG_STAGE_BYTES + f_off;
+    u32x4 a[4], bx[4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) a[i] = k < k_end ? *(const u32x4*)(wrow[i] + k) : (u32x4){0, 0, 0, 0};
-  };
-  auto load_x = [&](u32x4 (&b)[4], int k) {
+    for (int i = 0; i < 4; ++i) a[i] = *(const LDS_AS u32x4*)(sb + i * 16 * 256);
 #pragma unroll
-    for (int t = 0; t < 4; ++t) b[t] = (t < mt && k < k_end) ? *(const u32x4*)(xrow[t] + k) : (u32x4){0, 0, 0, 0};
-  };
-  constexpr int STRIDE = 4 * RG_K;  // this wave's steps
-  int k = k_begin + RG_K * w;
-  load_w(a0, k);
-  load_x(b0, k);
-  load_w(a1, k + STRIDE);
-  for (; k < k_end; k += STRIDE) {
-    load_w(a2, k + 2 * STRIDE);
-    load_x(b1, k + STRIDE);
+    for (int t = 0; t < 4; ++t) bx[t] = *(const LDS_AS u32x4*)(sb + RG_TILE_BYTES + t * 16 * 256);
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
       for (int t = 0; t < 4; ++t)
-        if (t < mt)
-          acc[i][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a0[i]),
-                                                              __builtin_bit_cast(bf16x8_t, b0[t]), acc[i][t], 0, 0, 0);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      a0[i] = a1[i];
-      a1[i] = a2[i];
-      b0[i] = b1[i];
-    }
+        acc[i][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a[i]),
+                                                            __builtin_bit_cast(bf16x8_t, bx[t]), acc[i][t], 0, 0, 0);
   }
   // lane holds C^T[n0 + 16i + 4G + r][m0 + 16t + l%16]: 4 consecutive n of one m
+  float* red = (float*)lds;  // [m][n], 16 KB
   for (int ww = 0; ww < 4; ++ww) {
+    rg_lds_barrier();  // the stages (or the previous wave's sums) are done with
     if (w == ww) {
 #pragma unroll
       for (int i = 0; i < 4; ++i)
@@ -145,8 +184,8 @@ __global__ __launch_bounds__(256) void k_rowgemm(int M, int N, int K, int kc, co
           }
         }
     }
-    __syncthreads();
   }
+  rg_lds_barrier();
   // 64 rows m of 64 n: 16 threads per row, 4 n each
 #pragma unroll
   for (int u = 0; u < 4; ++u) {
@@ -185,7 +224,7 @@ RowPlan row_plan(int M, int N, int K) {
   const int max_splits = (K + 1023) / 1024;
   splits = splits < 1 ? 1 : (splits > max_splits ? max_splits : splits);
   int kc = (K + splits - 1) / splits;
-  kc = (kc + 4 * RG_K - 1) / (4 * RG_K) * (4 * RG_K);
+  kc = (kc + RG_SK - 1) / RG_SK * RG_SK;
   RowPlan p;
   p.kc = kc;
   p.splits = (K + kc - 1) / kc;
@@ -193,7 +232,7 @@ RowPlan row_plan(int M, int N, int K) {
 }
 
 bool row_path(const mla_dims& d, int M, int N, int K) {
-  return d.dtype == MLA_BF16 && M <= 256 && K % 32 == 0 && N % 4 == 0;
+  return d.dtype == MLA_BF16 && M <= 256 && K % RG_SK == 0 && N % 4 == 0;
 }
 
 }  // namespace
