@@ -69,8 +69,8 @@ __global__ __launch_bounds__(256) void k_fold_wo(int d_model, int H, int dv, int
   }
 }
 
-constexpr int RG_N = 64;     // weight rows per workgroup
-constexpr int RG_M = 64;     // activation rows per workgroup
+constexpr int RG_N = 64;     // weight rows per work item
+constexpr int RG_M = 64;     // activation rows per work item
 constexpr int RG_K = 32;     // k per MFMA step
 constexpr int RG_SK = 128;   // k per LDS stage: 4 MFMA steps, one per wave
 constexpr int RG_STAGES = 5;
@@ -78,6 +78,7 @@ constexpr int RG_TILE_BYTES = 64 * RG_SK * 2;            // 16 KB: 64 rows x 256
 constexpr int RG_STAGE_BYTES = 2 * RG_TILE_BYTES;        // weight tile, then activation tile
 constexpr int RG_DMA = RG_TILE_BYTES / 16 / 256;         // 4 copies per lane per tile
 static_assert(RG_STAGES * RG_STAGE_BYTES <= 160 * 1024, "LDS budget of one workgroup");
+static_assert(RG_M * RG_N * 4 <= RG_STAGE_BYTES, "an item's sums fit in one stage");
 
 template <int N>
 __device__ __forceinline__ void rg_wait_vmcnt() {
@@ -94,66 +95,87 @@ __device__ __forceinline__ void rg_dma16(const void* base, uint32_t voff, uint32
                : "memory", "m0");
 }
 
-// grid (ceil(N / 64), splits, ceil(M / 64)); 4 waves. The workgroup computes
-// C^T[n, m] for 64 weight rows n and 64 activation rows m over its k slice.
-// Both operands stream to LDS in stages of 64 rows x 128 k (each copy
+// Persistent: one workgroup of 4 waves per CU walks the work items
+// blockIdx.x, blockIdx.x + gridDim.x, ... An item (weight tile nt, k slice sp,
+// activation tile mt) computes C^T[n, m] for 64 weight rows n and 64
+// activation rows m over k in [sp kc, (sp + 1) kc): the partial sum
+// part[sp][m][n]. The stages of all of a workgroup's items form one stream:
+// weight and activation tiles of 64 rows x 128 k go HBM -> LDS (each copy
 // instruction moves four whole 256-byte row segments) through a ring of five
-// stages, four in flight, so 64 KB of the weight stream per CU is outstanding
-// without holding any of it in registers (and with no register loads in the
-// loop, whose waits the compiler would place behind the copies). Tile
-// position p (16-byte units) holds chunk (p % 16) ^ (row % 16) of row p / 16,
-// so the 16 rows that one fragment read touches sit in 16 distinct bank
+// stages, four in flight across item boundaries, so 64 KB of the weight per
+// CU stays outstanding from the first stage to the last, with no register
+// loads in the loop (whose waits the compiler would place behind the copies).
+// Tile position p (16-byte units) holds chunk (p % 16) ^ (row % 16) of row
+// p / 16, so the 16 rows one fragment read touches sit in 16 distinct bank
 // groups. Wave w takes MFMA step w of every stage with all 64 x 64 outputs
-// (4 x 4 tiles of 16 x 16: A = weight rows, lane row 16i + l%16, k + 8(l/16)
-// .. +7; B = activation rows 16t + l%16, the same k), so each fragment feeds
-// four MFMAs; the four waves' sums are added in LDS at the end. Rows past M
-// or N are clamped to the last row (read, never stored). K % 128 == 0 and
-// kc % 128 == 0.
-__global__ __launch_bounds__(256, 1) void k_rowgemm(int M, int N, int K, int kc, const bf16* __restrict__ x,
-                                                    const bf16* __restrict__ wt, float* __restrict__ part) {
-  __shared__ __attribute__((aligned(1024))) char lds[RG_STAGES * RG_STAGE_BYTES];  // 160 KB
+// (4 x 4 tiles of 16 x 16: A = weight rows, lane row 16i + l%16, k +
+// 8(l/16) .. +7; B = activation rows 16t + l%16, the same k), so each
+// fragment feeds four MFMAs. At an item's last stage the four waves' sums
+// are added in LDS, in the slot of that stage (whose next copies are issued
+// only after the following barrier), and stored. Rows past M or N are
+// clamped to the last row
+// (read, never stored). K % 128 == 0 and kc % 128 == 0, kc divides K.
+__global__ __launch_bounds__(256, 1) void k_rowgemm(int M, int N, int K, int kc, int n_items,
+                                                    const bf16* __restrict__ x, const bf16* __restrict__ wt,
+                                                    float* __restrict__ part) {
+  __shared__ __attribute__((aligned(1024))) char lds[RG_STAGES * RG_STAGE_BYTES];
   const int lane = threadIdx.x & 63, w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int i16 = lane & 15, G = lane >> 4;
-  const int n0 = blockIdx.x * RG_N, sp = blockIdx.y, m0 = blockIdx.z * RG_M;
-  const int k_begin = sp * kc, k_end = min(K, k_begin + kc);
-  const int n_st = (k_end - k_begin) / RG_SK;
-  // copy j of wave w fills tile positions (4w + j) * 64 + lane
-  const bf16* wbase = wt + (size_t)n0 * K + k_begin;
-  const bf16* xbase = x + (size_t)m0 * K + k_begin;
-  uint32_t w_off[RG_DMA], x_off[RG_DMA];
+  const int n_tiles = (N + RG_N - 1) / RG_N, m_tiles = (M + RG_M - 1) / RG_M;
+  const int spi = kc / RG_SK;  // stages per item
+  const int my_items = n_items > (int)blockIdx.x ? (n_items - 1 - (int)blockIdx.x) / (int)gridDim.x + 1 : 0;
+  const int total = my_items * spi;
+  // item j of this workgroup: id = blockIdx.x + j gridDim.x = (sp n_tiles + nt) m_tiles + mt, so the
+  // items that run at the same time share k slices (and the activation rows in L2)
+  auto item_coords = [&](int j, int& nt, int& sp, int& mt) {
+    const int id = (int)blockIdx.x + j * (int)gridDim.x;
+    mt = id % m_tiles;
+    nt = (id / m_tiles) % n_tiles;
+    sp = id / (m_tiles * n_tiles);
+  };
+  // copy j of wave w fills tile positions (4w + j) * 64 + lane: row r, chunk c
+  uint32_t rel[RG_DMA];  // r * K * 2 + 16 c (the row is clamped per item)
+  int rows_r[RG_DMA];
 #pragma unroll
   for (int j = 0; j < RG_DMA; ++j) {
     const int pos = (4 * w + j) * 64 + lane, r = pos >> 4, c = (pos & 15) ^ (r & 15);
-    w_off[j] = (uint32_t)(min(n0 + r, N - 1) - n0) * (uint32_t)K * 2u + 16u * c;
-    x_off[j] = (uint32_t)(min(m0 + r, M - 1) - m0) * (uint32_t)K * 2u + 16u * c;
+    rows_r[j] = r;
+    rel[j] = 16u * c;
   }
   const uint32_t lds_base = (uint32_t)(size_t)(LDS_AS char*)lds;
-  auto issue_stage = [&](int st) {
-    const uint32_t dst = __builtin_amdgcn_readfirstlane(lds_base + (st % RG_STAGES) * RG_STAGE_BYTES +
+  auto issue_stage = [&](int g) {
+    int nt, sp, mt;
+    item_coords(g / spi, nt, sp, mt);
+    const int st = g % spi, n0 = nt * RG_N, m0 = mt * RG_M;
+    const size_t k0 = (size_t)sp * kc + (size_t)st * RG_SK;
+    const char* ws = (const char*)(wt + (size_t)n0 * K + k0);
+    const char* xs = (const char*)(x + (size_t)m0 * K + k0);
+    const uint32_t dst = __builtin_amdgcn_readfirstlane(lds_base + (g % RG_STAGES) * RG_STAGE_BYTES +
                                                         w * RG_DMA * 1024);
-    const char* ws = (const char*)(wbase + st * RG_SK);
-    const char* xs = (const char*)(xbase + st * RG_SK);
 #pragma unroll
-    for (int j = 0; j < RG_DMA; ++j) rg_dma16(ws, w_off[j], dst + j * 1024);
+    for (int j = 0; j < RG_DMA; ++j)
+      rg_dma16(ws, (uint32_t)(min(n0 + rows_r[j], N - 1) - n0) * (uint32_t)K * 2u + rel[j], dst + j * 1024);
 #pragma unroll
-    for (int j = 0; j < RG_DMA; ++j) rg_dma16(xs, x_off[j], dst + RG_TILE_BYTES + j * 1024);
+    for (int j = 0; j < RG_DMA; ++j)
+      rg_dma16(xs, (uint32_t)(min(m0 + rows_r[j], M - 1) - m0) * (uint32_t)K * 2u + rel[j],
+               dst + RG_TILE_BYTES + j * 1024);
   };
   // fragment reads: row 16i + i16 of a tile, chunk (4w + G) ^ i16
   const uint32_t f_off = (uint32_t)(i16 * 256 + (((4 * w + G) ^ i16) << 4));
 
   f32x4 acc[4][4] = {};  // [weight tile i][activation tile t]
-  for (int st = 0; st < RG_STAGES - 1 && st < n_st; ++st) issue_stage(st);
-  for (int st = 0; st < n_st; ++st) {
-    // stage st's copies (8 per lane) are done once at most those of the
+  for (int g = 0; g < RG_STAGES - 1 && g < total; ++g) issue_stage(g);
+  for (int g = 0; g < total; ++g) {
+    // stage g's copies (8 per lane) are done once at most those of the
     // stages after it that were issued are still out
-    const int after = min(RG_STAGES - 2, n_st - 1 - st);
+    const int after = min(RG_STAGES - 2, total - 1 - g);
     if (after >= 3) rg_wait_vmcnt<3 * 2 * RG_DMA>();
     else if (after == 2) rg_wait_vmcnt<2 * 2 * RG_DMA>();
     else if (after == 1) rg_wait_vmcnt<2 * RG_DMA>();
     else rg_wait_vmcnt<0>();
-    rg_lds_barrier();  // stage st visible to all; stage st - 1 (the slot of st + 4) read by all
-    if (st + RG_STAGES - 1 < n_st) issue_stage(st + RG_STAGES - 1);
-    const LDS_AS char* sb = (const LDS_AS char*)lds + (st % RG_STAGES) * RG_STAGE_BYTES + f_off;
+    rg_lds_barrier();  // stage g visible to all; stage g - 1 (the slot of g + 4) read by all
+    if (g + RG_STAGES - 1 < total) issue_stage(g + RG_STAGES - 1);
+    const LDS_AS char* sb = (const LDS_AS char*)lds + (g % RG_STAGES) * RG_STAGE_BYTES + f_off;
     u32x4 a[4], bx[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) a[i] = *(const LDS_AS u32x4*)(sb + i * 16 * 256);
@@ -165,33 +187,44 @@ __global__ __launch_bounds__(256, 1) void k_rowgemm(int M, int N, int K, int kc,
       for (int t = 0; t < 4; ++t)
         acc[i][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a[i]),
                                                             __builtin_bit_cast(bf16x8_t, bx[t]), acc[i][t], 0, 0, 0);
-  }
-  // lane holds C^T[n0 + 16i + 4G + r][m0 + 16t + l%16]: 4 consecutive n of one m
-  float* red = (float*)lds;  // [m][n], 16 KB
-  for (int ww = 0; ww < 4; ++ww) {
-    rg_lds_barrier();  // the stages (or the previous wave's sums) are done with
-    if (w == ww) {
+    if (g % spi != spi - 1) continue;
+    // last stage of an item: lane holds C^T[n0 + 16i + 4G + r][m0 + 16t + l%16]
+    // (4 consecutive n of one m); the waves add theirs in turn into [m][n]
+    // sums in this stage's slot, once every wave has read its fragments
+    float* red = (float*)(lds + (g % RG_STAGES) * RG_STAGE_BYTES);
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
+    for (int ww = 0; ww < 4; ++ww) {
+      rg_lds_barrier();
+      if (w == ww) {
 #pragma unroll
-        for (int t = 0; t < 4; ++t) {
-          float* r = red + (16 * t + i16) * RG_N + 16 * i + 4 * G;
-          if (ww == 0) {
-            *(f32x4*)r = acc[i][t];
-          } else {
-            const f32x4 o = *(const f32x4*)r;
-            *(f32x4*)r = (f32x4){o[0] + acc[i][t][0], o[1] + acc[i][t][1], o[2] + acc[i][t][2], o[3] + acc[i][t][3]};
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+          for (int t = 0; t < 4; ++t) {
+            float* r = red + (16 * t + i16) * RG_N + 16 * i + 4 * G;
+            if (ww == 0) {
+              *(f32x4*)r = acc[i][t];
+            } else {
+              const f32x4 o = *(const f32x4*)r;
+              *(f32x4*)r = (f32x4){o[0] + acc[i][t][0], o[1] + acc[i][t][1], o[2] + acc[i][t][2],
+                                   o[3] + acc[i][t][3]};
+            }
+            acc[i][t] = (f32x4){0.f, 0.f, 0.f, 0.f};
           }
-        }
+      }
     }
-  }
-  rg_lds_barrier();
-  // 64 rows m of 64 n: 16 threads per row, 4 n each
+    rg_lds_barrier();
+    int nt, sp, mt;
+    item_coords(g / spi, nt, sp, mt);
+    const int n0 = nt * RG_N, m0 = mt * RG_M;
+    // 64 rows m of 64 n: 16 threads per row, 4 n each
 #pragma unroll
-  for (int u = 0; u < 4; ++u) {
-    const int mm = 16 * u + (threadIdx.x >> 4), nn = 4 * (threadIdx.x & 15);
-    const int m = m0 + mm, n = n0 + nn;
-    if (m < M && n < N) *(f32x4*)(part + ((size_t)sp * M + m) * N + n) = *(const f32x4*)(red + mm * RG_N + nn);
+    for (int u = 0; u < 4; ++u) {
+      const int mm = 16 * u + (threadIdx.x >> 4), nn = 4 * (threadIdx.x & 15);
+      const int m = m0 + mm, n = n0 + nn;
+      if (m < M && n < N) *(f32x4*)(part + ((size_t)sp * M + m) * N + n) = *(const f32x4*)(red + mm * RG_N + nn);
+    }
+    // the copies into this slot are issued only after the next stage's
+    // barrier, which every wave reaches after these reads
   }
 }
 
@@ -213,22 +246,39 @@ __global__ __launch_bounds__(256) void k_rowgemm_sum(int M, int N, int splits, c
 }
 
 struct RowPlan {
-  int splits, kc;
+  int splits, kc, items, grid;
 };
 
-// enough workgroups to stream the weight from every CU (about 1024), with k
-// slices of at least 1024 so the partial sums stay small against the weight
-RowPlan row_plan(int M, int N, int K) {
+// k slices: kc a multiple of 128 that divides K. A CU streams its items one
+// after another at a rate set by the bytes it keeps in flight, so the time
+// goes as (rounds of items per CU) x (weight bytes per item), plus the fp32
+// partial sums of every slice (written, then read by the sum), spread over
+// all CUs; the plan takes the slice count with the least of that.
+RowPlan row_plan(int M, int N, int K, int cus) {
   const int tiles = ((N + RG_N - 1) / RG_N) * ((M + RG_M - 1) / RG_M);
-  int splits = (1024 + tiles - 1) / tiles;
-  const int max_splits = (K + 1023) / 1024;
-  splits = splits < 1 ? 1 : (splits > max_splits ? max_splits : splits);
-  int kc = (K + splits - 1) / splits;
-  kc = (kc + RG_SK - 1) / RG_SK * RG_SK;
-  RowPlan p;
-  p.kc = kc;
-  p.splits = (K + kc - 1) / kc;
-  return p;
+  const int S = K / RG_SK;
+  const double w_bytes = 2.0 * N * K, p_bytes = 8.0 * M * N;
+  RowPlan best{1, K, tiles, tiles < cus ? tiles : cus};
+  double best_cost = -1.0;
+  for (int s = 1; s <= S && s <= 64; ++s) {
+    if (S % s) continue;
+    const int items = tiles * s;
+    const int rounds = (items + cus - 1) / cus;
+    const double cost = rounds * w_bytes / items + (s > 1 ? p_bytes * s / cus : 0.0);
+    if (best_cost < 0.0 || cost < best_cost) {
+      best_cost = cost;
+      best = RowPlan{s, K / s, items, items < cus ? items : cus};
+    }
+  }
+  return best;
+}
+
+int device_cus() {
+  int dev = 0, cus = 256;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
+    cus = 256;
+  return cus;
 }
 
 bool row_path(const mla_dims& d, int M, int N, int K) {
@@ -239,7 +289,7 @@ bool row_path(const mla_dims& d, int M, int N, int K) {
 
 size_t rows_times_weight_workspace(const mla_dims& d, int M, int N, int K) {
   if (!row_path(d, M, N, K)) return 0;
-  const RowPlan p = row_plan(M, N, K);
+  const RowPlan p = row_plan(M, N, K, device_cus());
   return (size_t)p.splits * M * N * sizeof(float);
 }
 
@@ -247,10 +297,10 @@ hipError_t rows_times_weight(const mla_dims& d, int M, int N, int K, const void*
                              void* ws, size_t ws_bytes, const char* prof_name, hipStream_t s) {
   ProfScope ps(prof_name, s);
   if (row_path(d, M, N, K)) {
-    const RowPlan p = row_plan(M, N, K);
+    const RowPlan p = row_plan(M, N, K, device_cus());
     if (ws_bytes < (size_t)p.splits * M * N * sizeof(float)) return hipErrorInvalidValue;
-    hipLaunchKernelGGL(k_rowgemm, dim3((N + RG_N - 1) / RG_N, p.splits, (M + RG_M - 1) / RG_M), dim3(256), 0, s, M, N,
-                       K, p.kc, (const bf16*)x, (const bf16*)w, (float*)ws);
+    hipLaunchKernelGGL(k_rowgemm, dim3(p.grid), dim3(256), 0, s, M, N, K, p.kc, p.items, (const bf16*)x,
+                       (const bf16*)w, (float*)ws);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     const size_t quads = (size_t)M * N / 4;
