@@ -214,6 +214,25 @@ def test_mfma_path_is_selected_for_the_v3_shape():
     assert mla.mla_decode_path(Dims(4, 32, 8, 16, 16, dtype="f32")) == 0
 
 
+def test_decode_at_the_longest_context_of_the_fast_path():
+    """One sequence of 2^20 - 5 tokens: 16384 pages, the most the MFMA decode
+    takes (runs of 64 pages, one page number per lane; 256 splits, the most
+    the combine merges), with a ragged last page and shuffled pages. Checked
+    against the oracle's absorbed form (pinned equal to the explicit one),
+    which never forms the 2^20 x 128 keys per head."""
+    _log("decode at the longest fast-path context: B=1 H=16 L=2^20-5")
+    case = make_decode_case(61, 1, Dims(16, **V3), [(1 << 20) - 5], shuffle=True)
+    assert mla.mla_decode_path(case.dims) == 1
+    # a workspace is needed only on the MFMA path (the generic kernel takes none)
+    assert mla.mla_decode_workspace_size(mla.Dims.of(case.dims), 1, (1 << 20) - 5) > 0
+    got = run_decode(case)
+    _log("  GPU done, oracle (absorbed form)")
+    c = case.cache
+    ref = oracle.absorbed_decode(case.dims, case.q_nope, case.q_pe, case.w_uk, case.w_uv, c.pool, c.block_table,
+                                 c.context_lens)
+    assert_parity(got, ref, "bf16", "L = 2^20 - 5")
+
+
 @pytest.mark.parametrize("H", [1, 48, 100, 129, 256])
 def test_decode_odd_head_counts(H):
     """Up to 128 heads the MFMA path runs; 129 .. 256 (the largest head count
