@@ -149,3 +149,72 @@ def test_chunked_prefill_replays_in_a_graph():
 
     _replays_match(lambda: mla.mla_prefill(d, qn, qp, wk, wv, c, out=out, workspace=ws),
                    lambda: mla.mla_prefill(d, qn, qp, wk, wv, c), set_inputs)
+
+
+def test_output_projection_and_folded_decode_replay_in_a_graph():
+    _log("graph: mla_output_project, mla_decode_folded")
+    from synth import draw_output_weights
+    case = make_decode_case(65, 4, Dims(128, **V3), [1, 129, 1000, 3000], shuffle=True)
+    c = device_cache(case.cache)
+    d = case.dims
+    d_model = 1024
+    qn, qp = to_torch(case.q_nope).unsqueeze(1), to_torch(case.q_pe).unsqueeze(1)
+    wk, wv = to_torch(case.w_uk), to_torch(case.w_uv)
+    w_o = to_torch(draw_output_weights(66, d_model, 128, 128))
+    w_ouv = mla.mla_fold_output_weights(d, wv, w_o)
+    ws_f = torch.empty(mla.mla_decode_folded_workspace_size(d, case.batch, 1, c.max_context, d_model),
+                       dtype=torch.uint8, device="cuda")
+    y = torch.empty((case.batch, 1, d_model), dtype=torch.bfloat16, device="cuda")
+    sets = _query_sets(case, 3)
+
+    def set_inputs(k):
+        qn.copy_(to_torch(sets[k][0]).unsqueeze(1))
+        qp.copy_(to_torch(sets[k][1]).unsqueeze(1))
+
+    _replays_match(lambda: mla.mla_decode_folded(d, qn, qp, wk, w_ouv, c, out=y, workspace=ws_f),
+                   lambda: mla.mla_decode_folded(d, qn, qp, wk, w_ouv, c), set_inputs)
+
+    x = torch.empty((case.batch, 128, 128), dtype=torch.bfloat16, device="cuda")
+    ws_o = torch.empty(max(mla.mla_output_workspace_size(d, case.batch, d_model), 1), dtype=torch.uint8,
+                       device="cuda")
+    yo = torch.empty((case.batch, d_model), dtype=torch.bfloat16, device="cuda")
+    rng = np.random.default_rng(9)
+    from synth import f32_to_bf16_bits
+    xs = [f32_to_bf16_bits(rng.standard_normal((case.batch, 128, 128)).astype(np.float32) * 0.05) for _ in range(3)]
+
+    def set_x(k):
+        x.copy_(to_torch(xs[k]))
+
+    _replays_match(lambda: mla.mla_output_project(d, x, w_o, out=yo, workspace=ws_o),
+                   lambda: mla.mla_output_project(d, x, w_o), set_x)
+
+
+def test_fp8_projection_replays_in_a_graph():
+    _log("graph: mla_rope_latent_project_fp8")
+    from synth import f32_to_bf16_bits, make_project_case
+    d = Dims(128, **V3)
+    case = make_project_case(67, batch=2, seq_len=130, d_model=512, dims=d, shuffle=True)
+    T, nb = case.n_tokens, case.num_blocks
+    pb = mla.mla_fp8_page_bytes(d, 64)
+    h = to_torch(case.h)
+    wd, wr = to_torch(case.w_dkv), to_torch(case.w_kr)
+    pos, slots = to_torch(case.positions), to_torch(case.slots)
+    pages = torch.zeros((nb, pb), dtype=torch.uint8, device="cuda")
+    ws = torch.empty(max(mla.mla_project_fp8_workspace_size(d, T), 1), dtype=torch.uint8, device="cuda")
+    rng = np.random.default_rng(11)
+    hs = [case.h] + [f32_to_bf16_bits(rng.standard_normal(case.h.shape).astype(np.float32)) for _ in range(2)]
+
+    def set_inputs(k):
+        h.copy_(to_torch(hs[k]))
+
+    def capture():
+        mla.mla_rope_latent_project_fp8(d, h, wd, wr, pos, slots, pages, 64, workspace=ws)
+        return pages
+
+    def eager():
+        fresh = torch.zeros_like(pages)
+        mla.mla_rope_latent_project_fp8(d, h, wd, wr, pos, slots, fresh, 64)
+        torch.cuda.synchronize()
+        return fresh
+
+    _replays_match(capture, eager, set_inputs)
