@@ -190,3 +190,45 @@ def dequantize_pool(pages, page: int, d_c: int, d_rope: int) -> np.ndarray:
     the rows the attention over an FP8 cache reads."""
     codes, kbits, E = unpack_pages(pages, page, d_c, d_rope)
     return dequantize_rows(codes, kbits, E).reshape(np.asarray(pages).shape[0], page, d_c + d_rope)
+
+
+# ------------------------------------------------ decode with an FP8 query --
+def fp8_query_decode(dims, q_nope, q_pe, w_uk, w_uv, pool, block_table, context_lens, drop_page=None):
+    """Decode over a (dequantised) cache with the absorbed query in the form
+    an FP8 decode feeds it to an FP8 product, for one query per sequence.
+
+    The decode itself is "DeepSeek-V2 paper digest" §2.2-2.3 in its absorbed
+    form (scores c_t . q_abs + k_pe,t . RoPE(q_pe), values W_UV,h sum_t p_t c_t);
+    the FP8 cache is [IP] §6.3. What this adds is the query rounding that the
+    library's FP8 decode declares: with lam = softmax scale * log2(e), the
+    latent part lam * W_UK,h^T q_nope and the rotary part lam * RoPE(q_pe) are
+    each rounded to bfloat16, and the latent part is then quantised like a
+    cache row (one power-of-two scale per head, codes RNE to E4M3). Scores are
+    then base-2 logits of the rounded query; everything else is exact (fp64).
+
+    drop_page = (b, j) leaves logical page j (64 tokens) of sequence b out of
+    the attention while the query keeps its position (a negative control)."""
+    from .mla import _head_rows, gather_rows, rope, round_to, widen
+    H, dn, dv, dc = dims.n_heads, dims.d_nope, dims.d_v, dims.d_c
+    lam = dims.scale * np.log2(np.e)
+    wuk, wuv = widen(w_uk), widen(w_uv)
+    qn_all, qp_all = widen(q_nope), widen(q_pe)
+    B = qn_all.shape[0]
+    out = np.empty((B, H, dv))
+    for b in range(B):
+        rows = gather_rows(pool, block_table, context_lens, b)
+        L = rows.shape[0]
+        keep = np.ones(L, dtype=bool)
+        if drop_page is not None and drop_page[0] == b:
+            keep[64 * drop_page[1]:64 * (drop_page[1] + 1)] = False
+        c, kpe = rows[keep, :dc], rows[keep, dc:]
+        qpe = rope(qp_all[b], L - 1, dims.rope_base)
+        for h in range(H):
+            q_c = round_to(lam * (_head_rows(wuk, h, dn).T @ qn_all[b, h]), "bf16")
+            e = scale_exponent(np.abs(q_c).max())
+            q_c8 = e4m3_round(q_c * 2.0 ** (-e)) * 2.0 ** e
+            q_r = round_to(lam * qpe[h], "bf16")
+            s2 = c @ q_c8 + kpe @ q_r
+            p = np.exp2(s2 - s2.max())
+            out[b, h] = _head_rows(wuv, h, dv) @ (p @ c) / p.sum()
+    return out

@@ -32,11 +32,19 @@ def bar(dtype):
     weight the same again, so the output's normwise error sits near 3 %
     (measured 2-4 % on the oracle with those roundings); the bar allows
     8 % = 1.3 * 2^-4, and 15 % of max|ref| for the largest element. There is
-    no absolute bar: short contexts have outputs near 1."""
+    no absolute bar: short contexts have outputs near 1.
+
+    "fp8q" is the same decode against the oracle's decode with the query
+    rounded as the FP8 decode rounds it (fp8.fp8_query_decode), so only the
+    kernel's E4M3 rounding of the probabilities is left (a relative 2^-4 per
+    weight; 1-3 % normwise when simulated with the exact row max as the
+    reference): normwise 4 %, 10 % of max|ref| for the largest element."""
     if dtype == "f32":
         return 1e-4, 1e-4, 1e-4
     if dtype == "fp8":
         return float("inf"), 8e-2, 0.15
+    if dtype == "fp8q":
+        return float("inf"), 4e-2, 0.10
     return 2e-2, 1e-2, 5e-2
 
 

@@ -203,3 +203,81 @@ def _scale_one_low(amax):
 def test_fp8_pins_catch_planted_mistake(name, attr, fake, monkeypatch):
     monkeypatch.setattr(fp8, attr, fake)
     assert not _pins_pass(), name
+
+
+# ----------------------------------------------- decode with an FP8 query ---
+# fp8_query_decode is the oracle's decode with the absorbed query rounded the
+# way the FP8 decode feeds it to the FP8 product. Its pins: with a query that
+# every rounding keeps exact it is the plain decode; on a realistic case its
+# distance from the plain decode is that of an E4M3 rounding of the query;
+# dropping a page with a position-free query is the decode of the other pages.
+
+def _exact_query_case(seed, n_pages, L, H=2):
+    """lam = softmax scale * log2(e) = 1 and an absorbed query of integers
+    |.| <= 8 (exact in bf16 and in E4M3 at the per-head scale), rotary query 0
+    (so the score does not depend on the position)."""
+    from synth import Dims
+    import oracle
+    dims = Dims(H, 16, 8, 4, 4, softmax_scale=1.0 / np.log2(np.e))
+    rng = np.random.default_rng(seed)
+    w_uk = rng.integers(0, 2, size=(H * 4, 16)).astype(np.float64)
+    q_nope = rng.integers(-2, 3, size=(1, H, 4)).astype(np.float64)
+    q_pe = np.zeros((1, H, 8))
+    w_uv = oracle.round_to(rng.standard_normal((H * 4, 16)) * 0.25, "bf16")
+    pool = oracle.round_to(rng.standard_normal((n_pages, 64, 24)), "bf16")
+    table = rng.permutation(n_pages).astype(np.int32)[None, :]
+    lens = np.array([L], dtype=np.int32)
+    return dims, q_nope, q_pe, w_uk, w_uv, pool, table, lens
+
+
+def _fp8_query_pins_pass():
+    import oracle
+    from synth import Dims, make_decode_case
+    try:
+        # 1. exact query: equals the plain decode
+        dims, qn, qp, wuk, wuv, pool, table, lens = _exact_query_case(3, 3, 150)
+        lam = dims.scale * np.log2(np.e)
+        assert abs(lam - 1.0) < 1e-15
+        q_abs = np.stack([wuk[h * 4:(h + 1) * 4].T @ qn[0, h] for h in range(2)])
+        assert np.all(q_abs == np.round(q_abs)) and np.abs(q_abs).max() <= 8
+        got = fp8.fp8_query_decode(dims, qn, qp, wuk, wuv, pool, table, lens)
+        ref = oracle.decode(dims, qn, qp, wuk, wuv, pool, table, lens)
+        assert np.allclose(got, ref, rtol=1e-12, atol=1e-14), float(np.abs(got - ref).max())
+        # 2. dropping logical page 1 of 3 (query without a rotary part) is the
+        # decode over logical pages 0 and 2
+        got = fp8.fp8_query_decode(dims, qn, qp, wuk, wuv, pool, table, lens, drop_page=(0, 1))
+        t2 = table[:, [0, 2]]
+        ref = oracle.decode(dims, qn, qp, wuk, wuv, pool, t2, np.array([150 - 64], dtype=np.int32))
+        assert np.allclose(got, ref, rtol=1e-12, atol=1e-14), float(np.abs(got - ref).max())
+        # 3. a realistic query (V3 head widths): the rounding moves the output
+        # by an E4M3-sized amount (unit roundoff 2^-4; about 2 % here), far
+        # more than the bf16 rounding alone (about 0.15 %) and far less than
+        # 2^-3
+        case = make_decode_case(7, 1, Dims(8, 512, 64, 128, 128), [300], shuffle=True)
+        c = case.cache
+        a = fp8.fp8_query_decode(case.dims, case.q_nope, case.q_pe, case.w_uk, case.w_uv, c.pool, c.block_table,
+                                 c.context_lens)
+        b = oracle.decode(case.dims, case.q_nope, case.q_pe, case.w_uk, case.w_uv, c.pool, c.block_table,
+                          c.context_lens)
+        rel = np.linalg.norm(a - b) / np.linalg.norm(b)
+        assert 2.0 ** -7 < rel < 2.0 ** -3, rel
+    except (AssertionError, ValueError):
+        return False
+    return True
+
+
+def test_fp8_query_decode_pins_pass():
+    assert _fp8_query_pins_pass()
+
+
+def _round_nothing(x):
+    return np.asarray(x, dtype=np.float64)
+
+
+@pytest.mark.parametrize("name,attr,fake", [
+    ("query not rounded to E4M3", "e4m3_round", _round_nothing),
+    ("query scale one binade low", "scale_exponent", _scale_one_low),
+])
+def test_fp8_query_pins_catch_planted_mistake(name, attr, fake, monkeypatch):
+    monkeypatch.setattr(fp8, attr, fake)
+    assert not _fp8_query_pins_pass(), name

@@ -129,7 +129,32 @@ def test_decode_fp8_small(name, H, Q, lens, shuffle):
     _log(f"decode fp8 {name}")
     case = make_decode_case(500 + H + Q, len(lens), Dims(H, **V3), lens, shuffle=shuffle, q_len=Q)
     pages, deq = _fp8_case(case)
-    assert_parity(_run_fp8(case, pages), _oracle_fp8(case, deq), "fp8", name)
+    got = _run_fp8(case, pages)
+    assert_parity(got, _oracle_fp8(case, deq), "fp8", name)
+    if Q == 1:
+        # with the query rounded as the kernel rounds it, only the rounding
+        # of the probabilities is left: a bar twice as tight
+        c = case.cache
+        ref_q = fp8.fp8_query_decode(case.dims, case.q_nope, case.q_pe, case.w_uk, case.w_uv, deq, c.block_table,
+                                     c.context_lens)
+        assert_parity(got, ref_q, "fp8q", name + " (FP8 query)")
+
+
+def test_decode_fp8_tight_bar_catches_a_skipped_page():
+    """A page left out in the middle of a 3000-token context (the query keeping
+    its position) moves the output by several percent: within the loose bar
+    against the plain oracle (8 %) such a mistake could hide behind the
+    query's E4M3 rounding, so the tight bar against the FP8-query oracle must
+    reject it while the kernel passes."""
+    _log("decode fp8: skipped page against the FP8-query oracle")
+    case = make_decode_case(503, 2, Dims(32, **V3), [3000, 2100], shuffle=True)
+    pages, deq = _fp8_case(case)
+    got = _run_fp8(case, pages)
+    c = case.cache
+    args = (case.dims, case.q_nope, case.q_pe, case.w_uk, case.w_uv, deq, c.block_table, c.context_lens)
+    assert_parity(got, fp8.fp8_query_decode(*args), "fp8q", "3000 / 2100 tokens")
+    for b, page in ((0, 23), (1, 16)):
+        assert fails_bar(got, fp8.fp8_query_decode(*args, drop_page=(b, page)), "fp8q"), (b, page)
 
 
 def test_decode_fp8_negative_controls_fail_the_bar():
