@@ -33,6 +33,12 @@ Readings taken where the pages are silent (each a choice, stated once):
 * Page layout, for pages of P tokens: P rows of [d_c code bytes || d_rope
   bfloat16 k_pe values], then the P scale bytes, then zero bytes up to a
   multiple of 16.
+* fp8_query_decode: the pages say nothing of the query of an FP8 decode; this
+  reference takes the library's declared query arithmetic (the absorbed
+  query scaled by softmax scale * log2(e), rounded to bfloat16, its latent
+  part then quantised like a cache row with one scale per head) so that a
+  tighter bar can be set on what is left. Its pins are in
+  tests/test_fp8_pins.py.
 """
 from __future__ import annotations
 
