@@ -314,6 +314,17 @@ mla_status mla_output_workspace_size(const mla_dims* dims, int32_t n_rows, int32
 mla_status mla_decode_folded_workspace_size(const mla_dims* dims, int32_t batch, int32_t q_len,
                                             int32_t max_context, int32_t d_model, size_t* bytes);
 
+/* One call for the three core entry points, with two sizes whose meaning
+ * depends on op (the same values as the specific functions above):
+ *   MLA_OP_PROJECT  size_a = n_tokens, size_b = d_q (0: no query path)
+ *   MLA_OP_DECODE   size_a = batch,    size_b = max_context
+ *   MLA_OP_PREFILL  size_a = batch,    size_b = seq_len (no cached prefix:
+ *                   max_context = seq_len; for a prefix use
+ *                   mla_prefill_workspace_size)
+ * Another op gives MLA_ERR_UNSUPPORTED and leaves *bytes untouched. */
+typedef enum { MLA_OP_PROJECT = 0, MLA_OP_DECODE = 1, MLA_OP_PREFILL = 2 } mla_op;
+mla_status mla_workspace_size(int32_t op, const mla_dims* dims, int32_t size_a, int32_t size_b, size_t* bytes);
+
 /* Static description of a status code (never NULL). */
 const char* mla_status_string(mla_status status);
 

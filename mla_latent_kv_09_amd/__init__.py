@@ -25,7 +25,7 @@ __all__ = [
     "mla_decode_fp8_workspace_size", "mla_decode_noalloc", "mla_noalloc_scratch_bytes",
     "mla_rope_latent_project_fp8", "mla_project_fp8_workspace_size",
     "mla_output_project", "mla_output_workspace_size", "mla_fold_output_weights", "mla_decode_folded",
-    "mla_decode_folded_workspace_size",
+    "mla_decode_folded_workspace_size", "mla_workspace_size", "MLA_OP_PROJECT", "MLA_OP_DECODE", "MLA_OP_PREFILL",
     "mla_status_string", "mla_decode_path", "mla_prefill_path", "mla_version",
 ]
 
@@ -33,6 +33,7 @@ _PKG = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_PKG, "libmla.so")
 
 MLA_F32, MLA_BF16 = 0, 1
+MLA_OP_PROJECT, MLA_OP_DECODE, MLA_OP_PREFILL = 0, 1, 2
 _TORCH_DTYPE = {MLA_F32: torch.float32, MLA_BF16: torch.bfloat16}
 
 
@@ -104,6 +105,7 @@ def library():
         lib.mla_decode_workspace_size.argtypes = [pd, i32, i32, ctypes.POINTER(sz)]
         lib.mla_decode_multi_workspace_size.argtypes = [pd, i32, i32, i32, ctypes.POINTER(sz)]
         lib.mla_prefill_workspace_size.argtypes = [pd, i32, i32, i32, ctypes.POINTER(sz)]
+        lib.mla_workspace_size.argtypes = [i32, pd, i32, i32, ctypes.POINTER(sz)]
         lib.mla_status_string.argtypes = [ctypes.c_int]
         lib.mla_status_string.restype = ctypes.c_char_p
         lib.mla_decode_path.argtypes = [pd, i32, i32]
@@ -113,7 +115,8 @@ def library():
         for f in ("mla_rope_latent_project", "mla_decode", "mla_decode_multi", "mla_prefill",
                   "mla_project_workspace_size", "mla_decode_workspace_size", "mla_decode_multi_workspace_size",
                   "mla_prefill_workspace_size", "mla_profile_begin", "mla_profile_only", "mla_decode_fp8",
-                  "mla_quantize_fp8", "mla_fp8_page_bytes", "mla_decode_fp8_workspace_size"):
+                  "mla_quantize_fp8", "mla_fp8_page_bytes", "mla_decode_fp8_workspace_size",
+                  "mla_workspace_size"):
             getattr(lib, f).restype = ctypes.c_int
         for f in ("mla_decode_path", "mla_prefill_path", "mla_version"):
             getattr(lib, f).restype = ctypes.c_int32
@@ -298,6 +301,15 @@ def mla_prefill_workspace_size(dims, batch: int, seq_len: int, max_context: int)
     n = ctypes.c_size_t(0)
     _ok(library().mla_prefill_workspace_size(ctypes.byref(Dims.of(dims).c()), batch, seq_len, max_context,
                                              ctypes.byref(n)), "mla_prefill_workspace_size")
+    return n.value
+
+
+def mla_workspace_size(op: int, dims, size_a: int, size_b: int) -> int:
+    """Workspace of MLA_OP_PROJECT (n_tokens, d_q), MLA_OP_DECODE (batch,
+    max_context) or MLA_OP_PREFILL (batch, seq_len) (see include/mla.h)."""
+    n = ctypes.c_size_t(0)
+    _ok(library().mla_workspace_size(op, ctypes.byref(Dims.of(dims).c()), size_a, size_b, ctypes.byref(n)),
+        "mla_workspace_size")
     return n.value
 
 

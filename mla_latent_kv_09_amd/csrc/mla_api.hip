@@ -148,6 +148,15 @@ mla_status mla_prefill_workspace_size(const mla_dims* d, int32_t batch, int32_t 
   return MLA_OK;
 }
 
+mla_status mla_workspace_size(int32_t op, const mla_dims* d, int32_t size_a, int32_t size_b, size_t* bytes) {
+  switch (op) {
+    case MLA_OP_PROJECT: return mla_project_workspace_size(d, size_a, size_b, bytes);
+    case MLA_OP_DECODE: return mla_decode_workspace_size(d, size_a, size_b, bytes);
+    case MLA_OP_PREFILL: return mla_prefill_workspace_size(d, size_a, size_b, size_b, bytes);
+    default: return MLA_ERR_UNSUPPORTED;
+  }
+}
+
 int32_t mla_decode_path(const mla_dims* d, int32_t block_size, int32_t paged) {
   if (check_dims(d) != MLA_OK) return -1;
   mla::CacheView v{};

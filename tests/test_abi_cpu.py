@@ -213,3 +213,18 @@ def test_workspace_sizes_and_paths():
     assert mla.mla_decode_path(V3(dtype=9), 64, 1) == -1
     with pytest.raises(mla.MLAError):
         mla.mla_decode_workspace_size(V3(dtype=9), 1, 1)
+
+
+def test_one_workspace_call_for_the_three_core_entry_points():
+    d = V3()
+    assert mla.mla_workspace_size(mla.MLA_OP_PROJECT, d, 16, 1536) == mla.mla_project_workspace_size(d, 16, 1536)
+    assert mla.mla_workspace_size(mla.MLA_OP_DECODE, d, 64, 8192) == mla.mla_decode_workspace_size(d, 64, 8192)
+    assert mla.mla_workspace_size(mla.MLA_OP_PREFILL, d, 4, 4096) == \
+        mla.mla_prefill_workspace_size(d, 4, 4096, 4096)
+    assert mla.mla_workspace_size(mla.MLA_OP_DECODE, d, 64, 8192) > 0
+    lib = mla.library()
+    n = ctypes.c_size_t(12345)
+    assert lib.mla_workspace_size(7, ctypes.byref(d.c() if hasattr(d, "c") else d), 1, 1, ctypes.byref(n)) == 4
+    assert n.value == 12345                               # untouched on an unknown op
+    with pytest.raises(mla.MLAError):
+        mla.mla_workspace_size(mla.MLA_OP_DECODE, d, -1, 8192)
