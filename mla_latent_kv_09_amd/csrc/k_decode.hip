@@ -263,8 +263,10 @@ __global__ __launch_bounds__(256) void k_absorb(int B, int H, int q_len, const b
 }
 
 // ------------------------------------------------------------- k_split ----
-// grid (splits, B); 256 threads (4 waves); one block per (sequence, run of
-// pages). The run is walked in tiles of 32 cache rows (half a page, 36 KB).
+// grid (splits, B, head groups); 256 threads (4 waves); one block per
+// (sequence, run of pages, group of up to 128 heads: one group unless there
+// are more than 128 heads). The run is walked in tiles of 32 cache rows (half
+// a page, 36 KB).
 //
 // Work split inside the block, per tile:
 //   scores    wave w owns heads 32w .. 32w+31: S^T[t, h] = row_t . Qt[h]
@@ -379,7 +381,10 @@ __global__ __launch_bounds__(SPLIT_THREADS, 1) void k_split(int H, int B, int q_
   // the wave index is uniform: keep it (and the LDS bases derived from it) in SGPRs
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
   const int hl = lane & 31, g = lane >> 5, i16 = lane & 15, G = lane >> 4;
-  const int h_own = w * 32 + hl;  // head of this lane in the score phase
+  // head group: blocks with blockIdx.z = z take heads 128z .. 128z+127
+  // (several groups only for more than 128 heads; each streams the run)
+  const int h0 = MAX_HEADS * blockIdx.z;
+  const int h_own = h0 + w * 32 + hl;  // head of this lane in the score phase
   const int32_t* table = block_table + (size_t)seq * max_blocks;
 
   // Streams tile i into ring slot i % 4: 9 direct-to-LDS 16-byte loads per
@@ -739,7 +744,7 @@ __global__ __launch_bounds__(SPLIT_THREADS, 1) void k_split(int H, int B, int q_
     // rows of 512 values as bf16: 64 lanes per row, 8 values (16 bytes) each
 #pragma unroll
     for (int k = 0; k < 8; ++k) {
-      const int row = 4 * k + (threadIdx.x >> 6), c8 = threadIdx.x & 63, hh = 32 * ht + row;
+      const int row = 4 * k + (threadIdx.x >> 6), c8 = threadIdx.x & 63, hh = h0 + 32 * ht + row;
       if (hh < H) {
         const f32x4 x = *(const LDS_AS f32x4*)(ost + row * OP + 8 * c8);
         const f32x4 y = *(const LDS_AS f32x4*)(ost + row * OP + 8 * c8 + 4);
@@ -889,7 +894,7 @@ __global__ __launch_bounds__(256) void k_combine_uv(int H, int B, int q_len, int
 
 bool decode_fast_supported(const mla_dims& d, const CacheView& c) {
   return d.dtype == MLA_BF16 && d.d_c == DC && d.d_rope == DR && d.d_nope == DN && d.d_v == DV &&
-         d.n_heads <= MAX_HEADS && c.paged &&
+         d.n_heads <= 2 * MAX_HEADS && c.paged &&
          c.block_size == PAGE;
 }
 
@@ -952,7 +957,7 @@ hipError_t decode_fast(const mla_dims& d, float scale, int n_seq, int q_len, int
 
   hipError_t e = decode_absorb(d, scale, batch, q_len, q_nope, q_pe, w_uk, c.context_lens, qt, "mla_decode_absorb", s);
   if (e != hipSuccess) return e;
-  const dim3 grid(p.splits, batch);
+  const dim3 grid(p.splits, batch, (H + MAX_HEADS - 1) / MAX_HEADS);
   {
     ProfScope ps("mla_decode_split", s);
     const bool pair_xcd = q_len > 1 && ((int64_t)n_seq * p.splits) % 8 == 0;

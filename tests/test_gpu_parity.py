@@ -235,10 +235,12 @@ def test_decode_at_the_longest_context_of_the_fast_path():
 
 @pytest.mark.parametrize("H", [1, 48, 100, 129, 256])
 def test_decode_odd_head_counts(H):
-    """Up to 128 heads the MFMA path runs; 129 .. 256 (the largest head count
-    the library accepts) take the generic kernels."""
+    """Every head count the library accepts (1 .. 256) runs on the MFMA path;
+    above 128 the split kernel runs head groups of 128 (129: a second group
+    of one head; 256: two full groups)."""
     _log(f"decode H={H}")
     case = make_decode_case(200 + H, 3, Dims(H, **V3), [129, 1, 640], shuffle=True)
+    assert mla.mla_decode_path(case.dims) == 1
     assert_parity(run_decode(case), oracle_decode(case), "bf16", f"H={H}")
 
 
@@ -349,6 +351,8 @@ MULTI = [
     ("H128 q2 identity pages", 128, 2, [64, 2047], False),
     # the largest q_len the library accepts; 8 sequences, so paired XCD order
     ("H8 q64 max", 8, 64, [64, 65, 100, 300, 700, 64, 1000, 129], True),
+    # two head groups of the split kernel, the second one partial
+    ("H200 q2 head groups", 200, 2, [2, 64, 700, 1500], True),
 ]
 
 
