@@ -351,6 +351,7 @@ __device__ __forceinline__ void mfma_qk_done(f32x16& acc) {
 // outstanding global loads (vmcnt 0), which would drain the tile prefetch.
 __device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
 
+template <int NHT>
 __global__ __launch_bounds__(SPLIT_THREADS, 1) void k_split(int H, int B, int q_len, bool pair_xcd, int splits,
                                                             int pps,
                                                             const bf16* __restrict__ qt,
@@ -454,11 +455,11 @@ __global__ __launch_bounds__(SPLIT_THREADS, 1) void k_split(int H, int B, int q_
   load_tile(0);
   if (n_tiles > 1) load_tile(1);
 
-  f32x16 o[4][4];  // [column tile][head tile]
+  f32x16 o[4][NHT];  // [column tile][head tile]
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) o[i][j] = (f32x16){};
+    for (int j = 0; j < NHT; ++j) o[i][j] = (f32x16){};
   float m_run = -INFINITY, l_run = 0.f;
 
   // LDS byte offsets of this lane's operand reads (lane part; the rest is a
@@ -579,7 +580,7 @@ __global__ __launch_bounds__(SPLIT_THREADS, 1) void k_split(int H, int B, int q_
     const LDS_AS char* tq = slot(i);
     const LDS_AS char* tv = slot(i - 1);
     const LDS_AS char* pb = pbuf(i - 1);
-    bf16x8_t pf[4];  // P fragments of the current PV step j (j = 0 first)
+    bf16x8_t pf[NHT];  // P fragments of the current PV step j (j = 0 first)
     bf16x8_t va[2];
     auto va_read = [&](int k) {
       const int j = k >> 2, ct = k & 3;
@@ -590,7 +591,7 @@ __global__ __launch_bounds__(SPLIT_THREADS, 1) void k_split(int H, int B, int q_
       const int ct = k & 3;
       if (k + 1 < 8) va[(k + 1) & 1] = va_read(k + 1);
 #pragma unroll
-      for (int ht = 0; ht < 4; ++ht) {
+      for (int ht = 0; ht < NHT; ++ht) {
         o[ct][ht] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[k & 1], pf[ht], o[ct][ht], 0, 0, 0);
         if (k == 3) pf[ht] = *(const LDS_AS bf16x8_t*)(pb + (2 * ht + 1) * 1024);
       }
@@ -601,7 +602,7 @@ __global__ __launch_bounds__(SPLIT_THREADS, 1) void k_split(int H, int B, int q_
     u32x4 fa[QK_AHEAD];
     if constexpr (PV) {
 #pragma unroll
-      for (int ht = 0; ht < 4; ++ht) pf[ht] = *(const LDS_AS bf16x8_t*)(pb + (2 * ht) * 1024);
+      for (int ht = 0; ht < NHT; ++ht) pf[ht] = *(const LDS_AS bf16x8_t*)(pb + (2 * ht) * 1024);
     }
     if constexpr (QK) {
 #pragma unroll
@@ -615,10 +616,10 @@ __global__ __launch_bounds__(SPLIT_THREADS, 1) void k_split(int H, int B, int q_
     // step it runs after the first score MFMAs, while their results are
     // pending, instead of holding them back until the fragments arrive.
     auto p_flags = [&]() __attribute__((always_inline)) {
-      u32x4 raw[4];
+      u32x4 raw[NHT];
       uint32_t flag = 0;
 #pragma unroll
-      for (int ht = 0; ht < 4; ++ht) {
+      for (int ht = 0; ht < NHT; ++ht) {
         raw[ht] = __builtin_bit_cast(u32x4, pf[ht]);
         flag |= (raw[ht][0] | raw[ht][1] | raw[ht][2] | raw[ht][3]) & 0x80008000u;
         u32x4 v = raw[ht];
@@ -628,7 +629,7 @@ __global__ __launch_bounds__(SPLIT_THREADS, 1) void k_split(int H, int B, int q_
       }
       if (__ballot(flag != 0)) {
 #pragma unroll
-        for (int ht = 0; ht < 4; ++ht) {
+        for (int ht = 0; ht < NHT; ++ht) {
           int kk = 0;
 #pragma unroll
           for (int q = 0; q < 4; ++q)
@@ -678,10 +679,30 @@ __global__ __launch_bounds__(SPLIT_THREADS, 1) void k_split(int H, int B, int q_
           if (8 * (r >> 2) + 4 * g + (r & 3) >= valid) sc[r] = -INFINITY;
       }
     } else if constexpr (PV) {
+      // a wave without heads of its own (fewer than 128 heads) still brings
+      // in its share of tile dma_i: two copies per value group, one more after
 #pragma unroll
       for (int k = 0; k < 4; ++k) {
         pv_group(k);
+        if (dma_i >= 0) {
+#pragma unroll
+          for (int c = 2 * k; c < 2 * k + 2; ++c) {
+            const uint32_t off = (c & 1) ? (ld_off[c / 2] >> 16) : (ld_off[c / 2] & 0xFFFFu);
+            dma16s(dma_src, off, dma_dst + c * 64 * 16);
+          }
+        }
         __builtin_amdgcn_sched_barrier(0);
+      }
+      if (dma_i >= 0) {
+        constexpr int c = TILE_LOADS - 1;
+        dma16s(dma_src, (c & 1) ? (ld_off[c / 2] >> 16) : (ld_off[c / 2] & 0xFFFFu), dma_dst + c * 64 * 16);
+      }
+    } else if (dma_i >= 0) {
+      // neither product (the first step of a wave without heads): the copies only
+#pragma unroll
+      for (int c = 0; c < TILE_LOADS; ++c) {
+        const uint32_t off = (c & 1) ? (ld_off[c / 2] >> 16) : (ld_off[c / 2] & 0xFFFFu);
+        dma16s(dma_src, off, dma_dst + c * 64 * 16);
       }
     }
 #pragma unroll
@@ -707,13 +728,19 @@ __global__ __launch_bounds__(SPLIT_THREADS, 1) void k_split(int H, int B, int q_
 #pragma unroll
   for (int s = 0; s < QK_STEPS; ++s) asm volatile("" : "+v"(qf[s]));
   lds_barrier();
+  // With fewer than 128 heads (NHT < 4 head tiles of 32), waves w >= NHT own
+  // no heads: they skip the scores and the softmax, and take only their value
+  // columns (of the NHT real head tiles) and their copies.
+  const bool qk_wave = NHT == 4 || w < NHT;
   // the copies of tile i + 2 go out during step i (spread over its score MFMAs)
-  step(T{}, F{}, 0, n_tiles > 2 ? 2 : -1);
+  if (qk_wave) step(T{}, F{}, 0, n_tiles > 2 ? 2 : -1);
+  else step(F{}, F{}, 0, n_tiles > 2 ? 2 : -1);
   for (int i = 1; i < n_tiles; ++i) {
     if (i + 1 < n_tiles) wait_vmcnt<TILE_LOADS>();  // tile i landed, tile i+1 may fly
     else wait_vmcnt<0>();
     lds_barrier();  // tile i and P of tile i-1 visible; slot (i+2)%4 and P buffer i%2 free
-    step(T{}, T{}, i, i + 2 < n_tiles ? i + 2 : -1);
+    if (qk_wave) step(T{}, T{}, i, i + 2 < n_tiles ? i + 2 : -1);
+    else step(F{}, T{}, i, i + 2 < n_tiles ? i + 2 : -1);
   }
   clear_tail(n_tiles - 1);
   lds_barrier();
@@ -731,7 +758,7 @@ __global__ __launch_bounds__(SPLIT_THREADS, 1) void k_split(int H, int B, int q_
   constexpr int OP = DC + 4;  // staged row pitch in floats (2064 bytes)
   LDS_AS float* ost = (LDS_AS float*)lds;
 #pragma unroll
-  for (int ht = 0; ht < 4; ++ht) {
+  for (int ht = 0; ht < NHT; ++ht) {
     lds_barrier();  // the previous rows (or the last step's operands) are read
 #pragma unroll
     for (int ct = 0; ct < 4; ++ct)
@@ -961,9 +988,16 @@ hipError_t decode_fast(const mla_dims& d, float scale, int n_seq, int q_len, int
   {
     ProfScope ps("mla_decode_split", s);
     const bool pair_xcd = q_len > 1 && ((int64_t)n_seq * p.splits) % 8 == 0;
-    hipLaunchKernelGGL(k_split, grid, dim3(SPLIT_THREADS), 0, s, H, batch, q_len, pair_xcd, p.splits,
-                       p.pages_per_split, qt,
-                       (const bf16*)c.rows, c.block_table, c.max_blocks, c.context_lens, part_o, part_ml);
+    // head tiles of 32 with real heads: 1 or 2 for small head counts, else 4
+    const int nht = H <= 32 ? 1 : (H <= 64 ? 2 : 4);
+    auto go = [&](auto kern) {
+      hipLaunchKernelGGL(kern, grid, dim3(SPLIT_THREADS), 0, s, H, batch, q_len, pair_xcd, p.splits,
+                         p.pages_per_split, qt, (const bf16*)c.rows, c.block_table, c.max_blocks, c.context_lens,
+                         part_o, part_ml);
+    };
+    if (nht == 1) go(k_split<1>);
+    else if (nht == 2) go(k_split<2>);
+    else go(k_split<4>);
   }
   if ((e = hipGetLastError()) != hipSuccess) return e;
   return decode_combine(d, batch, q_len, p.splits, p.pages_per_split, c.context_lens, part_o, part_ml, w_uv, out,
