@@ -71,7 +71,6 @@ __global__ __launch_bounds__(256) void k_fold_wo(int d_model, int H, int dv, int
 
 constexpr int RG_N = 64;     // weight rows per work item
 constexpr int RG_M = 64;     // activation rows per work item
-constexpr int RG_K = 32;     // k per MFMA step
 constexpr int RG_SK = 128;   // k per LDS stage: 4 MFMA steps, one per wave
 constexpr int RG_STAGES = 5;
 constexpr int RG_TILE_BYTES = 64 * RG_SK * 2;            // 16 KB: 64 rows x 256 bytes
