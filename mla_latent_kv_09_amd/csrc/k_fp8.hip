@@ -18,8 +18,9 @@
 //                 FP8 with the token's scale folded in, relative to the largest
 //                 token scale of the page, and the latent output uses the same
 //                 MFMA with that page scale.
-// The query q~ is quantised the same way (one scale per head), by the same
-// quantisation kernel, with k_pe's slice of it left in bf16.
+// The query q~ is quantised the same way (one scale per query row and head),
+// by the split kernel itself as it loads q~, with k_pe's slice of it left in
+// bf16.
 #include <math.h>
 
 #include <type_traits>
@@ -213,7 +214,7 @@ __device__ __forceinline__ void score_done(f32x16& x) {
 __device__ __forceinline__ void mfma_switch(f32x16& x) { asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" : "+v"(x)); }
 
 __global__ __launch_bounds__(THREADS, 1) void k_split8(int H, int B, int q_len, bool pair_xcd, int splits, int pps,
-                                                       const uint8_t* __restrict__ qt8, int q_page_bytes,
+                                                       const bf16* __restrict__ qt,
                                                        const uint8_t* __restrict__ pages,
                                                        const int32_t* __restrict__ block_table, int max_blocks,
                                                        const int32_t* __restrict__ ctx_lens,
@@ -279,17 +280,62 @@ __global__ __launch_bounds__(THREADS, 1) void k_split8(int H, int B, int q_len, 
   };
 
   // query of this lane's head (rows of heads >= H read head H - 1; nothing
-  // of theirs is stored): codes [32 bytes per K step], k_pe slice, scale
+  // of theirs is stored), read in bf16 and quantised here by the cache's
+  // rule (k_quant_fp8, the same operations): one power-of-two scale per
+  // (query row, head), the smallest 2^e with max|q~| <= 448 * 2^e, and codes
+  // RNE(q~ / 2^e). The lane holds latent columns 64 ks + 32 g .. +31 (its K
+  // step ks, as codes) and k_pe values 16 s + 8 g .. +7 (bf16).
   const int hq = min(h_own, H - 1);
-  const uint8_t* qrow = qt8 + (size_t)b * q_page_bytes + (size_t)hq * ROW8;
-  i32x8 qf[8];
+  const bf16* qrow = qt + ((size_t)b * H + hq) * (DC + DR);
+  u32x4 qb[8][4];
 #pragma unroll
   for (int ks = 0; ks < 8; ++ks)
-    qf[ks] = cat8(*(const u32x4*)(qrow + ks * 64 + 32 * g), *(const u32x4*)(qrow + ks * 64 + 32 * g + 16));
+#pragma unroll
+    for (int u = 0; u < 4; ++u) qb[ks][u] = *(const u32x4*)(qrow + 64 * ks + 32 * g + 8 * u);
   bf16x8_t qp[4];
 #pragma unroll
-  for (int s = 0; s < 4; ++s) qp[s] = __builtin_bit_cast(bf16x8_t, *(const u32x4*)(qrow + DC + 32 * s + 16 * g));
-  const int e_q = qt8[(size_t)b * q_page_bytes + (size_t)H * ROW8 + hq];
+  for (int s = 0; s < 4; ++s) qp[s] = __builtin_bit_cast(bf16x8_t, *(const u32x4*)(qrow + DC + 16 * s + 8 * g));
+  int e_q;
+  i32x8 qf[8];
+  {
+    // largest magnitude as bf16 bits (ordered as the magnitudes), over both
+    // halves of the head's columns (the other half is 32 lanes away)
+    uint32_t mb = 0;
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks)
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) mb = max(mb, max(qb[ks][u][q] & 0x7FFFu, (qb[ks][u][q] >> 16) & 0x7FFFu));
+    mb = max(mb, (uint32_t)__shfl_xor((int)mb, 32, 64));
+    const uint32_t fb = mb << 16;
+    const int field = (int)(fb >> 23);
+    int e = -127;
+    if (field != 0) {
+      e = field - 127 - 8;
+      if (__builtin_amdgcn_ldexpf(__uint_as_float(fb), -e) > 448.f) ++e;
+      e = max(e, -127);
+    }
+    e_q = e + 127;
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks)
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const u32x4 v = qb[ks][u];
+        float f[8];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          f[2 * q] = __builtin_amdgcn_ldexpf(__uint_as_float(v[q] << 16), -e);
+          f[2 * q + 1] = __builtin_amdgcn_ldexpf(__uint_as_float(v[q] & 0xFFFF0000u), -e);
+        }
+        int lo = __builtin_amdgcn_cvt_pk_fp8_f32(f[0], f[1], 0, false);
+        lo = __builtin_amdgcn_cvt_pk_fp8_f32(f[2], f[3], lo, true);
+        int hi = __builtin_amdgcn_cvt_pk_fp8_f32(f[4], f[5], 0, false);
+        hi = __builtin_amdgcn_cvt_pk_fp8_f32(f[6], f[7], hi, true);
+        qf[ks][2 * u] = lo;
+        qf[ks][2 * u + 1] = hi;
+      }
+  }
   wait_vmcnt<0>();
   {
     const char* src0 = copy_src(0);
@@ -663,17 +709,15 @@ bool decode_fp8_supported(const mla_dims& d, const CacheView& c) {
 
 namespace {
 struct Ws8 {
-  size_t qt, qt8, part_o, part_ml, total;
-  int splits, pps, q_page;
+  size_t qt, part_o, part_ml, total;
+  int splits, pps;
 };
 size_t al256(size_t x) { return (x + 255) & ~(size_t)255; }
 Ws8 ws8_layout(int H, int rows, int q_len, int max_context) {
   Ws8 l;
   decode_plan(rows, max_context, q_len, &l.pps, &l.splits);
-  l.q_page = (int)page_bytes_of(H, DC, DR);
   l.qt = 0;
-  l.qt8 = al256((size_t)rows * H * (DC + DR) * 2);
-  l.part_o = l.qt8 + al256((size_t)rows * l.q_page);
+  l.part_o = al256((size_t)rows * H * (DC + DR) * 2);
   l.part_ml = l.part_o + al256((size_t)H * rows * l.splits * DC * 2);
   l.total = l.part_ml + al256((size_t)H * rows * l.splits * 2 * 4);
   return l;
@@ -692,23 +736,15 @@ hipError_t decode_fp8(const mla_dims& d, float scale, int n_seq, int q_len, int 
   if (ws_bytes < l.total || l.splits > MAX_SPLITS) return hipErrorInvalidValue;
   char* base = (char*)ws;
   void* qt = base + l.qt;
-  uint8_t* qt8 = (uint8_t*)(base + l.qt8);
   bf16* part_o = (bf16*)(base + l.part_o);
   float* part_ml = (float*)(base + l.part_ml);
   hipError_t e = decode_absorb(d, scale, rows, q_len, q_nope, q_pe, w_uk, c.context_lens, qt, "mla_decode8_absorb", s);
   if (e != hipSuccess) return e;
   {
-    // q~ rows of one query row form one "page" of H heads
-    ProfScope ps("mla_decode8_quant_q", s);
-    hipLaunchKernelGGL(k_quant_fp8, dim3((rows * H + 3) / 4), dim3(256), 0, s, rows * H, DC, DR, (const bf16*)qt,
-                       (const int32_t*)nullptr, H, l.q_page, qt8);
-  }
-  if ((e = hipGetLastError()) != hipSuccess) return e;
-  {
     ProfScope ps("mla_decode8_split", s);
     const bool pair_xcd = q_len > 1 && ((int64_t)n_seq * l.splits) % 8 == 0;
     hipLaunchKernelGGL(k_split8, dim3(l.splits, rows), dim3(THREADS), 0, s, H, rows, q_len, pair_xcd, l.splits, l.pps,
-                       (const uint8_t*)qt8, l.q_page, (const uint8_t*)c.rows, c.block_table, c.max_blocks,
+                       (const bf16*)qt, (const uint8_t*)c.rows, c.block_table, c.max_blocks,
                        c.context_lens, part_o, part_ml);
   }
   if ((e = hipGetLastError()) != hipSuccess) return e;
