@@ -59,4 +59,82 @@ __device__ __forceinline__ float wave_max(float v) {
   return v;
 }
 
+// Longest runs first. A decode step cuts each query row's context (one new
+// token per row) into runs of `run` tokens, one workgroup each; the last run
+// of a row is usually shorter. Dispatch slot k (blocks start in slot order)
+// takes the k-th run in the order: every full run, row by row, then the rows'
+// last runs from the longest down (ties: lower row first). In plain row order
+// the short last runs sit among the full ones, so with a little more than one
+// round of full runs some full runs start only when another has finished; in
+// this order the short runs fill in behind the full ones. Every wave works it
+// out by itself from the context lengths (O(rows^2 / 64) for the last runs,
+// so the host uses it for at most 256 rows). Returns false when slot k has no
+// run; else the run's row, its index in the row and the row's context length.
+__device__ inline bool longest_run_first(int rows, int run, const int32_t* __restrict__ ctx_lens, int k,
+                                         int& row_out, int& split_out, int& len_out) {
+  const int lane = threadIdx.x & 63;
+  if (rows <= 64) {
+    // every row as long as the first and a whole number of runs: the order
+    // is plain row order (no scan)
+    const int len = lane < rows ? ctx_lens[lane] : 0;
+    const int len0 = __builtin_amdgcn_readfirstlane(len);
+    if (__ballot(lane < rows && len != len0) == 0 && len0 % run == 0) {
+      const int nf = len0 / run;
+      if (k >= rows * nf) return false;
+      row_out = k / nf;
+      split_out = k - row_out * nf;
+      len_out = len0;
+      return true;
+    }
+  }
+  int n_full = 0;
+  for (int base = 0; base < rows; base += 64) {
+    const int row = base + lane;
+    const int len = row < rows ? ctx_lens[row] : 0;
+    const int nf = len / run;
+    int incl = nf;  // inclusive prefix sum over the wave
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const int v = __shfl_up(incl, o, 64);
+      if (lane >= o) incl += v;
+    }
+    const int rel = k - n_full;
+    const uint64_t hit = __ballot(rel >= incl - nf && rel < incl);
+    if (hit != 0) {
+      const int l = __builtin_ctzll(hit);
+      row_out = base + l;
+      split_out = rel - (__builtin_amdgcn_readlane(incl, l) - __builtin_amdgcn_readlane(nf, l));
+      len_out = __builtin_amdgcn_readlane(len, l);
+      return true;
+    }
+    n_full += __builtin_amdgcn_readlane(incl, 63);
+  }
+  // last runs: rank = number of rows whose last run is longer, or as long
+  // and earlier (rows without one have rem = 0 and are never counted)
+  const int kp = k - n_full;
+  for (int base = 0; base < rows; base += 64) {
+    const int row = base + lane;
+    const int len = row < rows ? ctx_lens[row] : 0;
+    const int rem = len % run;
+    int rank = 0;
+    for (int base2 = 0; base2 < rows; base2 += 64) {
+      const int row2 = base2 + lane;
+      const int rem2 = row2 < rows ? ctx_lens[row2] % run : 0;
+      for (int j = 0; j < 64; ++j) {
+        const int r = __builtin_amdgcn_readlane(rem2, j);
+        rank += (r > rem) || (r == rem && base2 + j < row);
+      }
+    }
+    const uint64_t hit = __ballot(rem > 0 && rank == kp);
+    if (hit != 0) {
+      const int l = __builtin_ctzll(hit);
+      row_out = base + l;
+      len_out = __builtin_amdgcn_readlane(len, l);
+      split_out = len_out / run;  // after the row's full runs
+      return true;
+    }
+  }
+  return false;
+}
+
 }  // namespace mla

@@ -352,7 +352,7 @@ __device__ __forceinline__ void mfma_qk_done(f32x16& acc) {
 __device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
 
 template <int NHT>
-__global__ __launch_bounds__(SPLIT_THREADS, 1) void k_split(int H, int B, int q_len, bool pair_xcd, int splits,
+__global__ __launch_bounds__(SPLIT_THREADS, 1) void k_split(int H, int B, int q_len, int order, int splits,
                                                             int pps,
                                                             const bf16* __restrict__ qt,
                                                             const bf16* __restrict__ rows,
@@ -361,8 +361,12 @@ __global__ __launch_bounds__(SPLIT_THREADS, 1) void k_split(int H, int B, int q_
                                                             bf16* __restrict__ part_o, float* __restrict__ part_ml) {
   __shared__ __attribute__((aligned(1024))) char lds[SPLIT_LDS];
   // b is the query row (sequence b / q_len, new token b % q_len)
-  int split = blockIdx.x, b = blockIdx.y;
-  if (pair_xcd) {
+  // block order: 0 plain (split fastest), 1 rows of one sequence paired on
+  // an XCD (below), 2 longest runs first (one new token per row)
+  int split = blockIdx.x, b = blockIdx.y, len_b = 0;
+  if (order == 2) {
+    if (!longest_run_first(B, pps * PAGE, ctx_lens, blockIdx.y * gridDim.x + blockIdx.x, b, split, len_b)) return;
+  } else if (order == 1) {
     // the q_len rows of one (sequence, split) read the same pages: give them
     // consecutive dispatch slots of one XCD (block i runs on XCD i % 8) so
     // that all but the first find the pages in that XCD's L2. Needs the
@@ -374,7 +378,7 @@ __global__ __launch_bounds__(SPLIT_THREADS, 1) void k_split(int H, int B, int q_
     b = seq * q_len + j;
   }
   const int seq = b / q_len;
-  const int L = visible_rows(ctx_lens, b, q_len);
+  const int L = order == 2 ? len_b : visible_rows(ctx_lens, b, q_len);
   const int t_begin = split * pps * PAGE;
   const int t_end = min(t_begin + pps * PAGE, L);
   if (t_begin >= t_end) return;
@@ -988,10 +992,11 @@ hipError_t decode_fast(const mla_dims& d, float scale, int n_seq, int q_len, int
   {
     ProfScope ps("mla_decode_split", s);
     const bool pair_xcd = q_len > 1 && ((int64_t)n_seq * p.splits) % 8 == 0;
+    const int order = pair_xcd ? 1 : (q_len == 1 && batch <= 256 ? 2 : 0);
     // head tiles of 32 with real heads: 1 or 2 for small head counts, else 4
     const int nht = H <= 32 ? 1 : (H <= 64 ? 2 : 4);
     auto go = [&](auto kern) {
-      hipLaunchKernelGGL(kern, grid, dim3(SPLIT_THREADS), 0, s, H, batch, q_len, pair_xcd, p.splits,
+      hipLaunchKernelGGL(kern, grid, dim3(SPLIT_THREADS), 0, s, H, batch, q_len, order, p.splits,
                          p.pages_per_split, qt, (const bf16*)c.rows, c.block_table, c.max_blocks, c.context_lens,
                          part_o, part_ml);
     };

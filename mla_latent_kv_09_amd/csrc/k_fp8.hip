@@ -213,15 +213,19 @@ __device__ __forceinline__ void score_done(f32x16& x) {
 // MFMA kinds chain only after the first one's result is written)
 __device__ __forceinline__ void mfma_switch(f32x16& x) { asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" : "+v"(x)); }
 
-__global__ __launch_bounds__(THREADS, 1) void k_split8(int H, int B, int q_len, bool pair_xcd, int splits, int pps,
+__global__ __launch_bounds__(THREADS, 1) void k_split8(int H, int B, int q_len, int order, int splits, int pps,
                                                        const bf16* __restrict__ qt,
                                                        const uint8_t* __restrict__ pages,
                                                        const int32_t* __restrict__ block_table, int max_blocks,
                                                        const int32_t* __restrict__ ctx_lens,
                                                        bf16* __restrict__ part_o, float* __restrict__ part_ml) {
   __shared__ __attribute__((aligned(1024))) char lds[SPLIT8_LDS];
-  int split = blockIdx.x, b = blockIdx.y;
-  if (pair_xcd) {
+  // block order: 0 plain, 1 rows of one sequence paired on an XCD, 2 longest
+  // runs first (one new token per row), as in the bf16 kernel
+  int split = blockIdx.x, b = blockIdx.y, len_b = 0;
+  if (order == 2) {
+    if (!longest_run_first(B, pps * PAGE, ctx_lens, blockIdx.y * gridDim.x + blockIdx.x, b, split, len_b)) return;
+  } else if (order == 1) {
     // the q_len rows of one (sequence, split) on consecutive slots of one XCD
     const int lin = blockIdx.y * gridDim.x + blockIdx.x, local = lin >> 3;
     const int unit_local = local / q_len, j = local - unit_local * q_len;
@@ -230,7 +234,7 @@ __global__ __launch_bounds__(THREADS, 1) void k_split8(int H, int B, int q_len, 
     b = seq * q_len + j;
   }
   const int seq = b / q_len;
-  const int L = ctx_lens[seq] - (q_len - 1 - (b - seq * q_len));
+  const int L = order == 2 ? len_b : ctx_lens[seq] - (q_len - 1 - (b - seq * q_len));
   const int t_begin = split * pps * PAGE;
   const int t_end = min(t_begin + pps * PAGE, L);
   if (t_begin >= t_end) return;
@@ -743,7 +747,8 @@ hipError_t decode_fp8(const mla_dims& d, float scale, int n_seq, int q_len, int 
   {
     ProfScope ps("mla_decode8_split", s);
     const bool pair_xcd = q_len > 1 && ((int64_t)n_seq * l.splits) % 8 == 0;
-    hipLaunchKernelGGL(k_split8, dim3(l.splits, rows), dim3(THREADS), 0, s, H, rows, q_len, pair_xcd, l.splits, l.pps,
+    const int order = pair_xcd ? 1 : (q_len == 1 && rows <= 256 ? 2 : 0);
+    hipLaunchKernelGGL(k_split8, dim3(l.splits, rows), dim3(THREADS), 0, s, H, rows, q_len, order, l.splits, l.pps,
                        (const bf16*)qt, (const uint8_t*)c.rows, c.block_table, c.max_blocks,
                        c.context_lens, part_o, part_ml);
   }
