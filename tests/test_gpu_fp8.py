@@ -121,6 +121,9 @@ SMALL = [
     ("H128 q2 pairs", 128, 2, [2, 64, 65, 127, 128, 129, 1500, 2047], True),
     ("H32 q3 few units", 32, 3, [3, 129, 700], True),
     ("H8 q64 max", 8, 64, [64, 65, 100, 300, 700, 64, 1000, 129], True),
+    # more than 64 rows of one token each: the split kernel's longest-first
+    # run order over several passes of 64 rows (runs of 640 tokens here)
+    ("H32 q1 130 rows", 32, 1, [int(x) for x in np.random.default_rng(9).integers(1, 1100, 130)] , True),
 ]
 
 

@@ -233,6 +233,46 @@ def test_decode_at_the_longest_context_of_the_fast_path():
     assert_parity(got, ref, "bf16", "L = 2^20 - 5")
 
 
+def _ragged_lens(seed, n, hi, exact=()):
+    lens = np.random.default_rng(seed).integers(1, hi + 1, n)
+    for i, v in enumerate(exact):
+        lens[7 * i + 3] = v
+    return [int(x) for x in lens]
+
+
+# With one new token per row and at most 256 rows, the split kernels take a
+# step's runs longest first: every full run (row by row), then the rows'
+# shorter last runs by decreasing length. The order is worked out from the
+# context lengths in passes of 64 rows; these batches need several passes,
+# mix rows with full runs only (a context that is a whole number of runs),
+# last runs only and both, and take more than one round of the chip. Every
+# row is checked (against the absorbed oracle, pinned equal to the explicit
+# one): a run taken twice or never would show in some row. Runs are of
+# pps * 64 tokens, with pps = clamp(ceil(rows * max_pages / 256), 4, 32).
+RUN_ORDER = [
+    # rows, H, contexts: 130 rows, pps 13 (runs of 832 tokens)
+    ("130 rows H128", 130, 128, _ragged_lens(71, 130, 1600, exact=(832, 1600, 831))),
+    # 200 rows, pps 32 (runs of 2048 tokens)
+    ("200 rows H16", 200, 16, _ragged_lens(72, 200, 4000, exact=(2048, 4000, 1))),
+    # 256 rows, the most in this order; pps 32 (runs of 2048 tokens)
+    ("256 rows H48", 256, 48, _ragged_lens(73, 256, 3000, exact=(2048, 3000, 2047, 2049))),
+    # 300 rows: plain row order (pps 13, one run per row)
+    ("300 rows H16 plain order", 300, 16, _ragged_lens(74, 300, 700, exact=(256, 700))),
+]
+
+
+@pytest.mark.parametrize("name,rows,H,lens", RUN_ORDER, ids=[r[0] for r in RUN_ORDER])
+def test_decode_run_order_covers_every_run_once(name, rows, H, lens):
+    _log(f"decode, run order: {name}")
+    case = make_decode_case(80 + rows, rows, Dims(H, **V3), lens, shuffle=True)
+    assert mla.mla_decode_path(case.dims) == 1
+    got = run_decode(case)
+    c = case.cache
+    ref = oracle.absorbed_decode(case.dims, case.q_nope, case.q_pe, case.w_uk, case.w_uv, c.pool, c.block_table,
+                                 c.context_lens)
+    assert_parity(got, ref, "bf16", name)
+
+
 @pytest.mark.parametrize("H", [1, 48, 100, 129, 256])
 def test_decode_odd_head_counts(H):
     """Every head count the library accepts (1 .. 256) runs on the MFMA path;
