@@ -76,9 +76,9 @@ __device__ inline bool longest_run_first(int rows, int run, const int32_t* __res
   if (rows <= 64) {
     // every row as long as the first and a whole number of runs: the order
     // is plain row order (no scan)
-    const int len = lane < rows ? ctx_lens[lane] : 0;
+    const int len = lane < rows ? max(ctx_lens[lane], 0) : 0;
     const int len0 = __builtin_amdgcn_readfirstlane(len);
-    if (__ballot(lane < rows && len != len0) == 0 && len0 % run == 0) {
+    if (__ballot(lane < rows && len != len0) == 0 && len0 > 0 && len0 % run == 0) {
       const int nf = len0 / run;
       if (k >= rows * nf) return false;
       row_out = k / nf;
@@ -90,7 +90,7 @@ __device__ inline bool longest_run_first(int rows, int run, const int32_t* __res
   int n_full = 0;
   for (int base = 0; base < rows; base += 64) {
     const int row = base + lane;
-    const int len = row < rows ? ctx_lens[row] : 0;
+    const int len = row < rows ? max(ctx_lens[row], 0) : 0;
     const int nf = len / run;
     int incl = nf;  // inclusive prefix sum over the wave
 #pragma unroll
@@ -114,12 +114,12 @@ __device__ inline bool longest_run_first(int rows, int run, const int32_t* __res
   const int kp = k - n_full;
   for (int base = 0; base < rows; base += 64) {
     const int row = base + lane;
-    const int len = row < rows ? ctx_lens[row] : 0;
+    const int len = row < rows ? max(ctx_lens[row], 0) : 0;
     const int rem = len % run;
     int rank = 0;
     for (int base2 = 0; base2 < rows; base2 += 64) {
       const int row2 = base2 + lane;
-      const int rem2 = row2 < rows ? ctx_lens[row2] % run : 0;
+      const int rem2 = row2 < rows ? max(ctx_lens[row2], 0) % run : 0;
       for (int j = 0; j < 64; ++j) {
         const int r = __builtin_amdgcn_readlane(rem2, j);
         rank += (r > rem) || (r == rem && base2 + j < row);
