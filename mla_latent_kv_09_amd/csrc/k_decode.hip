@@ -1,11 +1,13 @@
 // MFMA decode path for the DeepSeek-V3 latent shape (bf16, d_c 512,
-// d_rope 64, d_nope = d_v = 128, 64-token pages, up to 128 heads).
+// d_rope 64, d_nope = d_v = 128, 64-token pages, up to 256 heads: groups of
+// 128 heads run side by side).
 //
 // Three kernels, one stream:
 //   k_absorb       Qt[b,h] = s*log2(e) * [W_UK,h^T q_nope[b,h] || RoPE(q_pe[b,h], L_b - 1)]
 //                  ("DeepSeek-V2 paper digest" §2.2: W_UK folded into the query;
 //                  §2.3: only the decoupled slice is rotated).
-//   k_split        one workgroup per (sequence, run of pages): every page of
+//   k_split        one workgroup per (query row, run of pages, head group),
+//                  runs dispatched longest first (common.h): every page of
 //                  64 cache rows (64 x 576 bf16 = 72 KB, contiguous in HBM) is
 //                  streamed into LDS once and shared by all heads. Scores
 //                  S^T[t,h] = row_t . Qt[h] are one 64 x H x 576 MFMA product per
