@@ -32,10 +32,7 @@ constexpr int DC = 512, DR = 64, ROW = DC + DR, DN = 128, DV = 128;
 constexpr int PAGE = 64;
 constexpr int ROW_BYTES = ROW * 2;               // 1152
 constexpr int ROW_CHUNKS = ROW_BYTES / 16;       // 72 chunks of 16 B
-constexpr int PAGE_BYTES = PAGE * ROW_BYTES;     // 73728
-constexpr int PAGE_CHUNKS = PAGE * ROW_CHUNKS;   // 4608
 constexpr int SPLIT_THREADS = 256;               // 4 waves
-constexpr int LOADS_PER_THREAD = PAGE_CHUNKS / SPLIT_THREADS;  // 18
 constexpr float LOG2E = 1.4426950408889634f;
 constexpr int MAX_SPLITS = 256;
 constexpr int MAX_HEADS = 128;
