@@ -787,61 +787,69 @@ __global__ __launch_bounds__(SPLIT_THREADS, 1) void k_split(int H, int B, int q_
 }
 
 // -------------------------------------------------------- k_combine_uv ----
-// One block per (head, tile of 16 query rows). Blocks of the same head share
-// blockIdx % 8, i.e. the same XCD and L2, so W_UV,h is fetched from HBM once.
-// Thread (r, q) = (tid / 16, tid % 16) owns row b0 + r and the latent columns
-// 8q + 128u .. +7 (u < 4). It reads (m, l) and its columns of the row's
-// partials itself, 4 splits at a time, and merges them online:
+// One block per (head, tile of TR query rows), TR = 16, or 4 where 16 would
+// leave most of the chip idle. Blocks of the same head share blockIdx % 8,
+// i.e. the same XCD and L2, so W_UV,h is fetched from HBM once. Thread
+// (r, q) = (tid / TPR, tid % TPR), TPR = 256 / TR, owns row b0 + r and the
+// latent columns 8q + 8 TPR u .. +7. It reads (m, l) and its columns of the
+// row's partials itself, SG splits at a time (4 with TR = 16, 8 with TR = 4),
+// and merges them online:
 //   M = max_s m_s, o_c = sum_s 2^(m_s - M) O_s / sum_s 2^(m_s - M) l_s
-// (one group of at most 4 splits in the common case, so no rescale at all).
-// The first group's partials and (m, l) are requested before anything else;
-// this wave's W_UV,h fragments (128 registers) only once the merge is done,
-// which keeps the kernel at two waves per SIMD (holding both would take one
-// block round more). Then out^T[v, b] = sum_c W_UV[h*128 + v, c] o_c[b, c]
-// on MFMA from o_c staged in LDS as bf16; each lane ends with 4 consecutive
-// outputs of one row (one 8-byte store).
+// When no row has more than SG splits (MULTI false, the common case) that is
+// one group, loaded before anything else and merged with no rescale. With
+// more, each following group is requested while the one before it is merged.
+// This wave's W_UV,h fragments (128 registers) are loaded only once the merge
+// is done, which keeps the kernel at two waves per SIMD (holding both would
+// take one block round more). Then out^T[v, b] = sum_c W_UV[h*128 + v, c]
+// o_c[b, c] on MFMA from o_c staged in LDS as bf16; each lane ends with 4
+// consecutive outputs of one row (one 8-byte store).
 // With UV false, the W_UV product is left out and o_c itself is written, as
 // out [B, H, 512] bf16, for an output projection with W_UV folded into W_O.
-template <bool UV>
+template <bool UV, int TR, bool MULTI>
 __global__ __launch_bounds__(256) void k_combine_uv(int H, int B, int q_len, int splits, int pps,
                                                     const int32_t* __restrict__ ctx_lens,
                                                     const bf16* __restrict__ part_o,
                                                     const float* __restrict__ part_ml,
                                                     const bf16* __restrict__ w_uv, bf16* __restrict__ out) {
+  // TR query rows per block (16, or 4 when the grid would be small), TPR
+  // threads per row, each with CPT latent columns in NU loads of 8 per split
+  constexpr int TPR = 256 / TR, CPT = DC / TPR, NU = CPT / 8;
   constexpr int LDO = DC + 8;
-  constexpr int SG = 4;  // splits per load group
+  constexpr int SG = TR == 16 ? 4 : 8;  // splits per load group
   __shared__ __attribute__((aligned(16))) bf16 oc[16 * LDO];
-  const int nbt = (B + 15) / 16;
+  const int nbt = (B + TR - 1) / TR;
   const int bid = blockIdx.x, xcd = bid & 7, k = bid >> 3;
   const int bt = k % nbt, h = (k / nbt) * 8 + xcd;
   if (h >= H) return;
-  const int b0 = bt * 16;
+  const int b0 = bt * TR;
   const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
   const int i16 = lane & 15, G = lane >> 4;
-  const int r = tid >> 4, q = tid & 15, b = b0 + r;
+  const int r = tid / TPR, q = tid % TPR, b = b0 + r;
   const int len = b < B ? visible_rows(ctx_lens, b, q_len) : 0;
   // splits that hold rows of this query row; the others were never written
   const int ns = len > 0 ? ((len + PAGE - 1) / PAGE + pps - 1) / pps : 0;
   const bf16* po = part_o + ((size_t)h * B + (b < B ? b : 0)) * splits * DC + 8 * q;
   const float* ml = part_ml + ((size_t)h * B + (b < B ? b : 0)) * splits * 2;
   typedef __attribute__((ext_vector_type(2))) float f32x2_t;
-  u32x4 pv[SG][4];
-  f32x2_t mlv[SG];
-  auto issue = [&](int s0) {
+  // two groups of partials in registers: the next group's loads are in
+  // flight while the current one is merged (with up to 16 splits, four
+  // groups in turn would otherwise each wait a whole memory round trip)
+  u32x4 pv0[SG][NU], pv1[SG][NU];
+  f32x2_t ml0[SG], ml1[SG];
+  auto issue = [&](int s0, u32x4 (&pv)[SG][NU], f32x2_t (&mlv)[SG]) __attribute__((always_inline)) {
 #pragma unroll
     for (int d = 0; d < SG; ++d) {
       const int sp = s0 + d;
       if (sp < ns) {
         mlv[d] = *(const f32x2_t*)(ml + 2 * sp);
 #pragma unroll
-        for (int u = 0; u < 4; ++u) pv[d][u] = *(const u32x4*)(po + (size_t)sp * DC + 128 * u);
+        for (int u = 0; u < NU; ++u) pv[d][u] = *(const u32x4*)(po + (size_t)sp * DC + 8 * TPR * u);
       }
     }
   };
-  issue(0);
-  float acc[4][8] = {};
+  float acc[NU][8] = {};
   float M = -INFINITY, l = 0.f;
-  for (int s0 = 0; s0 < ns; s0 += SG) {
+  auto merge = [&](int s0, const u32x4 (&pv)[SG][NU], const f32x2_t (&mlv)[SG]) __attribute__((always_inline)) {
     float Mg = M;
 #pragma unroll
     for (int d = 0; d < SG; ++d)
@@ -850,7 +858,7 @@ __global__ __launch_bounds__(256) void k_combine_uv(int H, int B, int q_len, int
       const float a = __builtin_amdgcn_exp2f(M - Mg);
       l *= a;
 #pragma unroll
-      for (int u = 0; u < 4; ++u)
+      for (int u = 0; u < NU; ++u)
 #pragma unroll
         for (int x = 0; x < 8; ++x) acc[u][x] *= a;
       M = Mg;
@@ -861,7 +869,7 @@ __global__ __launch_bounds__(256) void k_combine_uv(int H, int B, int q_len, int
         const float e = __builtin_amdgcn_exp2f(mlv[d][0] - M);
         l += e * mlv[d][1];
 #pragma unroll
-        for (int u = 0; u < 4; ++u)
+        for (int u = 0; u < NU; ++u)
 #pragma unroll
           for (int x = 0; x < 4; ++x) {
             acc[u][2 * x] += e * __uint_as_float(pv[d][u][x] << 16);
@@ -869,7 +877,18 @@ __global__ __launch_bounds__(256) void k_combine_uv(int H, int B, int q_len, int
           }
       }
     }
-    if (s0 + SG < ns) issue(s0 + SG);
+  };
+  issue(0, pv0, ml0);
+  if constexpr (!MULTI) {
+    merge(0, pv0, ml0);  // every row has at most SG splits
+  } else {
+    for (int s0 = 0; s0 < ns; s0 += 2 * SG) {
+      if (s0 + SG < ns) issue(s0 + SG, pv1, ml1);
+      merge(s0, pv0, ml0);
+      if (s0 + SG >= ns) break;
+      if (s0 + 2 * SG < ns) issue(s0 + 2 * SG, pv0, ml0);
+      merge(s0 + SG, pv1, ml1);
+    }
   }
   // W_UV,h fragments of this wave (rows 32w .. 32w+31, all 512 columns);
   // their loads fly while o_c is staged
@@ -884,23 +903,25 @@ __global__ __launch_bounds__(256) void k_combine_uv(int H, int B, int q_len, int
   }
   const float il = ns > 0 ? 1.f / l : 0.f;
 #pragma unroll
-  for (int u = 0; u < 4; ++u) {
+  for (int u = 0; u < NU; ++u) {
     bf16x8_t v;
 #pragma unroll
     for (int x = 0; x < 8; ++x) v[x] = (__bf16)(acc[u][x] * il);
-    *(bf16x8_t*)&oc[r * LDO + 8 * q + 128 * u] = v;
+    *(bf16x8_t*)&oc[r * LDO + 8 * q + 8 * TPR * u] = v;
   }
   __syncthreads();
   if constexpr (!UV) {
-    // o_c rows of the 16 query rows: 16 threads per row, 64 bytes each
+    // o_c rows of the block's query rows: TPR threads per row, CPT columns each
     if (b < B) {
-      bf16* dst = out + ((size_t)b * H + h) * DC + 32 * q;
+      bf16* dst = out + ((size_t)b * H + h) * DC + CPT * q;
 #pragma unroll
-      for (int u = 0; u < 4; ++u) *(u32x4*)(dst + 8 * u) = *(const u32x4*)&oc[r * LDO + 32 * q + 8 * u];
+      for (int u = 0; u < NU; ++u) *(u32x4*)(dst + 8 * u) = *(const u32x4*)&oc[r * LDO + CPT * q + 8 * u];
     }
     return;
   }
-  // wave w: outputs v = 32w .. 32w+31 (two 16-row tiles), all 16 query rows
+  // wave w: outputs v = 32w .. 32w+31 (two 16-row tiles), the block's query
+  // rows as the 16 MFMA columns (with TR = 4, columns 4-15 are left over and
+  // not stored)
   f32x4 oacc[2] = {};
 #pragma unroll
   for (int ks = 0; ks < DC / 32; ++ks) {
@@ -910,7 +931,7 @@ __global__ __launch_bounds__(256) void k_combine_uv(int H, int B, int q_len, int
       oacc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(wf[ks][mt]), bo, oacc[mt], 0, 0, 0);
   }
   const int bo_seq = b0 + i16;
-  if (bo_seq < B) {
+  if (i16 < TR && bo_seq < B) {
 #pragma unroll
     for (int mt = 0; mt < 2; ++mt) {
       typedef __attribute__((ext_vector_type(4))) __bf16 bf16x4_t;
@@ -949,15 +970,25 @@ hipError_t decode_combine(const mla_dims& d, int rows, int q_len, int splits, in
                           const void* part_o, const float* part_ml, const void* w_uv, void* out,
                           const char* prof_name, hipStream_t s) {
   const int H = d.n_heads;
-  const int nbt = (rows + 15) / 16;
   const int hpad = (H + 7) / 8 * 8;
+  // 16 query rows per block, or 4 where that would leave most of the chip idle
+  // (few heads and rows: the blocks then each stream fewer partials)
+  const bool small = hpad * ((rows + 15) / 16) < 128;
+  const int nbt = small ? (rows + 3) / 4 : (rows + 15) / 16;
   ProfScope ps(prof_name, s);
-  if (w_uv)
-    hipLaunchKernelGGL(k_combine_uv<true>, dim3(hpad * nbt), dim3(256), 0, s, H, rows, q_len, splits, pps, ctx_lens,
+  auto go = [&](auto kern) {
+    hipLaunchKernelGGL(kern, dim3(hpad * nbt), dim3(256), 0, s, H, rows, q_len, splits, pps, ctx_lens,
                        (const bf16*)part_o, part_ml, (const bf16*)w_uv, (bf16*)out);
-  else
-    hipLaunchKernelGGL(k_combine_uv<false>, dim3(hpad * nbt), dim3(256), 0, s, H, rows, q_len, splits, pps,
-                       ctx_lens, (const bf16*)part_o, part_ml, nullptr, (bf16*)out);
+  };
+  // one group of splits per row (the common case) or several
+  const bool multi = splits > (small ? 8 : 4);
+  if (w_uv) {
+    if (small) multi ? go(k_combine_uv<true, 4, true>) : go(k_combine_uv<true, 4, false>);
+    else multi ? go(k_combine_uv<true, 16, true>) : go(k_combine_uv<true, 16, false>);
+  } else {
+    if (small) multi ? go(k_combine_uv<false, 4, true>) : go(k_combine_uv<false, 4, false>);
+    else multi ? go(k_combine_uv<false, 16, true>) : go(k_combine_uv<false, 16, false>);
+  }
   return hipGetLastError();
 }
 
