@@ -825,9 +825,16 @@ __global__ __launch_bounds__(256) void k_combine_uv(int H, int B, int q_len, int
   const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
   const int i16 = lane & 15, G = lane >> 4;
   const int r = tid / TPR, q = tid % TPR, b = b0 + r;
-  const int len = b < B ? visible_rows(ctx_lens, b, q_len) : 0;
+  // the row's sequence length is requested first and used only after the
+  // partials' loads are out (visible_rows with its arithmetic deferred)
+  const int seq = b / q_len;
+  const int seq_len = b < B ? ctx_lens[seq] : 0;
   // splits that hold rows of this query row; the others were never written
-  const int ns = len > 0 ? ((len + PAGE - 1) / PAGE + pps - 1) / pps : 0;
+  auto row_splits = [&]() __attribute__((always_inline)) {
+    const int len = b < B ? seq_len - (q_len - 1 - (b - seq * q_len)) : 0;
+    return len > 0 ? ((len + PAGE - 1) / PAGE + pps - 1) / pps : 0;
+  };
+  int ns = MULTI ? row_splits() : 0;
   const bf16* po = part_o + ((size_t)h * B + (b < B ? b : 0)) * splits * DC + 8 * q;
   const float* ml = part_ml + ((size_t)h * B + (b < B ? b : 0)) * splits * 2;
   typedef __attribute__((ext_vector_type(2))) float f32x2_t;
@@ -836,11 +843,16 @@ __global__ __launch_bounds__(256) void k_combine_uv(int H, int B, int q_len, int
   // groups in turn would otherwise each wait a whole memory round trip)
   u32x4 pv0[SG][NU], pv1[SG][NU];
   f32x2_t ml0[SG], ml1[SG];
+  // With one group every slot is loaded, without waiting for the context
+  // length: slots past the launch's splits repeat its last split, and a split
+  // past the row's context holds stale or unwritten values; both are loaded
+  // but never merged.
   auto issue = [&](int s0, u32x4 (&pv)[SG][NU], f32x2_t (&mlv)[SG]) __attribute__((always_inline)) {
 #pragma unroll
     for (int d = 0; d < SG; ++d) {
-      const int sp = s0 + d;
-      if (sp < ns) {
+      int sp = s0 + d;
+      if (!MULTI) sp = sp < splits ? sp : splits - 1;
+      if (!MULTI || sp < ns) {
         mlv[d] = *(const f32x2_t*)(ml + 2 * sp);
 #pragma unroll
         for (int u = 0; u < NU; ++u) pv[d][u] = *(const u32x4*)(po + (size_t)sp * DC + 8 * TPR * u);
@@ -879,6 +891,23 @@ __global__ __launch_bounds__(256) void k_combine_uv(int H, int B, int q_len, int
     }
   };
   issue(0, pv0, ml0);
+  // W_UV,h fragments of this wave (rows 32w .. 32w+31, all 512 columns)
+  u32x4 wf[DC / 32][2];
+  auto load_wuv = [&]() __attribute__((always_inline)) {
+    const bf16* wv = w_uv + (size_t)h * DV * DC;
+#pragma unroll
+    for (int ks = 0; ks < DC / 32; ++ks)
+#pragma unroll
+      for (int mt = 0; mt < 2; ++mt)
+        wf[ks][mt] = *(const u32x4*)(wv + (size_t)(32 * w + 16 * mt + i16) * DC + 32 * ks + 8 * G);
+  };
+  // with one group they go out right behind the partials, and the context
+  // length is needed only for the merge
+  if constexpr (UV && !MULTI) load_wuv();
+  if constexpr (!MULTI) {
+    __builtin_amdgcn_sched_barrier(0);
+    ns = row_splits();
+  }
   if constexpr (!MULTI) {
     merge(0, pv0, ml0);  // every row has at most SG splits
   } else {
@@ -890,17 +919,9 @@ __global__ __launch_bounds__(256) void k_combine_uv(int H, int B, int q_len, int
       merge(s0 + SG, pv1, ml1);
     }
   }
-  // W_UV,h fragments of this wave (rows 32w .. 32w+31, all 512 columns);
-  // their loads fly while o_c is staged
-  u32x4 wf[DC / 32][2];
-  if constexpr (UV) {
-    const bf16* wv = w_uv + (size_t)h * DV * DC;
-#pragma unroll
-    for (int ks = 0; ks < DC / 32; ++ks)
-#pragma unroll
-      for (int mt = 0; mt < 2; ++mt)
-        wf[ks][mt] = *(const u32x4*)(wv + (size_t)(32 * w + 16 * mt + i16) * DC + 32 * ks + 8 * G);
-  }
+  // with several groups, once they are merged (their loads fly while o_c is
+  // staged)
+  if constexpr (UV && MULTI) load_wuv();
   const float il = ns > 0 ? 1.f / l : 0.f;
 #pragma unroll
   for (int u = 0; u < NU; ++u) {

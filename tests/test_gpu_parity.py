@@ -334,6 +334,30 @@ def test_decode_ignores_non_finite_rows_past_the_context():
     assert_parity(got, oracle_decode(case), "bf16", "poisoned tails")
 
 
+# rows with fewer page runs than the launch has splits, with one or several
+# groups of splits in the combine, at 4 and 16 query rows per combine block
+NAN_WS = [
+    ("H16 ragged tails", 16, [1, 63, 64, 65, 700]),
+    ("H128 ragged tails", 128, [1, 129, 1000]),
+    ("H32 long", 32, [5000, 3]),
+    ("H128 eight rows", 128, [1, 64, 65, 700, 2000, 4097, 130, 3000]),
+]
+
+
+@pytest.mark.parametrize("name,H,lens", NAN_WS, ids=[c[0] for c in NAN_WS])
+def test_decode_with_a_nan_filled_workspace(name, H, lens):
+    """The split partials of runs past a row's context are never written, so
+    they hold whatever the workspace held before; filled with NaN bytes here,
+    they must not reach the output."""
+    _log(f"decode over a NaN-filled workspace: {name}")
+    case = make_decode_case(46, len(lens), Dims(H, **V3), lens, shuffle=True)
+    n = mla.mla_decode_workspace_size(mla.Dims.of(case.dims), len(lens), max(lens))
+    ws = torch.full((n,), 0xFF, dtype=torch.uint8, device="cuda")
+    got = run_decode(case, workspace=ws)
+    assert np.all(np.isfinite(got))
+    assert_parity(got, oracle_decode(case), "bf16", name)
+
+
 def test_chunked_prefill_ignores_non_finite_rows_past_the_context():
     _log("chunked prefill with NaN/Inf rows past the context")
     dims = Dims(16, **V3)
