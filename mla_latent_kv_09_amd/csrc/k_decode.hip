@@ -154,33 +154,36 @@ struct RopeFreq {
   double theta[DR / 2];
 };
 
-// grid (H, DC / 128); 4 waves; one block round on the chip for H = 128. Block
-// (h, c0) forms Qt[:, h, c0 .. c0+127] for every query row as the transposed
-// product Qt^T[c, b] = sum_j W_UK[h*128+j, c] q_nope[b, h, j]. The 128 x 128
-// slice of W_UK,h (32 KB) and the first 64 query rows are requested before
-// anything else, so each block has all of its HBM reads in flight at once.
+// grid (H, DC / CW); 4 waves; one block round on the chip for H = 128. Block
+// (h, c0) forms Qt[:, h, c0 .. c0+CW-1] for every query row as the transposed
+// product Qt^T[c, b] = sum_j W_UK[h*128+j, c] q_nope[b, h, j]. CW is 128
+// columns, or 64 or 32 with fewer than 64 heads, so that the grid still has
+// about one block per compute unit. The 128 x CW slice of W_UK,h and the first
+// 64 query rows are requested before anything else, so each block has all of
+// its HBM reads in flight at once.
 // The slice is staged in LDS and read transposed (the A operand); wave w takes
 // query rows 16w .. 16w+15 of each 64-row chunk (the B operand, straight from
-// memory: 8 consecutive j of one row per lane) against all 8 column tiles, so
-// every query element is loaded once per block. Results go through LDS so
-// that each row segment (128 columns, 256 bytes) is written whole. The blocks
+// memory: 8 consecutive j of one row per lane) against all CW / 16 column
+// tiles, so every query element is loaded once per block. Results go through
+// LDS so that each row segment (CW columns) is written whole. The blocks
 // of head h also write its rotated, scaled q_pe slice, each for every 4th row.
+template <int CW>
 __global__ __launch_bounds__(256) void k_absorb(int B, int H, int q_len, const bf16* __restrict__ q_nope,
                                                 const bf16* __restrict__ q_pe, const bf16* __restrict__ w_uk,
                                                 const int32_t* __restrict__ ctx_lens, float qscale, RopeFreq rope,
                                                 bf16* __restrict__ qt) {
-  constexpr int CW = 128;       // columns of one block
-  constexpr int LD = CW + 8;    // padded row (272 B): two-way LDS conflicts at most on the transposed reads
+  constexpr int LD = CW + 8;    // padded row (272 B at CW = 128): two-way LDS conflicts at most on the transposed reads
   constexpr int NCB = DC / CW;  // column blocks per head
+  constexpr int CPR = CW / 8;   // 16-byte chunks per slice row
   __shared__ __attribute__((aligned(16))) bf16 wt[DN * LD];
   __shared__ __attribute__((aligned(16))) bf16 ot[64 * LD];
   const int h = blockIdx.x, c0 = blockIdx.y * CW;
   const int w = threadIdx.x >> 6, lane = threadIdx.x & 63, i16 = lane & 15, G = lane >> 4;
-  // W_UK slice: 128 rows of 256 bytes, 16 lanes per row, 8 loads per lane
+  // W_UK slice: 128 rows of 2 CW bytes, CPR lanes per row
   u32x4 wr[DN * CW / 8 / 256];
 #pragma unroll
   for (int u = 0; u < DN * CW / 8 / 256; ++u) {
-    const int i = threadIdx.x + 256 * u, j = i >> 4, ch = i & 15;
+    const int i = threadIdx.x + 256 * u, j = i / CPR, ch = i % CPR;
     wr[u] = *(const u32x4*)(w_uk + (size_t)(h * DN + j) * DC + c0 + ch * 8);
   }
   auto load_q = [&](int b0, u32x4 (&qv)[DN / 32]) {
@@ -204,7 +207,7 @@ __global__ __launch_bounds__(256) void k_absorb(int B, int H, int q_len, const b
   }
 #pragma unroll
   for (int u = 0; u < DN * CW / 8 / 256; ++u) {
-    const int i = threadIdx.x + 256 * u, j = i >> 4, ch = i & 15;
+    const int i = threadIdx.x + 256 * u, j = i / CPR, ch = i % CPR;
     *(u32x4*)&wt[j * LD + ch * 8] = wr[u];
   }
   __syncthreads();
@@ -214,17 +217,33 @@ __global__ __launch_bounds__(256) void k_absorb(int B, int H, int q_len, const b
 #pragma unroll
     for (int ks = 0; ks < DN / 32; ++ks) cur[ks] = qv[ks];
     if (b0 + 64 < B) load_q(b0 + 64, qv);
+    // one K step at a time over the CW / 16 column tiles (independent
+    // accumulators); the next step's transposing reads go out before this
+    // step's MFMAs
     f32x4 acc[CW / 16];
 #pragma unroll
-    for (int ct = 0; ct < CW / 16; ++ct) {
-      acc[ct] = (f32x4){0.f, 0.f, 0.f, 0.f};
+    for (int ct = 0; ct < CW / 16; ++ct) acc[ct] = (f32x4){0.f, 0.f, 0.f, 0.f};
+    bf16x8_t af[2][CW / 16];
+    auto read_step = [&](int ks, bf16x8_t (&a)[CW / 16]) __attribute__((always_inline)) {
 #pragma unroll
-      for (int ks = 0; ks < DN / 32; ++ks) {
+      for (int ct = 0; ct < CW / 16; ++ct) {
         const int k0 = 32 * ks + 8 * G, col = 16 * ct + 4 * (i16 & 3);
-        const bf16x8_t af = cat_tr(tr_read(wbase + ((k0 + (i16 >> 2)) * LD + col) * 2),
-                                   tr_read(wbase + ((k0 + 4 + (i16 >> 2)) * LD + col) * 2));
-        acc[ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af, as_bf16x8(cur[ks]), acc[ct], 0, 0, 0);
+        a[ct] = cat_tr(tr_read(wbase + ((k0 + (i16 >> 2)) * LD + col) * 2),
+                       tr_read(wbase + ((k0 + 4 + (i16 >> 2)) * LD + col) * 2));
       }
+    };
+    read_step(0, af[0]);
+    __builtin_amdgcn_sched_group_barrier(0x100, CW / 8, 0);
+#pragma unroll
+    for (int ks = 0; ks < DN / 32; ++ks) {
+      if (ks + 1 < DN / 32) {
+        read_step(ks + 1, af[(ks + 1) & 1]);
+        __builtin_amdgcn_sched_group_barrier(0x100, CW / 8, 0);
+      }
+#pragma unroll
+      for (int ct = 0; ct < CW / 16; ++ct)
+        acc[ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[ks & 1][ct], as_bf16x8(cur[ks]), acc[ct], 0, 0, 0);
+      __builtin_amdgcn_sched_group_barrier(0x008, CW / 16, 0);
     }
     // lane: columns 16 ct + 4 G .. +3 of row 16 w + i16; each wave stages and
     // stores only its own 16 rows
@@ -236,8 +255,8 @@ __global__ __launch_bounds__(256) void k_absorb(int B, int H, int q_len, const b
                      (__bf16)(acc[ct][3] * qscale)};
     __syncthreads();
 #pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      const int r = 16 * w + 4 * k + (lane >> 4), ch = lane & 15, b = b0 + r;
+    for (int k = 0; k < CPR / 4; ++k) {
+      const int r = 16 * w + (64 / CPR) * k + lane / CPR, ch = lane % CPR, b = b0 + r;
       if (b < B) *(u32x4*)(qt + ((size_t)b * H + h) * ROW + c0 + 8 * ch) = *(const u32x4*)&ot[r * LD + 8 * ch];
     }
     __syncthreads();  // this chunk's rows are out of ot before the next one lands
@@ -981,9 +1000,16 @@ hipError_t decode_absorb(const mla_dims& d, float scale, int rows, int q_len, co
   ProfScope ps(prof_name, s);
   RopeFreq rope;
   for (int i = 0; i < DR / 2; ++i) rope.theta[i] = pow((double)d.rope_base, -2.0 * i / (double)DR);
-  hipLaunchKernelGGL(k_absorb, dim3(d.n_heads, DC / 128), dim3(256), 0, s, rows, d.n_heads, q_len,
-                     (const bf16*)q_nope, (const bf16*)q_pe, (const bf16*)w_uk, ctx_lens, scale * LOG2E, rope,
-                     (bf16*)qt);
+  // narrower column blocks with fewer heads, so the grid stays near one block
+  // per compute unit
+  const int H = d.n_heads;
+  auto go = [&](auto kern, int cw) {
+    hipLaunchKernelGGL(kern, dim3(H, DC / cw), dim3(256), 0, s, rows, H, q_len, (const bf16*)q_nope,
+                       (const bf16*)q_pe, (const bf16*)w_uk, ctx_lens, scale * LOG2E, rope, (bf16*)qt);
+  };
+  if (H >= 64) go(k_absorb<128>, 128);
+  else if (H >= 32) go(k_absorb<64>, 64);
+  else go(k_absorb<32>, 32);
   return hipGetLastError();
 }
 
