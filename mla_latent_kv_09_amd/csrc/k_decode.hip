@@ -126,7 +126,7 @@ Plan plan_splits(int batch, int max_context, int q_len) {
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 struct WsLayout {
-  size_t qt, part_o, part_ml, total;
+  size_t qt, part_o, part_ml, run, total;
 };
 
 WsLayout ws_layout(int H, int batch, int splits) {
@@ -134,7 +134,8 @@ WsLayout ws_layout(int H, int batch, int splits) {
   l.qt = 0;
   l.part_o = align256((size_t)batch * H * ROW * 2);
   l.part_ml = l.part_o + align256((size_t)H * batch * splits * DC * 2);
-  l.total = l.part_ml + align256((size_t)H * batch * splits * 2 * 4);
+  l.run = l.part_ml + align256((size_t)H * batch * splits * 2 * 4);
+  l.total = l.run + 256;  // the run length the split kernel used, for the combine
   return l;
 }
 
@@ -371,7 +372,7 @@ __device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(
 
 template <int NHT>
 __global__ __launch_bounds__(SPLIT_THREADS, 1) void k_split(int H, int B, int q_len, int order, int splits,
-                                                            int pps,
+                                                            int pps, int budget, int32_t* __restrict__ run_out,
                                                             const bf16* __restrict__ qt,
                                                             const bf16* __restrict__ rows,
                                                             const int32_t* __restrict__ block_table,
@@ -381,9 +382,19 @@ __global__ __launch_bounds__(SPLIT_THREADS, 1) void k_split(int H, int B, int q_
   // b is the query row (sequence b / q_len, new token b % q_len)
   // block order: 0 plain (split fastest), 1 rows of one sequence paired on
   // an XCD (below), 2 longest runs first (one new token per row)
+  // With the longest-first order the run length may grow from pps so that
+  // the step's runs fit in one round of `budget` workgroups; the first block
+  // records the length used for the combine.
   int split = blockIdx.x, b = blockIdx.y, len_b = 0;
+  int lens[4] = {0, 0, 0, 0};
+  if (order == 2) load_row_lens(B, ctx_lens, lens);
+  // (only when the launch's slots, splits x B, exceed one round: otherwise
+  // the runs of pps fit whatever the lengths)
+  const int pps_run = order == 2 && splits * B > budget ? one_round_run_pages(pps, 64, budget, PAGE, lens) : pps;
+  if ((blockIdx.x | blockIdx.y | blockIdx.z) == 0 && threadIdx.x == 0) *run_out = pps_run;
   if (order == 2) {
-    if (!longest_run_first(B, pps * PAGE, ctx_lens, blockIdx.y * gridDim.x + blockIdx.x, b, split, len_b)) return;
+    if (!longest_run_first(B, pps_run * PAGE, lens, blockIdx.y * gridDim.x + blockIdx.x, b, split, len_b))
+      return;
   } else if (order == 1) {
     // the q_len rows of one (sequence, split) read the same pages: give them
     // consecutive dispatch slots of one XCD (block i runs on XCD i % 8) so
@@ -397,8 +408,8 @@ __global__ __launch_bounds__(SPLIT_THREADS, 1) void k_split(int H, int B, int q_
   }
   const int seq = b / q_len;
   const int L = order == 2 ? len_b : visible_rows(ctx_lens, b, q_len);
-  const int t_begin = split * pps * PAGE;
-  const int t_end = min(t_begin + pps * PAGE, L);
+  const int t_begin = split * pps_run * PAGE;
+  const int t_end = min(t_begin + pps_run * PAGE, L);
   if (t_begin >= t_end) return;
   const int n_tiles = (t_end - t_begin + TILE - 1) / TILE;
   // the wave index is uniform: keep it (and the LDS bases derived from it) in SGPRs
@@ -825,7 +836,8 @@ __global__ __launch_bounds__(SPLIT_THREADS, 1) void k_split(int H, int B, int q_
 // With UV false, the W_UV product is left out and o_c itself is written, as
 // out [B, H, 512] bf16, for an output projection with W_UV folded into W_O.
 template <bool UV, int TR, bool MULTI>
-__global__ __launch_bounds__(256) void k_combine_uv(int H, int B, int q_len, int splits, int pps,
+__global__ __launch_bounds__(256) void k_combine_uv(int H, int B, int q_len, int splits,
+                                                    const int32_t* __restrict__ run_pages,
                                                     const int32_t* __restrict__ ctx_lens,
                                                     const bf16* __restrict__ part_o,
                                                     const float* __restrict__ part_ml,
@@ -848,6 +860,7 @@ __global__ __launch_bounds__(256) void k_combine_uv(int H, int B, int q_len, int
   // partials' loads are out (visible_rows with its arithmetic deferred)
   const int seq = b / q_len;
   const int seq_len = b < B ? ctx_lens[seq] : 0;
+  const int pps = *run_pages;  // pages per run, as the split kernel used them
   // splits that hold rows of this query row; the others were never written
   auto row_splits = [&]() __attribute__((always_inline)) {
     const int len = b < B ? seq_len - (q_len - 1 - (b - seq * q_len)) : 0;
@@ -983,6 +996,14 @@ __global__ __launch_bounds__(256) void k_combine_uv(int H, int B, int q_len, int
 
 }  // namespace
 
+int device_cus() {
+  int dev = 0, n = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+    return 256;
+  return n;
+}
+
 bool decode_fast_supported(const mla_dims& d, const CacheView& c) {
   return d.dtype == MLA_BF16 && d.d_c == DC && d.d_rope == DR && d.d_nope == DN && d.d_v == DV &&
          d.n_heads <= 2 * MAX_HEADS && c.paged &&
@@ -1013,7 +1034,8 @@ hipError_t decode_absorb(const mla_dims& d, float scale, int rows, int q_len, co
   return hipGetLastError();
 }
 
-hipError_t decode_combine(const mla_dims& d, int rows, int q_len, int splits, int pps, const int32_t* ctx_lens,
+hipError_t decode_combine(const mla_dims& d, int rows, int q_len, int splits, const int32_t* run_pages,
+                          const int32_t* ctx_lens,
                           const void* part_o, const float* part_ml, const void* w_uv, void* out,
                           const char* prof_name, hipStream_t s) {
   const int H = d.n_heads;
@@ -1024,7 +1046,7 @@ hipError_t decode_combine(const mla_dims& d, int rows, int q_len, int splits, in
   const int nbt = small ? (rows + 3) / 4 : (rows + 15) / 16;
   ProfScope ps(prof_name, s);
   auto go = [&](auto kern) {
-    hipLaunchKernelGGL(kern, dim3(hpad * nbt), dim3(256), 0, s, H, rows, q_len, splits, pps, ctx_lens,
+    hipLaunchKernelGGL(kern, dim3(hpad * nbt), dim3(256), 0, s, H, rows, q_len, splits, run_pages, ctx_lens,
                        (const bf16*)part_o, part_ml, (const bf16*)w_uv, (bf16*)out);
   };
   // one group of splits per row (the common case) or several
@@ -1062,6 +1084,7 @@ hipError_t decode_fast(const mla_dims& d, float scale, int n_seq, int q_len, int
   bf16* qt = (bf16*)(base + l.qt);
   bf16* part_o = (bf16*)(base + l.part_o);
   float* part_ml = (float*)(base + l.part_ml);
+  int32_t* run = (int32_t*)(base + l.run);
 
   hipError_t e = decode_absorb(d, scale, batch, q_len, q_nope, q_pe, w_uk, c.context_lens, qt, "mla_decode_absorb", s);
   if (e != hipSuccess) return e;
@@ -1072,17 +1095,19 @@ hipError_t decode_fast(const mla_dims& d, float scale, int n_seq, int q_len, int
     const int order = pair_xcd ? 1 : (q_len == 1 && batch <= 256 ? 2 : 0);
     // head tiles of 32 with real heads: 1 or 2 for small head counts, else 4
     const int nht = H <= 32 ? 1 : (H <= 64 ? 2 : 4);
+    // workgroups of one round per head group (one split workgroup per CU)
+    const int budget = max(1, device_cus() / (int)grid.z);
     auto go = [&](auto kern) {
       hipLaunchKernelGGL(kern, grid, dim3(SPLIT_THREADS), 0, s, H, batch, q_len, order, p.splits,
-                         p.pages_per_split, qt, (const bf16*)c.rows, c.block_table, c.max_blocks, c.context_lens,
-                         part_o, part_ml);
+                         p.pages_per_split, budget, run, qt, (const bf16*)c.rows, c.block_table, c.max_blocks,
+                         c.context_lens, part_o, part_ml);
     };
     if (nht == 1) go(k_split<1>);
     else if (nht == 2) go(k_split<2>);
     else go(k_split<4>);
   }
   if ((e = hipGetLastError()) != hipSuccess) return e;
-  return decode_combine(d, batch, q_len, p.splits, p.pages_per_split, c.context_lens, part_o, part_ml, w_uv, out,
+  return decode_combine(d, batch, q_len, p.splits, run, c.context_lens, part_o, part_ml, w_uv, out,
                         "mla_decode_combine_uv", s);
 }
 

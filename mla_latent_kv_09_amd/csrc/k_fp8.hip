@@ -214,6 +214,7 @@ __device__ __forceinline__ void score_done(f32x16& x) {
 __device__ __forceinline__ void mfma_switch(f32x16& x) { asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" : "+v"(x)); }
 
 __global__ __launch_bounds__(THREADS, 1) void k_split8(int H, int B, int q_len, int order, int splits, int pps,
+                                                       int budget, int32_t* __restrict__ run_out,
                                                        const bf16* __restrict__ qt,
                                                        const uint8_t* __restrict__ pages,
                                                        const int32_t* __restrict__ block_table, int max_blocks,
@@ -221,10 +222,18 @@ __global__ __launch_bounds__(THREADS, 1) void k_split8(int H, int B, int q_len, 
                                                        bf16* __restrict__ part_o, float* __restrict__ part_ml) {
   __shared__ __attribute__((aligned(1024))) char lds[SPLIT8_LDS];
   // block order: 0 plain, 1 rows of one sequence paired on an XCD, 2 longest
-  // runs first (one new token per row), as in the bf16 kernel
+  // runs first (one new token per row) with the run length that fits one
+  // round, as in the bf16 kernel (the first block records it for the combine)
   int split = blockIdx.x, b = blockIdx.y, len_b = 0;
+  int lens[4] = {0, 0, 0, 0};
+  if (order == 2) load_row_lens(B, ctx_lens, lens);
+  // (only when the launch's slots, splits x B, exceed one round: otherwise
+  // the runs of pps fit whatever the lengths)
+  const int pps_run = order == 2 && splits * B > budget ? one_round_run_pages(pps, 64, budget, PAGE, lens) : pps;
+  if ((blockIdx.x | blockIdx.y) == 0 && threadIdx.x == 0) *run_out = pps_run;
   if (order == 2) {
-    if (!longest_run_first(B, pps * PAGE, ctx_lens, blockIdx.y * gridDim.x + blockIdx.x, b, split, len_b)) return;
+    if (!longest_run_first(B, pps_run * PAGE, lens, blockIdx.y * gridDim.x + blockIdx.x, b, split, len_b))
+      return;
   } else if (order == 1) {
     // the q_len rows of one (sequence, split) on consecutive slots of one XCD
     const int lin = blockIdx.y * gridDim.x + blockIdx.x, local = lin >> 3;
@@ -235,8 +244,8 @@ __global__ __launch_bounds__(THREADS, 1) void k_split8(int H, int B, int q_len, 
   }
   const int seq = b / q_len;
   const int L = order == 2 ? len_b : ctx_lens[seq] - (q_len - 1 - (b - seq * q_len));
-  const int t_begin = split * pps * PAGE;
-  const int t_end = min(t_begin + pps * PAGE, L);
+  const int t_begin = split * pps_run * PAGE;
+  const int t_end = min(t_begin + pps_run * PAGE, L);
   if (t_begin >= t_end) return;
   const int n_tiles = (t_end - t_begin + PAGE - 1) / PAGE;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
@@ -713,7 +722,7 @@ bool decode_fp8_supported(const mla_dims& d, const CacheView& c) {
 
 namespace {
 struct Ws8 {
-  size_t qt, part_o, part_ml, total;
+  size_t qt, part_o, part_ml, run, total;
   int splits, pps;
 };
 size_t al256(size_t x) { return (x + 255) & ~(size_t)255; }
@@ -723,7 +732,8 @@ Ws8 ws8_layout(int H, int rows, int q_len, int max_context) {
   l.qt = 0;
   l.part_o = al256((size_t)rows * H * (DC + DR) * 2);
   l.part_ml = l.part_o + al256((size_t)H * rows * l.splits * DC * 2);
-  l.total = l.part_ml + al256((size_t)H * rows * l.splits * 2 * 4);
+  l.run = l.part_ml + al256((size_t)H * rows * l.splits * 2 * 4);
+  l.total = l.run + 256;  // the run length the split kernel used, for the combine
   return l;
 }
 }  // namespace
@@ -742,6 +752,7 @@ hipError_t decode_fp8(const mla_dims& d, float scale, int n_seq, int q_len, int 
   void* qt = base + l.qt;
   bf16* part_o = (bf16*)(base + l.part_o);
   float* part_ml = (float*)(base + l.part_ml);
+  int32_t* run = (int32_t*)(base + l.run);
   hipError_t e = decode_absorb(d, scale, rows, q_len, q_nope, q_pe, w_uk, c.context_lens, qt, "mla_decode8_absorb", s);
   if (e != hipSuccess) return e;
   {
@@ -749,11 +760,11 @@ hipError_t decode_fp8(const mla_dims& d, float scale, int n_seq, int q_len, int 
     const bool pair_xcd = q_len > 1 && ((int64_t)n_seq * l.splits) % 8 == 0;
     const int order = pair_xcd ? 1 : (q_len == 1 && rows <= 256 ? 2 : 0);
     hipLaunchKernelGGL(k_split8, dim3(l.splits, rows), dim3(THREADS), 0, s, H, rows, q_len, order, l.splits, l.pps,
-                       (const bf16*)qt, (const uint8_t*)c.rows, c.block_table, c.max_blocks,
+                       device_cus(), run, (const bf16*)qt, (const uint8_t*)c.rows, c.block_table, c.max_blocks,
                        c.context_lens, part_o, part_ml);
   }
   if ((e = hipGetLastError()) != hipSuccess) return e;
-  return decode_combine(d, rows, q_len, l.splits, l.pps, c.context_lens, part_o, part_ml, w_uv, out,
+  return decode_combine(d, rows, q_len, l.splits, run, c.context_lens, part_o, part_ml, w_uv, out,
                         "mla_decode8_combine_uv", s);
 }
 

@@ -272,14 +272,6 @@ RowPlan row_plan(int M, int N, int K, int cus) {
   return best;
 }
 
-int device_cus() {
-  int dev = 0, cus = 256;
-  if (hipGetDevice(&dev) != hipSuccess ||
-      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
-    cus = 256;
-  return cus;
-}
-
 bool row_path(const mla_dims& d, int M, int N, int K) {
   return d.dtype == MLA_BF16 && M <= 256 && K % RG_SK == 0 && N % 4 == 0;
 }

@@ -65,12 +65,16 @@ hipError_t decode_fast(const mla_dims& d, float scale, int n_seq, int q_len, int
 // decode_combine merges per-split partials [H][rows][splits][512] bf16 and
 // (m, l) [H][rows][splits][2] and applies W_UV (w_uv == nullptr: writes the
 // merged latent output o_c [rows, H, 512] bf16 instead; so does decode_fast).
+// run_pages (device) holds the pages per run the split kernel used, at least
+// decode_plan's pages_per_split, so a row has at most `splits` runs.
+// device_cus is the current device's compute-unit count.
 void decode_plan(int rows, int max_context, int q_len, int* pages_per_split, int* splits);
+int device_cus();
 hipError_t decode_absorb(const mla_dims& d, float scale, int rows, int q_len, const void* q_nope, const void* q_pe,
                          const void* w_uk, const int32_t* ctx_lens, void* qt, const char* prof_name, hipStream_t s);
-hipError_t decode_combine(const mla_dims& d, int rows, int q_len, int splits, int pps, const int32_t* ctx_lens,
-                          const void* part_o, const float* part_ml, const void* w_uv, void* out,
-                          const char* prof_name, hipStream_t s);
+hipError_t decode_combine(const mla_dims& d, int rows, int q_len, int splits, const int32_t* run_pages,
+                          const int32_t* ctx_lens, const void* part_o, const float* part_ml, const void* w_uv,
+                          void* out, const char* prof_name, hipStream_t s);
 
 // ---- FP8 latent cache (E4M3 codes, one power-of-two scale per token) ------
 // Page of P tokens: P rows of [d_c codes || d_rope bf16 k_pe], then P scale

@@ -124,3 +124,25 @@ def score_jump_case(case, jump_log2, low_pages=2):
     case.cache.pool = f32_to_bf16_bits(pool)
     case.q_pe = f32_to_bf16_bits(q_pe)
     return case
+
+
+def host_run_pages(rows, max_context):
+    """Pages per run as the library's host side plans a decode step with one
+    new token per row: about one run per compute unit over rows x the
+    longest context's pages, clamped to 4..32."""
+    max_pages = -(-max_context // 64)
+    return max(4, min(32, -(-rows * max_pages // 256)))
+
+
+def one_round_run_pages(lens, pps, budget):
+    """The run length the split kernels take over contexts `lens`: the
+    smallest length in (pps, min(64, 5 pps / 4)] whose runs fit in one round
+    of `budget` workgroups when the runs of pps need a second round (but not
+    a third), else pps."""
+    runs = lambda q: sum(-(-int(L) // (64 * q)) for L in lens)
+    if runs(pps) <= budget or runs(pps) > 2 * budget:
+        return pps
+    for q in range(pps + 1, min(64, pps + pps // 4) + 1):
+        if runs(q) <= budget:
+            return q
+    return pps

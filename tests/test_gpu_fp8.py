@@ -15,7 +15,7 @@ import oracle
 from oracle import fp8
 from synth import Dims, f32_to_bf16_bits, from_torch, make_decode_case, to_torch, workload
 
-from gpu_helpers import assert_parity, fails_bar
+from gpu_helpers import assert_parity, fails_bar, host_run_pages, one_round_run_pages
 
 pytestmark = pytest.mark.gpu
 
@@ -255,6 +255,43 @@ def test_workload3_fp8_full_size_sampled():
     deq = np.zeros((nb, P, R))
     deq[used] = fp8.dequantize_pool(want, P, 512, 64)
     assert_parity(got[sample], _oracle_fp8(case, deq, seqs=sample), "fp8", "workload 3, fp8 cache")
+
+
+def test_fp8_decode_lengthens_runs_to_fit_one_round():
+    """256 rows of up to 2200 tokens: runs of 32 pages (the host's choice)
+    would take 267 workgroups, so the FP8 split kernel takes runs of 34 pages
+    (one round on a 256-CU device) and the combine reads that length back.
+    Rows with 33 or 34 pages (one run now, two at 32) and the longest and
+    shortest rows against the oracle over the oracle's own pages."""
+    _log("fp8 decode with runs lengthened to fit one round")
+    lens = [int(x) for x in np.random.default_rng(120).integers(1, 2201, 256)]
+    case = make_decode_case(82, 256, Dims(32, **V3), lens, shuffle=True)
+    c = case.cache
+    nb, P, R = c.pool.shape
+    pages = _gpu_quantize(case.dims, c.pool.reshape(nb * P, R), np.arange(nb * P, dtype=np.int32), nb, P)
+    cache = mla.Fp8Cache(to_torch(pages), to_torch(c.context_lens.astype(np.int32)), max(lens),
+                         to_torch(c.block_table.astype(np.int32)))
+    n = mla.mla_decode_fp8_workspace_size(mla.Dims.of(case.dims), 256, 1, max(lens))
+    ws = torch.empty(n, dtype=torch.uint8, device="cuda")
+    out = mla.mla_decode_fp8(case.dims, to_torch(case.q_nope), to_torch(case.q_pe), to_torch(case.w_uk),
+                             to_torch(case.w_uv), cache, workspace=ws)
+    torch.cuda.synchronize()
+    got = from_torch(out)
+    used = int(ws[n - 256:n - 252].view(torch.int32).item())
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    pps = host_run_pages(256, max(lens))
+    assert used == one_round_run_pages(lens, pps, cus)
+    if cus == 256:
+        assert used > pps
+    n_pages = [(L + 63) // 64 for L in lens]
+    joined = [b for b in range(256) if pps < n_pages[b] <= used][:4]
+    sample = sorted(set(joined) | {int(np.argmax(lens)), int(np.argmin(lens)), 0, 255})
+    used_pages = np.unique(np.concatenate([c.block_table[b, :n_pages[b]] for b in sample]))
+    want = fp8.quantize_pool(oracle.widen(c.pool[used_pages]), 512)
+    assert np.array_equal(pages[used_pages], want)
+    deq = np.zeros((nb, P, R))
+    deq[used_pages] = fp8.dequantize_pool(want, P, 512, 64)
+    assert_parity(got[sample], _oracle_fp8(case, deq, seqs=sample), "fp8", "runs lengthened to one round")
 
 
 def _decode_fp8_bytes(pages, bs, d_c, d_rope):

@@ -13,7 +13,8 @@ import mla_latent_kv_09_amd as mla
 import oracle
 from synth import Dims, from_torch, make_decode_case, make_project_case, to_torch, workload
 
-from gpu_helpers import assert_parity, assert_projection_parity, device_cache, fails_bar, run_decode
+from gpu_helpers import (assert_parity, assert_projection_parity, device_cache, fails_bar, host_run_pages,
+                         one_round_run_pages, run_decode)
 
 pytestmark = pytest.mark.gpu
 
@@ -267,6 +268,39 @@ def test_decode_run_order_covers_every_run_once(name, rows, H, lens):
     case = make_decode_case(80 + rows, rows, Dims(H, **V3), lens, shuffle=True)
     assert mla.mla_decode_path(case.dims) == 1
     got = run_decode(case)
+    c = case.cache
+    ref = oracle.absorbed_decode(case.dims, case.q_nope, case.q_pe, case.w_uk, case.w_uv, c.pool, c.block_table,
+                                 c.context_lens)
+    assert_parity(got, ref, "bf16", name)
+
+
+# Runs a little longer than the host's choice. The host sets pps from the
+# longest context alone; when the actual contexts then cut into a few more
+# runs than the chip has compute units (one split workgroup each), the split
+# kernel lengthens the runs by up to a quarter so that they fit one round,
+# and the combine reads the length it used (from the workspace's last 256
+# bytes). These batches take that path on a 256-CU device.
+LONGER_RUNS = [
+    # 230 rows: pps 28 gives 257 runs, 29 gives 246
+    ("230 rows H16", 230, 16, _ragged_lens(214, 230, 2000)),
+    # 256 rows: pps 32 (the cap) gives 267 runs, 34 gives 256
+    ("256 rows H32", 256, 32, _ragged_lens(120, 256, 2200)),
+]
+
+
+@pytest.mark.parametrize("name,rows,H,lens", LONGER_RUNS, ids=[r[0] for r in LONGER_RUNS])
+def test_decode_lengthens_runs_to_fit_one_round(name, rows, H, lens):
+    _log(f"decode with runs lengthened to fit one round: {name}")
+    case = make_decode_case(81, rows, Dims(H, **V3), lens, shuffle=True)
+    n = mla.mla_decode_workspace_size(mla.Dims.of(case.dims), rows, max(lens))
+    ws = torch.empty(n, dtype=torch.uint8, device="cuda")
+    got = run_decode(case, workspace=ws)
+    used = int(ws[n - 256:n - 252].view(torch.int32).item())
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    pps = host_run_pages(rows, max(lens))
+    assert used == one_round_run_pages(lens, pps, cus)
+    if cus == 256:
+        assert used > pps
     c = case.cache
     ref = oracle.absorbed_decode(case.dims, case.q_nope, case.q_pe, case.w_uk, case.w_uv, c.pool, c.block_table,
                                  c.context_lens)
