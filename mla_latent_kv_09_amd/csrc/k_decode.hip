@@ -111,7 +111,10 @@ Plan plan_splits(int batch, int max_context, int q_len) {
   const int max_pages = (max_context + PAGE - 1) / PAGE;
   // aim for one workgroup per compute unit across the batch, 4..32 pages each;
   // with several rows per sequence up to 64, which halves the partials
-  // (one per row and run) where the rows alone fill the chip
+  // (one per row and run) where the rows alone fill the chip. This sees only
+  // the longest context; with one new token per row the split kernel may
+  // lengthen the runs once it has the actual lengths (never shorten them, so
+  // `splits` bounds every row's runs).
   const int cap = q_len > 1 ? 64 : 32;
   int pps = (int)(((int64_t)batch * max_pages + 255) / 256);
   pps = pps < 4 ? 4 : (pps > cap ? cap : pps);
