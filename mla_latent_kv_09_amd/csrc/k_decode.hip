@@ -937,8 +937,11 @@ __global__ __launch_bounds__(256) void k_combine_uv(int H, int B, int q_len, int
         wf[ks][mt] = *(const u32x4*)(wv + (size_t)(32 * w + 16 * mt + i16) * DC + 32 * ks + 8 * G);
   };
   // with one group they go out right behind the partials, and the context
-  // length is needed only for the merge
-  if constexpr (UV && !MULTI) load_wuv();
+  // length is needed only for the merge; so they do with 4-row tiles (used
+  // only where the grid is small, so registers do not limit the waves that
+  // run at once)
+  constexpr bool EARLY_WUV = UV && (!MULTI || TR == 4);
+  if constexpr (EARLY_WUV) load_wuv();
   if constexpr (!MULTI) {
     __builtin_amdgcn_sched_barrier(0);
     ns = row_splits();
@@ -956,7 +959,7 @@ __global__ __launch_bounds__(256) void k_combine_uv(int H, int B, int q_len, int
   }
   // with several groups, once they are merged (their loads fly while o_c is
   // staged)
-  if constexpr (UV && MULTI) load_wuv();
+  if constexpr (UV && !EARLY_WUV) load_wuv();
   const float il = ns > 0 ? 1.f / l : 0.f;
 #pragma unroll
   for (int u = 0; u < NU; ++u) {

@@ -285,6 +285,9 @@ LONGER_RUNS = [
     ("230 rows H16", 230, 16, _ragged_lens(214, 230, 2000)),
     # 256 rows: pps 32 (the cap) gives 267 runs, 34 gives 256
     ("256 rows H32", 256, 32, _ragged_lens(120, 256, 2200)),
+    # two head groups (128 + 72 heads), so a round is half the CUs per group:
+    # pps 4 gives 129 runs, 5 gives 108
+    ("51 rows H200", 51, 200, _ragged_lens(1875, 51, 1000)),
 ]
 
 
@@ -298,7 +301,7 @@ def test_decode_lengthens_runs_to_fit_one_round(name, rows, H, lens):
     used = int(ws[n - 256:n - 252].view(torch.int32).item())
     cus = torch.cuda.get_device_properties(0).multi_processor_count
     pps = host_run_pages(rows, max(lens))
-    assert used == one_round_run_pages(lens, pps, cus)
+    assert used == one_round_run_pages(lens, pps, cus // ((H + 127) // 128))  # a round per head group
     if cus == 256:
         assert used > pps
     c = case.cache
