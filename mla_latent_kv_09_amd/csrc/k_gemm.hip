@@ -35,8 +35,9 @@ constexpr int HEAD_W = 128;  // head width of the per-head epilogues
 // Block tile 256 x BN with BN = 64 NI, WAVES waves: two along the A rows (128
 // each) and WAVES / 2 along the B rows, so each wave owns 128 A-rows x
 // 64 NI / (WAVES / 2) B-rows (4 x NW MFMA tiles of 32 x 32). NI = 2: 256 x
-// 128, three 48 KB stages; NI = 4: 256 x 256, two 64 KB stages (half the
-// copies per MFMA). With 8 waves (NI = 4 only) two waves share each SIMD, so
+// 128, three 48 KB stages; NI = 3: 256 x 192, two 56 KB stages (the latent
+// projection, whose 576 columns are three such tiles); NI = 4: 256 x 256, two
+// 64 KB stages (half the copies per MFMA). With 8 waves (NI = 4 only) two waves share each SIMD, so
 // one wave's copies, LDS reads and epilogue stores issue while the other's
 // MFMAs run; each then holds 128 accumulators instead of 256.
 template <int NI, int WAVES>
@@ -106,7 +107,7 @@ __global__ __launch_bounds__(64 * WAVES, 1) void k_gemm(GemmArgs g) {
   // of them; otherwise plain row order (A shared across the XCDs).
   const int m_tiles = (g.M + BM - 1) / BM;
   int mt = bid / n_tiles, nt = bid % n_tiles;
-  if (NI == 2 && n_tiles <= 16 && m_tiles % 8 == 0) {
+  if ((NI == 2 || NI == 3) && n_tiles <= 16 && m_tiles % 8 == 0) {
     const int xcd = bid & 7, local = bid >> 3;
     mt = (local / n_tiles) * 8 + xcd;
     nt = local % n_tiles;
@@ -352,7 +353,20 @@ hipError_t gemm_fast(const GemmArgs& g, int epi, hipStream_t s) {
   // 256-wide tiles where there are enough of them to fill the chip several
   // times over (and no partial tile); 128-wide otherwise
   const bool wide = epi != 1 && g.N % 256 == 0 && m_tiles * (g.N / 256) >= 1024;
-  const int grid = m_tiles * (wide ? g.N / 256 : (g.N + 127) / 128);
+  // The latent projection (N = d_c + d_rope, 576 for the DeepSeek-V3 shape)
+  // has few column tiles, so the last round of blocks can be mostly empty:
+  // 64 row tiles x 5 tiles of 128 columns are 320 blocks, two rounds on 256
+  // CUs with the second a quarter full. Where N is a whole number of
+  // 192-column tiles and those take less time by rounds x tile width (64 x 3
+  // = 192 blocks: one round of 1.5x the work), the 256 x 192 tile is used.
+  bool w192 = false;
+  if (epi == 1 && g.N % 192 == 0) {
+    const int cus = device_cus();
+    const long r128 = ((long)m_tiles * ((g.N + 127) / 128) + cus - 1) / cus;
+    const long r192 = ((long)m_tiles * (g.N / 192) + cus - 1) / cus;
+    w192 = r192 * 192 < r128 * 128;
+  }
+  const int grid = m_tiles * (wide ? g.N / 256 : w192 ? g.N / 192 : (g.N + 127) / 128);
   auto go = [&](auto kern, int waves) { hipLaunchKernelGGL(kern, dim3(grid), dim3(64 * waves), 0, s, g); };
   // The K/V up-projections (K = 512: eight K steps, then a 128 KB output
   // tile) run 8 waves, two per SIMD, which measured 7 % faster there; the
@@ -362,7 +376,8 @@ hipError_t gemm_fast(const GemmArgs& g, int epi, hipStream_t s) {
     else if (epi == 3) go(k_gemm<3, 4, 8>, 8);
     else go(k_gemm<0, 4, 4>, 4);
   } else {
-    if (epi == 1) go(k_gemm<1, 2, 4>, 4);
+    if (epi == 1 && w192) go(k_gemm<1, 3, 4>, 4);
+    else if (epi == 1) go(k_gemm<1, 2, 4>, 4);
     else if (epi == 2) go(k_gemm<2, 2, 4>, 4);
     else if (epi == 3) go(k_gemm<3, 2, 4>, 4);
     else go(k_gemm<0, 2, 4>, 4);

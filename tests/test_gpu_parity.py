@@ -545,6 +545,28 @@ def _check_rows(got_rows, ref_rows):
         float(np.abs(got_rows - ref_rows).max())
 
 
+@pytest.mark.parametrize("batch,seq_len", [(2, 7000), (2, 8192)])
+def test_latent_projection_192_wide_tiles(batch, seq_len):
+    """Latent projection over 14,000 and 16,384 tokens (N = 576): these take
+    the 256 x 192 GEMM tiles (one round of 55 or 64 row tiles x 3 column tiles
+    instead of two rounds of 128-wide tiles), the first with a ragged last row
+    tile in plain order, the second with the column tiles of each row tile on
+    one XCD. Every cache row is compared with the oracle, RoPE at positions up
+    to 8191 included."""
+    _log(f"latent projection, 256 x 192 tiles, B={batch} S={seq_len}")
+    dims = Dims(128, **V3)
+    case = make_project_case(60 + seq_len % 7, batch=batch, seq_len=seq_len, d_model=256, dims=dims,
+                             shuffle=True, draw_query=False)
+    rows = torch.full((case.num_blocks, 64, dims.row), 3.0, dtype=torch.bfloat16, device="cuda")
+    lens = torch.full((batch,), seq_len, dtype=torch.int32, device="cuda")
+    cache = mla.Cache(rows, lens, seq_len, to_torch(case.block_table))
+    mla.mla_rope_latent_project(dims, to_torch(case.h), to_torch(case.w_dkv), to_torch(case.w_kr),
+                                to_torch(case.positions), to_torch(case.slots), cache)
+    torch.cuda.synchronize()
+    got_rows = from_torch(rows)[case.slots // 64, case.slots % 64]
+    _check_rows(got_rows, oracle.latent_rows(case.h, case.w_dkv, case.w_kr, case.positions))
+
+
 def test_mfma_projection_and_prefill_ragged():
     _log("MFMA projection + prefill, B=2 S=300 H=128")
     dims = Dims(128, **V3)
