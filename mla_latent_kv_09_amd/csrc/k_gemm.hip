@@ -206,7 +206,10 @@ __global__ __launch_bounds__(64 * WAVES, 1) void k_gemm(GemmArgs g) {
   // Plain, head-major and blocked-transposed stores go through LDS: the tile
   // is staged (as C for EPI 0/3, as C^T for EPI 2) and then written as whole
   // 16-byte pieces of consecutive output bytes, instead of each store
-  // instruction touching 32 rows.
+  // instruction touching 32 rows. The stores are non-temporal: the outputs
+  // (up to 805 MB for the query up-projection) would otherwise stream through
+  // the 256 MB last-level cache and push out the operands that every round
+  // of blocks reads again.
   if constexpr (EPI != 1) {
     const bool aligned16 = g.N % 8 == 0 && g.c_split % 8 == 0 && g.ldc0 % 8 == 0 && g.ldc1 % 8 == 0 &&
                            ((size_t)g.c0 & 15) == 0 && ((size_t)g.c1 & 15) == 0;
@@ -239,7 +242,7 @@ __global__ __launch_bounds__(64 * WAVES, 1) void k_gemm(GemmArgs g) {
           const int b = m / g.a_seq, t = m - b * g.a_seq;
           bf16* dst = g.c0 + ((((size_t)b * n_heads + n / HEAD_W) * (g.a_seq / 64) + t / 64) * HEAD_W + n % HEAD_W) * 64 +
                       t % 64;
-          *(u32x4*)dst = *(const LDS_AS u32x4*)(ct + r * CT_PITCH + 8 * ch);
+          __builtin_nontemporal_store(*(const LDS_AS u32x4*)(ct + r * CT_PITCH + 8 * ch), (u32x4*)dst);
         }
       } else {
         // rows m (256 of them) x BN columns n, in 16-byte pieces of 8 n
@@ -250,10 +253,10 @@ __global__ __launch_bounds__(64 * WAVES, 1) void k_gemm(GemmArgs g) {
           const u32x4 v = *(const LDS_AS u32x4*)(ct + r * CT_PITCH + 8 * ch);
           if constexpr (EPI == 3) {
             const int b = m / g.a_seq, t = m - b * g.a_seq;
-            *(u32x4*)(g.c0 + (((size_t)b * n_heads + n / HEAD_W) * g.a_seq + t) * HEAD_W + n % HEAD_W) = v;
+            __builtin_nontemporal_store(v, (u32x4*)(g.c0 + (((size_t)b * n_heads + n / HEAD_W) * g.a_seq + t) * HEAD_W + n % HEAD_W));
           } else {
-            if (n < g.c_split) *(u32x4*)(g.c0 + (size_t)m * g.ldc0 + n) = v;
-            else *(u32x4*)(g.c1 + (size_t)m * g.ldc1 + (n - g.c_split)) = v;
+            if (n < g.c_split) __builtin_nontemporal_store(v, (u32x4*)(g.c0 + (size_t)m * g.ldc0 + n));
+            else __builtin_nontemporal_store(v, (u32x4*)(g.c1 + (size_t)m * g.ldc1 + (n - g.c_split)));
           }
         }
       }

@@ -460,7 +460,8 @@ __global__ __launch_bounds__(P_THREADS, 1) void k_prefill_attn(
     const int idx = threadIdx.x + P_THREADS * k, row = idx / (DV / 8), ch = idx % (DV / 8);
     const int s_out = s0 + row;
     if (s_out < S)
-      *(u32x4*)(out + (((size_t)b * S + s_out) * H + h) * DV + 8 * ch) = *(const LDS_AS u32x4*)(ost + row * OP + 8 * ch);
+      __builtin_nontemporal_store(*(const LDS_AS u32x4*)(ost + row * OP + 8 * ch),
+                                  (u32x4*)(out + (((size_t)b * S + s_out) * H + h) * DV + 8 * ch));
   }
 }
 
