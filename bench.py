@@ -17,9 +17,11 @@ Prefill (workload 5): one step is mla_rope_latent_project (latent rows into
 the cache, query path) followed by causal mla_prefill.
 
 By default the decode workloads run 200 untimed steps and then time 300, so
-that the timed region sees the chip's settled clock (it takes about 100 decode
+that the timed region sees the chip's settled clock (it takes about 150 decode
 steps to settle); prefill runs 10 + 50. Explicit --warmup / --steps are used
-as given.
+as given. After the timed region a decode line also carries a 'steady' pass
+(200 more untimed steps, then 300 timed) and a cold-cache pass; neither
+enters 'value'.
 
 Prints one JSON line with the throughput, the roofline position of the
 dominant kernel (timed with HIP events recorded around each library launch
@@ -75,6 +77,9 @@ def parse():
     ap.add_argument("--steps", type=int, default=None, help="timed steps (default 300; 50 for workload 5)")
     ap.add_argument("--warmup", type=int, default=None, help="untimed steps first (default 200; 10 for workload 5)")
     ap.add_argument("--workload", type=int, default=3, choices=sorted(WORKLOAD_NAMES))
+    ap.add_argument("--steady-steps", type=int, default=300,
+                    help="decode: after the timed steps, 200 more untimed and then this many timed, reported as "
+                         "'steady' beside the main figure (0 skips it)")
     ap.add_argument("--cold-steps", type=int, default=50,
                     help="decode: steps of the cold-cache pass (each after a 512 MiB read), after the timed steps")
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="budget of the CPU oracle sample")
@@ -296,6 +301,30 @@ def cold_pass(step, lib, kernel_name, n):
     del flush
     return {"steps": n, "flush_bytes": FLUSH_BYTES, "step_us_median": round(float(np.median(steps_us)), 2),
             "step_us_min": round(float(np.min(steps_us)), 2),
+            "split_us_mean": round(k[kernel_name][0] / k[kernel_name][1] * 1e3, 2)}
+
+
+def steady_pass(step, lib, kernel_name, n, warmup=200):
+    """After the timed region: warmup more untimed steps (the chip's clock
+    takes about 150 steps of sustained decode to settle), then n steps timed
+    between two events with the library's events around kernel_name. Returns
+    the step time and the kernel's mean time in microseconds."""
+    import torch
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    lib.mla_profile_only(kernel_name.encode())
+    lib.mla_profile_begin()
+    ev0.record(stream)
+    for _ in range(n):
+        step()
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    k = profile_end(lib)
+    lib.mla_profile_only(None)
+    return {"warmup": warmup, "steps": n, "step_us": round(ev0.elapsed_time(ev1) / n * 1e3, 2),
             "split_us_mean": round(k[kernel_name][0] / k[kernel_name][1] * 1e3, 2)}
 
 
@@ -599,6 +628,7 @@ def main():
         step()
     torch.cuda.synchronize()
     breakdown = profile_end(lib)
+    steady = steady_pass(step, lib, split_name, args.steady_steps) if args.steady_steps > 0 else None
     cold = cold_pass(step, lib, split_name, args.cold_steps)
 
     sum_l = int(c.context_lens.astype(np.int64).sum())
@@ -660,6 +690,10 @@ def main():
                  "mfma_TFLOP_per_s": round(step_flop / (ms * 1e-3) / 1e12, 1),
                  "mfma_frac": round(step_flop / (ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 4),
                  "kernels_us": kernels_us},
+        "steady": None if steady is None else {
+            **steady, "tokens_per_s": round(B * Q / (steady["step_us"] * 1e-6), 1),
+            "split_frac": round(cache_bytes / (steady["split_us_mean"] * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+            "order": "after the timed steps"},
         "cold": {**cold, "tokens_per_s": round(B * Q / (cold["step_us_median"] * 1e-6), 1),
                  "split_frac": round(cache_bytes / (cold["split_us_mean"] * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
                  "order": "after the timed steps"},
