@@ -213,6 +213,16 @@ __device__ __forceinline__ void score_done(f32x16& x) {
 // MFMA kinds chain only after the first one's result is written)
 __device__ __forceinline__ void mfma_switch(f32x16& x) { asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" : "+v"(x)); }
 
+// The lane index, computed in asm that the compiler cannot merge with an
+// earlier computation of it: code after the page loop that takes it from here
+// keeps nothing of the prologue live across the loop (the loop needs every
+// register, and a value held over it is spilled to scratch).
+__device__ __forceinline__ int opaque_lane() {
+  int l;
+  asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(l));
+  return l;
+}
+
 __global__ __launch_bounds__(THREADS, 1) void k_split8(int H, int B, int q_len, int order, int splits, int pps,
                                                        int budget, int32_t* __restrict__ run_out,
                                                        const bf16* __restrict__ qt,
@@ -242,6 +252,11 @@ __global__ __launch_bounds__(THREADS, 1) void k_split8(int H, int B, int q_len, 
     split = unit - seq * splits;
     b = seq * q_len + j;
   }
+  // the block's row and split are the same in every lane: keep them (and
+  // what derives from them) in scalar registers
+  b = __builtin_amdgcn_readfirstlane(b);
+  split = __builtin_amdgcn_readfirstlane(split);
+  len_b = __builtin_amdgcn_readfirstlane(len_b);
   const int seq = b / q_len;
   const int L = order == 2 ? len_b : ctx_lens[seq] - (q_len - 1 - (b - seq * q_len));
   const int t_begin = split * pps_run * PAGE;
@@ -410,7 +425,7 @@ __global__ __launch_bounds__(THREADS, 1) void k_split8(int H, int B, int q_len, 
     const int valid = t_end - (t_begin + i * PAGE);
     if (valid >= PAGE) return;
     LDS_AS char* base = (LDS_AS char*)(size_t)slot_addr(i);
-    const int first = w * 64 + (int)__builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u));
+    const int first = w * 64 + opaque_lane();
 #pragma unroll
     for (int k = 0; k < COPIES - 1; ++k) {
       const int pos = k * THREADS + first;
@@ -668,9 +683,17 @@ __global__ __launch_bounds__(THREADS, 1) void k_split8(int H, int B, int q_len, 
 
   // ---- partials (the bf16 kernel's layout): (m, l) by the head owner, O
   // rows through LDS, 32 heads at a time ----
-  l_run += __shfl_xor(l_run, 32, 64);
-  if (g == 0 && h_own < H) {
-    const size_t prow = ((size_t)h_own * B + b) * splits + split;
+  // The lane index is derived again (see opaque_lane), so nothing
+  // lane-dependent of the prologue stays live across the page loop.
+  const int lane_e = opaque_lane();
+  const int hl_e = lane_e & 31, g_e = lane_e >> 5, h_own_e = w * 32 + hl_e;
+  {
+    // row sum of the head over both halves of its rows (lanes l and l ^ 32)
+    const auto pr = __builtin_amdgcn_permlane32_swap(__float_as_uint(l_run), __float_as_uint(l_run), false, false);
+    l_run = __uint_as_float(pr[0]) + __uint_as_float(pr[1]);
+  }
+  if (g_e == 0 && h_own_e < H) {
+    const size_t prow = ((size_t)h_own_e * B + b) * splits + split;
     part_ml[prow * 2] = m_run;
     part_ml[prow * 2 + 1] = l_run;
   }
@@ -684,7 +707,7 @@ __global__ __launch_bounds__(THREADS, 1) void k_split8(int H, int B, int q_len, 
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
         const f32x4 v = {o[ct][ht][4 * q], o[ct][ht][4 * q + 1], o[ct][ht][4 * q + 2], o[ct][ht][4 * q + 3]};
-        *(LDS_AS f32x4*)(ost + hl * OP + 128 * w + 32 * ct + 8 * q + 4 * g) = v;
+        *(LDS_AS f32x4*)(ost + hl_e * OP + 128 * w + 32 * ct + 8 * q + 4 * g_e) = v;
       }
     lds_barrier();
 #pragma unroll
@@ -692,9 +715,9 @@ __global__ __launch_bounds__(THREADS, 1) void k_split8(int H, int B, int q_len, 
       const int hh = rr * 4 + w, h = 32 * ht + hh;
       if (h < H) {
         // 512 values as bf16: 8 per lane
-        const f32x4 x = *(const LDS_AS f32x4*)(ost + hh * OP + 8 * lane);
-        const f32x4 y = *(const LDS_AS f32x4*)(ost + hh * OP + 8 * lane + 4);
-        *(bf16x8_t*)(part_o + (((size_t)h * B + b) * splits + split) * DC + 8 * lane) =
+        const f32x4 x = *(const LDS_AS f32x4*)(ost + hh * OP + 8 * lane_e);
+        const f32x4 y = *(const LDS_AS f32x4*)(ost + hh * OP + 8 * lane_e + 4);
+        *(bf16x8_t*)(part_o + (((size_t)h * B + b) * splits + split) * DC + 8 * lane_e) =
             (bf16x8_t){(__bf16)x[0], (__bf16)x[1], (__bf16)x[2], (__bf16)x[3],
                        (__bf16)y[0], (__bf16)y[1], (__bf16)y[2], (__bf16)y[3]};
       }
